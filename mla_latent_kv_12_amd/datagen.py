@@ -1,0 +1,181 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module only draws random numbers and stores them (fp32, or bf16 bit
+patterns rounded to nearest-even); it performs none of the attention
+arithmetic.  Both the HIP path and the fp64 oracle consume exactly the
+arrays made here.
+
+Recipe (all draws from ``numpy.random.default_rng(seed)``, standard normals
+in float32, scaled where a standard deviation is given):
+  decode:  q_nope [B,H,dn], q_rope [B,H,dr], W_UK [H,dn,dc] (std 1/sqrt(dc)),
+           W_UV [H,dv,dc] (std 1/sqrt(dc)), the cache rows [B,Nmax,dc+dr]
+           sequence by sequence, then (ragged workloads only) the lengths
+           uniform in [1, Nmax].
+  prefill: q_nope [B,T,H,dn], q_rope [B,T,H,dr], W_UK, W_UV, then
+           x [B,T,d_model] ~ N(0,1) and W_DKV [dc,d_model] (std
+           1/sqrt(d_model)); the latent rows are c = W_DKV x (accumulated in
+           float64, then stored), and the decoupled RoPE keys k^R [B,T,dr]
+           ~ N(0,1).  Queries' RoPE channels and k^R are taken as already
+           rotated: a rotation maps i.i.d. standard normals to i.i.d. standard
+           normals, so the rotated values are drawn directly.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+SEED_BASE = 20260000
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest-even); returns uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + r) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact float32 value of bfloat16 bit patterns."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass
+class DecodeCase:
+    name: str
+    dtype: str            # "f32" or "bf16" (storage type of every tensor)
+    B: int
+    H: int
+    dc: int
+    dr: int
+    dn: int
+    dv: int
+    n_max: int
+    scale: float
+    q_nope: np.ndarray    # [B,H,dn]
+    q_rope: np.ndarray    # [B,H,dr]
+    w_uk: np.ndarray      # [H,dn,dc]
+    w_uv: np.ndarray      # [H,dv,dc]
+    cache: np.ndarray     # [B,n_max,dc+dr]: latent c then RoPE key
+    seqlens: np.ndarray   # int32 [B]
+
+    @property
+    def ckv(self) -> np.ndarray:
+        return self.cache[:, :, : self.dc]
+
+    @property
+    def kpe(self) -> np.ndarray:
+        return self.cache[:, :, self.dc:]
+
+
+@dataclasses.dataclass
+class PrefillCase:
+    name: str
+    dtype: str
+    B: int
+    T: int
+    H: int
+    dc: int
+    dr: int
+    dn: int
+    dv: int
+    scale: float
+    q_nope: np.ndarray    # [B,T,H,dn]
+    q_rope: np.ndarray    # [B,T,H,dr]
+    w_uk: np.ndarray
+    w_uv: np.ndarray
+    cache: np.ndarray     # [B,T,dc+dr]
+    seqlens: np.ndarray   # int32 [B] (== T: the prompt is the whole cache)
+
+    @property
+    def ckv(self) -> np.ndarray:
+        return self.cache[:, :, : self.dc]
+
+    @property
+    def kpe(self) -> np.ndarray:
+        return self.cache[:, :, self.dc:]
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _normal(rng, shape, std=1.0):
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return x
+
+
+def make_decode_case(*, B, H, dc, dr, dn, dv, n_max, dtype="bf16", seed=SEED_BASE,
+                     seqlens=None, ragged=False, scale=None, w_std=None, name="custom"):
+    """Draw one decode workload.  ``seqlens`` None -> every sequence full
+    (n_max) unless ``ragged`` (then uniform integers in [1, n_max])."""
+    rng = np.random.default_rng(seed)
+    w_std = 1.0 / math.sqrt(dc) if w_std is None else w_std
+    q_nope = _store(_normal(rng, (B, H, dn)), dtype)
+    q_rope = _store(_normal(rng, (B, H, dr)), dtype)
+    w_uk = _store(_normal(rng, (H, dn, dc), w_std), dtype)
+    w_uv = _store(_normal(rng, (H, dv, dc), w_std), dtype)
+    width = dc + dr
+    cache = np.empty((B, n_max, width), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    for b in range(B):  # sequence by sequence keeps peak host memory low
+        cache[b] = _store(_normal(rng, (n_max, width)), dtype)
+    if seqlens is None:
+        if ragged:
+            seqlens = rng.integers(1, n_max + 1, size=B)
+        else:
+            seqlens = np.full(B, n_max)
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dn + dr)
+    return DecodeCase(name, dtype, B, H, dc, dr, dn, dv, n_max, float(scale), q_nope, q_rope,
+                      w_uk, w_uv, cache, seqlens)
+
+
+def make_prefill_case(*, B, T, H, dc, dr, dn, dv, d_model, dtype="bf16", seed=SEED_BASE,
+                      scale=None, name="custom"):
+    rng = np.random.default_rng(seed)
+    w_std = 1.0 / math.sqrt(dc)
+    q_nope = _store(_normal(rng, (B, T, H, dn)), dtype)
+    q_rope = _store(_normal(rng, (B, T, H, dr)), dtype)
+    w_uk = _store(_normal(rng, (H, dn, dc), w_std), dtype)
+    w_uv = _store(_normal(rng, (H, dv, dc), w_std), dtype)
+    x = _store(_normal(rng, (B, T, d_model)), dtype)
+    w_dkv = _store(_normal(rng, (dc, d_model), 1.0 / math.sqrt(d_model)), dtype)
+    xf = bf16_to_f32(x) if dtype == "bf16" else x
+    wf = bf16_to_f32(w_dkv) if dtype == "bf16" else w_dkv
+    cache = np.empty((B, T, dc + dr), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    wt = wf.astype(np.float64).T
+    for b in range(B):
+        lat = (xf[b].astype(np.float64) @ wt).astype(np.float32)
+        cache[b, :, :dc] = _store(lat, dtype)
+    cache[:, :, dc:] = _store(_normal(rng, (B, T, dr)), dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dn + dr)
+    return PrefillCase(name, dtype, B, T, H, dc, dr, dn, dv, float(scale), q_nope, q_rope,
+                       w_uk, w_uv, cache, np.full(B, T, dtype=np.int32))
+
+
+# The five workloads: index -> (kind, keyword arguments).
+CONFIGS = {
+    0: ("decode", dict(name="tiny-f32 B1 H4 dc64 dr16 L128", dtype="f32", B=1, H=4, dc=64,
+                       dr=16, dn=32, dv=32, n_max=128)),
+    1: ("decode", dict(name="V3 bf16 B1 L4096", dtype="bf16", B=1, H=128, dc=512, dr=64,
+                       dn=128, dv=128, n_max=4096)),
+    2: ("decode", dict(name="V3 bf16 B32 ragged L~U[1,8192]", dtype="bf16", B=32, H=128,
+                       dc=512, dr=64, dn=128, dv=128, n_max=8192, ragged=True)),
+    3: ("decode", dict(name="V3 bf16 B8 L131072", dtype="bf16", B=8, H=128, dc=512, dr=64,
+                       dn=128, dv=128, n_max=131072)),
+    4: ("prefill", dict(name="V3 bf16 causal prefill B1 T4096", dtype="bf16", B=1, T=4096,
+                        H=128, dc=512, dr=64, dn=128, dv=128, d_model=7168)),
+}
+
+
+def make_config(index: int, seed: int | None = None):
+    kind, kw = CONFIGS[index]
+    seed = SEED_BASE + index if seed is None else seed
+    if kind == "decode":
+        return make_decode_case(seed=seed, **kw)
+    return make_prefill_case(seed=seed, **kw)

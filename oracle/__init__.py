@@ -1,0 +1,16 @@
+"""fp64 CPU oracle for MLA decode and naive causal prefill.
+
+Test infrastructure only: the tests, the smoke check and the benchmark's
+CPU-baseline leg use it; the product path (the HIP library and its binding)
+never imports, loads or calls anything in this package.
+"""
+from .oracle import (  # noqa: F401
+    OracleError,
+    build,
+    decode_absorbed,
+    decode_naive,
+    kv_cache_bytes,
+    max_threads,
+    prefill_naive,
+    set_threads,
+)

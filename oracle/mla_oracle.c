@@ -1,0 +1,301 @@
+/*
+ * mla_oracle.c -- plain fp64 CPU oracle for Multi-Head Latent Attention
+ * decode and naive causal prefill.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: it is used by the tests, by the smoke check and by the
+ * benchmark's CPU-baseline leg, and by nothing else.  It shares no code,
+ * header, table or helper with the HIP library.
+ *
+ * Every stored input (fp64, fp32 or bf16) is widened to double exactly; all
+ * arithmetic is double precision with plain sequential loops, in the order
+ * the definitions below state them.  Parallelism (OpenMP) is only over
+ * independent (sequence, head) pairs or query rows, so results do not depend
+ * on the thread count.
+ *
+ * Notation (the pages' own): c = latent cache row (d_c), k^R = decoupled
+ * RoPE key (d_r), W_UK[h] in R^{d_n x d_c} and W_UV[h] in R^{d_v x d_c}
+ * (row-major [H][d][d_c]), so k = W_UK[h] c and v = W_UV[h] c.
+ *
+ * Sources:
+ *  - "Deep-Dive: Multi-Head Latent Attention (MLA) and Low-Rank KV Cache
+ *    Compression in DeepSeek-V3", section 2 (per-head up-projections
+ *    k_{t,i} = W_UK(i) c_t, v_{t,i} = W_UV(i) c_t) and section 3 (scaled
+ *    dot-product softmax attention over the decompressed K and V).
+ *  - "mla-from-scratch" README, section "Absorption, and why RoPE breaks it"
+ *    (the score is an absorbed content term plus a decoupled positional term;
+ *    value-side absorption: attend over latents, up-project once).
+ *  - "DeepSeek MLA Architecture: How It Cuts KV Cache by 93%", section 2
+ *    (absorbed query q~ = W_UK^T q).
+ *  - songhuiming "MHA vs MLA" decode walk-through, MLA step 2 (the new
+ *    token's latent is appended to the cache before attention, so the cached
+ *    length counts the current token).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F64 = 0, OR_F32 = 1, OR_BF16 = 2 };
+
+typedef struct {
+    int64_t B, H, dc, dr, dn, dv;
+    int64_t ckv_sb, ckv_sn; /* element strides of the latent cache       */
+    int64_t kpe_sb, kpe_sn; /* element strides of the RoPE-key cache     */
+    int32_t dtype;          /* storage type of every input (OR_*)        */
+    int32_t reserved;
+    double scale;           /* softmax scale applied to the full score   */
+} oracle_dims;
+
+/* Exact widening of one stored element to double. */
+static double widen(const void *base, int dt, int64_t i)
+{
+    if (dt == OR_F64) return ((const double *)base)[i];
+    if (dt == OR_F32) return (double)((const float *)base)[i];
+    uint32_t u = ((uint32_t)((const uint16_t *)base)[i]) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static void widen_row(const void *base, int dt, int64_t off, int64_t n, double *dst)
+{
+    for (int64_t i = 0; i < n; ++i) dst[i] = widen(base, dt, off + i);
+}
+
+/* Softmax over s[0..L): p_n = exp(s_n - max) / sum_m exp(s_m - max).
+ * Returns sum_n p_n computed as its own sum (used by the normalisation pin). */
+static double softmax(const double *s, int64_t L, double *p)
+{
+    double m = -INFINITY;
+    for (int64_t n = 0; n < L; ++n) if (s[n] > m) m = s[n];
+    double z = 0.0;
+    for (int64_t n = 0; n < L; ++n) { p[n] = exp(s[n] - m); z += p[n]; }
+    double total = 0.0;
+    for (int64_t n = 0; n < L; ++n) { p[n] /= z; total += p[n]; }
+    return total;
+}
+
+/*
+ * O1 -- naive decode for one (b, h) with L cached rows: decompress every
+ * cached latent into k_n = [W_UK[h] c_n ; k^R_n] and v_n = W_UV[h] c_n,
+ * then out = sum_n softmax_n(scale * q . k_n) v_n with q = [q_nope ; q_rope].
+ * q_nope/q_rope are given as already-widened vectors.
+ */
+static double naive_one(const oracle_dims *d, const double *qn, const double *qr,
+                        const void *w_uk, const void *w_uv,
+                        const void *ckv, const void *kpe, int64_t b, int64_t h,
+                        int64_t L, double *out)
+{
+    const int dt = d->dtype;
+    const int64_t dc = d->dc, dr = d->dr, dn = d->dn, dv = d->dv;
+    for (int64_t i = 0; i < dv; ++i) out[i] = 0.0;
+    if (L <= 0) return 0.0;
+
+    double *c = malloc(sizeof(double) * (size_t)dc);
+    double *kr = malloc(sizeof(double) * (size_t)(dr > 0 ? dr : 1));
+    double *s = malloc(sizeof(double) * (size_t)L);
+    double *p = malloc(sizeof(double) * (size_t)L);
+    double *v = malloc(sizeof(double) * (size_t)dv);
+
+    /* scores against the decompressed keys */
+    for (int64_t n = 0; n < L; ++n) {
+        widen_row(ckv, dt, b * d->ckv_sb + n * d->ckv_sn, dc, c);
+        widen_row(kpe, dt, b * d->kpe_sb + n * d->kpe_sn, dr, kr);
+        double dot = 0.0;
+        for (int64_t i = 0; i < dn; ++i) {
+            double k = 0.0; /* k_nope[i] = sum_j W_UK[h][i][j] c[j] */
+            for (int64_t j = 0; j < dc; ++j)
+                k += widen(w_uk, dt, (h * dn + i) * dc + j) * c[j];
+            dot += qn[i] * k;
+        }
+        for (int64_t r = 0; r < dr; ++r) dot += qr[r] * kr[r];
+        s[n] = d->scale * dot;
+    }
+    double total = softmax(s, L, p);
+
+    /* weighted sum of the decompressed values */
+    for (int64_t n = 0; n < L; ++n) {
+        widen_row(ckv, dt, b * d->ckv_sb + n * d->ckv_sn, dc, c);
+        for (int64_t i = 0; i < dv; ++i) {
+            double acc = 0.0; /* v[i] = sum_j W_UV[h][i][j] c[j] */
+            for (int64_t j = 0; j < dc; ++j)
+                acc += widen(w_uv, dt, (h * dv + i) * dc + j) * c[j];
+            v[i] = acc;
+        }
+        for (int64_t i = 0; i < dv; ++i) out[i] += p[n] * v[i];
+    }
+    free(c); free(kr); free(s); free(p); free(v);
+    return total;
+}
+
+/*
+ * O2 -- absorbed decode for one (b, h): q~ = W_UK[h]^T q_nope,
+ * s_n = scale * (q~ . c_n + q_rope . k^R_n), the same softmax,
+ * o = sum_n p_n c_n (attention accumulated in latent space),
+ * out = W_UV[h] o (one up-projection at the end).
+ */
+static double absorbed_one(const oracle_dims *d, const double *qn, const double *qr,
+                           const void *w_uk, const void *w_uv,
+                           const void *ckv, const void *kpe, int64_t b, int64_t h,
+                           int64_t L, double *out)
+{
+    const int dt = d->dtype;
+    const int64_t dc = d->dc, dr = d->dr, dn = d->dn, dv = d->dv;
+    for (int64_t i = 0; i < dv; ++i) out[i] = 0.0;
+    if (L <= 0) return 0.0;
+
+    double *qa = malloc(sizeof(double) * (size_t)dc);
+    double *c = malloc(sizeof(double) * (size_t)dc);
+    double *kr = malloc(sizeof(double) * (size_t)(dr > 0 ? dr : 1));
+    double *s = malloc(sizeof(double) * (size_t)L);
+    double *p = malloc(sizeof(double) * (size_t)L);
+    double *o = malloc(sizeof(double) * (size_t)dc);
+
+    for (int64_t j = 0; j < dc; ++j) { /* q~[j] = sum_i W_UK[h][i][j] q_nope[i] */
+        double acc = 0.0;
+        for (int64_t i = 0; i < dn; ++i) acc += widen(w_uk, dt, (h * dn + i) * dc + j) * qn[i];
+        qa[j] = acc;
+    }
+    for (int64_t n = 0; n < L; ++n) {
+        widen_row(ckv, dt, b * d->ckv_sb + n * d->ckv_sn, dc, c);
+        widen_row(kpe, dt, b * d->kpe_sb + n * d->kpe_sn, dr, kr);
+        double content = 0.0, pos = 0.0;
+        for (int64_t j = 0; j < dc; ++j) content += qa[j] * c[j];
+        for (int64_t r = 0; r < dr; ++r) pos += qr[r] * kr[r];
+        s[n] = d->scale * (content + pos);
+    }
+    double total = softmax(s, L, p);
+    for (int64_t j = 0; j < dc; ++j) o[j] = 0.0;
+    for (int64_t n = 0; n < L; ++n) {
+        widen_row(ckv, dt, b * d->ckv_sb + n * d->ckv_sn, dc, c);
+        for (int64_t j = 0; j < dc; ++j) o[j] += p[n] * c[j];
+    }
+    for (int64_t i = 0; i < dv; ++i) { /* out[i] = sum_j W_UV[h][i][j] o[j] */
+        double acc = 0.0;
+        for (int64_t j = 0; j < dc; ++j) acc += widen(w_uv, dt, (h * dv + i) * dc + j) * o[j];
+        out[i] = acc;
+    }
+    free(qa); free(c); free(kr); free(s); free(p); free(o);
+    return total;
+}
+
+typedef double (*one_fn)(const oracle_dims *, const double *, const double *,
+                         const void *, const void *, const void *, const void *,
+                         int64_t, int64_t, int64_t, double *);
+
+static int check_dims(const oracle_dims *d)
+{
+    if (!d || d->B < 0 || d->H <= 0 || d->dc <= 0 || d->dr < 0 || d->dn <= 0 || d->dv <= 0) return 1;
+    if (d->dtype != OR_F64 && d->dtype != OR_F32 && d->dtype != OR_BF16) return 1;
+    return 0;
+}
+
+/* Decode over a list of (b, h) pairs (npairs entries of two int64), or over
+ * every pair in b-major order when pairs == NULL.  q_nope is [B][H][dn],
+ * q_rope is [B][H][dr].  out is [npairs][dv]; psum (optional) receives the
+ * separately summed softmax mass of each pair. */
+static int decode_common(one_fn fn, const oracle_dims *d, const void *q_nope, const void *q_rope,
+                         const void *w_uk, const void *w_uv, const void *ckv, const void *kpe,
+                         const int32_t *seqlens, const int64_t *pairs, int64_t npairs,
+                         double *out, double *psum)
+{
+    if (check_dims(d) || !out || !seqlens) return 1;
+    const int64_t total = pairs ? npairs : d->B * d->H;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t k = 0; k < total; ++k) {
+        const int64_t b = pairs ? pairs[2 * k] : k / d->H;
+        const int64_t h = pairs ? pairs[2 * k + 1] : k % d->H;
+        if (b < 0 || b >= d->B || h < 0 || h >= d->H) { bad = 1; continue; }
+        double *qn = malloc(sizeof(double) * (size_t)d->dn);
+        double *qr = malloc(sizeof(double) * (size_t)(d->dr > 0 ? d->dr : 1));
+        widen_row(q_nope, d->dtype, (b * d->H + h) * d->dn, d->dn, qn);
+        widen_row(q_rope, d->dtype, (b * d->H + h) * d->dr, d->dr, qr);
+        double t = fn(d, qn, qr, w_uk, w_uv, ckv, kpe, b, h, (int64_t)seqlens[b], out + k * d->dv);
+        if (psum) psum[k] = t;
+        free(qn); free(qr);
+    }
+    return bad;
+}
+
+int oracle_decode_naive(const oracle_dims *d, const void *q_nope, const void *q_rope,
+                        const void *w_uk, const void *w_uv, const void *ckv, const void *kpe,
+                        const int32_t *seqlens, const int64_t *pairs, int64_t npairs,
+                        double *out, double *psum)
+{
+    return decode_common(naive_one, d, q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens,
+                         pairs, npairs, out, psum);
+}
+
+int oracle_decode_absorbed(const oracle_dims *d, const void *q_nope, const void *q_rope,
+                           const void *w_uk, const void *w_uv, const void *ckv, const void *kpe,
+                           const int32_t *seqlens, const int64_t *pairs, int64_t npairs,
+                           double *out, double *psum)
+{
+    return decode_common(absorbed_one, d, q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens,
+                         pairs, npairs, out, psum);
+}
+
+/*
+ * O3 -- naive causal prefill.  T queries per sequence, q_nope [B][T][H][dn],
+ * q_rope [B][T][H][dr].  Query t of sequence b sits at position
+ * pos = L_b - T + t (the queries are the last T cached rows) and attends to
+ * cached rows 0..pos inclusive, through the same decompress-then-attend
+ * definition as O1.  rows lists (b, t) pairs; out is [nrows][H][dv].
+ */
+int oracle_prefill_naive(const oracle_dims *d, int64_t T, const void *q_nope, const void *q_rope,
+                         const void *w_uk, const void *w_uv, const void *ckv, const void *kpe,
+                         const int32_t *seqlens, const int64_t *rows, int64_t nrows, double *out)
+{
+    if (check_dims(d) || T <= 0 || !rows || !out || !seqlens) return 1;
+    int bad = 0;
+    const int64_t work = nrows * d->H;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t k = 0; k < work; ++k) {
+        const int64_t r = k / d->H, h = k % d->H;
+        const int64_t b = rows[2 * r], t = rows[2 * r + 1];
+        if (b < 0 || b >= d->B || t < 0 || t >= T || seqlens[b] < T) { bad = 1; continue; }
+        const int64_t pos = (int64_t)seqlens[b] - T + t;
+        double *qn = malloc(sizeof(double) * (size_t)d->dn);
+        double *qr = malloc(sizeof(double) * (size_t)(d->dr > 0 ? d->dr : 1));
+        widen_row(q_nope, d->dtype, ((b * T + t) * d->H + h) * d->dn, d->dn, qn);
+        widen_row(q_rope, d->dtype, ((b * T + t) * d->H + h) * d->dr, d->dr, qr);
+        naive_one(d, qn, qr, w_uk, w_uv, ckv, kpe, b, h, pos + 1, out + k * d->dv);
+        free(qn); free(qr);
+    }
+    return bad;
+}
+
+/*
+ * O4 -- latent-cache size in bytes: one row of d_c + d_r scalars per token
+ * per layer per sequence ("mla-from-scratch" README, cache table: MLA is
+ * d_c + d_rope = 512 + 64; eyestech-mla description, memory benchmark API).
+ */
+uint64_t oracle_kv_cache_bytes(int64_t n_layers, int64_t batch, int64_t seq_len,
+                               int64_t d_c, int64_t d_r, int64_t bytes_per_elem)
+{
+    return (uint64_t)n_layers * (uint64_t)batch * (uint64_t)seq_len *
+           (uint64_t)(d_c + d_r) * (uint64_t)bytes_per_elem;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

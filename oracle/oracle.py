@@ -1,0 +1,206 @@
+"""ctypes wrapper of the fp64 C oracle (``mla_oracle.c``).
+
+Test infrastructure only (see the package docstring).  Inputs are numpy
+arrays holding the exact stored values: float64, float32, or bfloat16 bit
+patterns as uint16.  The C code widens them to double itself.
+
+Parity status of each function (the pins live in ``tests/test_oracle_pins.py``):
+  decode_naive     pinned: torch fp64 scaled-dot-product attention over
+                   explicitly decompressed K/V, closed forms at L=1, uniform
+                   scores, softmax mass, cache permutation, padding.
+  decode_absorbed  pinned: equals decode_naive on the latent-width x length x
+                   RoPE-width grid, plus the same closed forms.
+  prefill_naive    pinned: torch fp64 attention with an explicit bottom-right
+                   causal mask; T=1 reduces to decode.
+  kv_cache_bytes   pinned: the cache tables printed on the pages.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mla_oracle.c")
+_LIB = os.path.join(_HERE, "libmla_oracle.so")
+
+OR_F64, OR_F32, OR_BF16 = 0, 1, 2
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("dc", ctypes.c_int64),
+        ("dr", ctypes.c_int64), ("dn", ctypes.c_int64), ("dv", ctypes.c_int64),
+        ("ckv_sb", ctypes.c_int64), ("ckv_sn", ctypes.c_int64),
+        ("kpe_sb", ctypes.c_int64), ("kpe_sn", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("scale", ctypes.c_double),
+    ]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP) into ``libmla_oracle.so``."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        vp, i64, dp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p
+        for name in ("oracle_decode_naive", "oracle_decode_absorbed"):
+            f = getattr(lib, name)
+            f.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, vp, vp, vp, vp, vp, i64, dp, dp]
+            f.restype = ctypes.c_int
+        lib.oracle_prefill_naive.argtypes = [ctypes.POINTER(_Dims), i64, vp, vp, vp, vp, vp, vp,
+                                             vp, vp, i64, dp]
+        lib.oracle_prefill_naive.restype = ctypes.c_int
+        lib.oracle_kv_cache_bytes.argtypes = [i64] * 6
+        lib.oracle_kv_cache_bytes.restype = ctypes.c_uint64
+        lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _code(a: np.ndarray) -> int:
+    if a.dtype == np.float64:
+        return OR_F64
+    if a.dtype == np.float32:
+        return OR_F32
+    if a.dtype == np.uint16:
+        return OR_BF16
+    raise OracleError(f"unsupported storage dtype {a.dtype}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _cache_view(cache: np.ndarray, dim: int):
+    """(base array, stride_b, stride_n) for a [B, N, >=dim] row-major view."""
+    if cache.ndim != 3:
+        raise OracleError("caches must be [B, N, width] views")
+    es = cache.dtype.itemsize
+    sb, sn, sc = (s // es for s in cache.strides)
+    if sc != 1 or cache.shape[2] != dim:
+        raise OracleError("cache rows must be contiguous and exactly the feature width")
+    return cache, sb, sn
+
+
+def _dims(q_nope, q_rope, w_uk, w_uv, ckv, kpe, scale, H_axis):
+    dt = _code(q_nope)
+    for a in (q_rope, w_uk, w_uv, ckv, kpe):
+        if _code(a) != dt:
+            raise OracleError("all inputs must share one storage dtype")
+    H, dn, dc = w_uk.shape
+    dv = w_uv.shape[1]
+    dr = q_rope.shape[-1]
+    _, csb, csn = _cache_view(ckv, dc)
+    _, ksb, ksn = _cache_view(kpe, dr) if dr > 0 else (kpe, 0, 0)
+    d = _Dims(B=ckv.shape[0], H=H, dc=dc, dr=dr, dn=dn, dv=dv, ckv_sb=csb, ckv_sn=csn,
+              kpe_sb=ksb, kpe_sn=ksn, dtype=dt, reserved=0, scale=float(scale))
+    return d
+
+
+def _base_ptr(a: np.ndarray):
+    # pointer to element [0,0,0] of a possibly strided cache view
+    return ctypes.c_void_p(a.__array_interface__["data"][0])
+
+
+def _decode(fname, q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, pairs):
+    q_nope = np.ascontiguousarray(q_nope)
+    q_rope = np.ascontiguousarray(q_rope)
+    w_uk = np.ascontiguousarray(w_uk)
+    w_uv = np.ascontiguousarray(w_uv)
+    d = _dims(q_nope, q_rope, w_uk, w_uv, ckv, kpe, scale, 1)
+    seq = np.ascontiguousarray(seqlens, dtype=np.int32)
+    if pairs is None:
+        n = d.B * d.H
+        pp = None
+    else:
+        pp = np.ascontiguousarray(np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
+        n = pp.shape[0]
+    out = np.zeros((n, d.dv), dtype=np.float64)
+    psum = np.zeros(n, dtype=np.float64)
+    rc = getattr(_load(), fname)(ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                 _ptr(w_uv), _base_ptr(ckv), _base_ptr(kpe), _ptr(seq),
+                                 _ptr(pp), n, _ptr(out), _ptr(psum))
+    if rc != 0:
+        raise OracleError(f"{fname} rejected its arguments")
+    if pairs is None:
+        return out.reshape(d.B, d.H, d.dv), psum.reshape(d.B, d.H)
+    return out, psum
+
+
+def decode_naive(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, pairs=None):
+    """O1: decompress-then-attend decode.  Returns (out, softmax_mass).
+
+    Shapes: q_nope [B,H,dn], q_rope [B,H,dr], w_uk [H,dn,dc], w_uv [H,dv,dc],
+    ckv [B,N,dc] and kpe [B,N,dr] (views into one buffer are fine),
+    seqlens [B] (cached length including the current token).
+    With ``pairs`` ([(b,h), ...]) only those pairs are computed and out is
+    [len(pairs), dv]; otherwise out is [B,H,dv].
+    """
+    return _decode("oracle_decode_naive", q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens,
+                   scale, pairs)
+
+
+def decode_absorbed(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, pairs=None):
+    """O2: absorbed decode (q~ = W_UK^T q_nope, latent-space attention, one
+    W_UV up-projection).  Same arguments and returns as :func:`decode_naive`."""
+    return _decode("oracle_decode_absorbed", q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens,
+                   scale, pairs)
+
+
+def prefill_naive(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, rows):
+    """O3: naive causal prefill for selected query rows.
+
+    q_nope [B,T,H,dn], q_rope [B,T,H,dr]; query t of sequence b sits at
+    position seqlens[b] - T + t and sees cached rows up to and including it.
+    rows = [(b, t), ...]; returns [len(rows), H, dv].
+    """
+    q_nope = np.ascontiguousarray(q_nope)
+    q_rope = np.ascontiguousarray(q_rope)
+    w_uk = np.ascontiguousarray(w_uk)
+    w_uv = np.ascontiguousarray(w_uv)
+    T = q_nope.shape[1]
+    d = _dims(q_nope, q_rope, w_uk, w_uv, ckv, kpe, scale, 2)
+    seq = np.ascontiguousarray(seqlens, dtype=np.int32)
+    rr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
+    out = np.zeros((rr.shape[0], d.H, d.dv), dtype=np.float64)
+    rc = _load().oracle_prefill_naive(ctypes.byref(d), T, _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                      _ptr(w_uv), _base_ptr(ckv), _base_ptr(kpe), _ptr(seq),
+                                      _ptr(rr), rr.shape[0], _ptr(out))
+    if rc != 0:
+        raise OracleError("oracle_prefill_naive rejected its arguments")
+    return out
+
+
+def kv_cache_bytes(n_layers, batch, seq_len, d_c=512, d_r=64, bytes_per_elem=2) -> int:
+    """O4: latent KV-cache bytes = layers * batch * seq * (d_c + d_r) * bytes."""
+    return int(_load().oracle_kv_cache_bytes(n_layers, batch, seq_len, d_c, d_r, bytes_per_elem))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))

@@ -1,0 +1,387 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+These run on the CPU only.  Each check is chosen so that a plausible mistake
+in the oracle (a dropped RoPE term, a transposed W_UK, a wrong scale, an
+off-by-one in the cached length or the causal mask, a broken softmax) fails
+at least one of them; the "mutation" tests at the end demonstrate that.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_12_amd import datagen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "cache_tables.json")
+
+
+def _rand_case(rng, B, H, dc, dr, dn, dv, N):
+    q_nope = rng.standard_normal((B, H, dn))
+    q_rope = rng.standard_normal((B, H, dr))
+    w_uk = rng.standard_normal((H, dn, dc)) / math.sqrt(dc)
+    w_uv = rng.standard_normal((H, dv, dc)) / math.sqrt(dc)
+    cache = rng.standard_normal((B, N, dc + dr))
+    return q_nope, q_rope, w_uk, w_uv, cache
+
+
+def _sdpa_decode(q_nope, q_rope, w_uk, w_uv, cache, seqlens, scale):
+    """Independent reference: materialise K and V per head (section 2 of the
+    distaisys deep-dive), then torch's fp64 scaled-dot-product attention."""
+    B, H, dn = q_nope.shape
+    dc = w_uk.shape[2]
+    out = np.zeros((B, H, w_uv.shape[1]))
+    for b in range(B):
+        L = int(seqlens[b])
+        if L == 0:
+            continue
+        c = torch.from_numpy(cache[b, :L, :dc])
+        kr = torch.from_numpy(cache[b, :L, dc:])
+        for h in range(H):
+            k = torch.cat([c @ torch.from_numpy(w_uk[h]).T, kr], dim=1)   # [L, dn+dr]
+            v = c @ torch.from_numpy(w_uv[h]).T                          # [L, dv]
+            q = torch.from_numpy(np.concatenate([q_nope[b, h], q_rope[b, h]]))[None, None]
+            o = torch.nn.functional.scaled_dot_product_attention(
+                q, k[None], v[None], scale=scale)
+            out[b, h] = o[0, 0].numpy()
+    return out
+
+
+def _rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# --------------------------------------------------------------------------
+# P8: cache arithmetic reproduces every table printed on the pages
+# --------------------------------------------------------------------------
+
+def test_cache_bytes_eyestech_telemetry():
+    g = json.load(open(GOLDEN))["eyestech_telemetry"]
+    for row in g["rows"]:
+        width = row["elems_per_token"]
+        dc, dr = row.get("d_c", width), row.get("d_r", 0)
+        assert dc + dr == width
+        for s, gib in zip(g["seq_lens"], row["gib"]):
+            nbytes = oracle.kv_cache_bytes(g["n_layers"], g["batch"], s, dc, dr, g["bytes_per_elem"])
+            assert round(nbytes / 2**30, 2) == pytest.approx(gib, abs=1e-9), (row["arch"], s)
+    mla = oracle.kv_cache_bytes(60, 8, 131072, 512, 64, 2)
+    mha32 = oracle.kv_cache_bytes(60, 8, 131072, 8192, 0, 2)
+    assert round(100 * (1 - mla / mha32), 2) == g["mla_reduction_vs_mha32_percent"]
+
+
+def test_cache_bytes_mla_from_scratch_table():
+    g = json.load(open(GOLDEN))["mla_from_scratch_table"]
+    mha = oracle.kv_cache_bytes(g["n_layers"], g["batch"], g["seq_len"], 8192, 0, 2)
+    for row in g["rows"]:
+        dc, dr = row.get("d_c", row["elems"]), row.get("d_r", 0)
+        nbytes = oracle.kv_cache_bytes(g["n_layers"], g["batch"], g["seq_len"], dc, dr,
+                                       g["bytes_per_elem"])
+        assert round(nbytes / 2**30, 2) == row["gib"], row["variant"]
+        assert round(mha / nbytes, 2) == row["ratio"], row["variant"]
+    with_rope = oracle.kv_cache_bytes(60, 1, 131072, 512, 64, 2)
+    without = oracle.kv_cache_bytes(60, 1, 131072, 512, 0, 2)
+    assert round((with_rope - without) / 2**30, 2) == g["rope_cost_gib"]
+    # 576 elements per token per layer
+    assert oracle.kv_cache_bytes(1, 1, 1, 512, 64, 1) == 576
+
+
+def test_cache_elems_songhuiming_99_tokens():
+    g = json.load(open(GOLDEN))["songhuiming_99_tokens"]
+    mla = oracle.kv_cache_bytes(g["n_layers"], 1, g["seq_len"], g["d_c"], 0, 1)
+    mha = oracle.kv_cache_bytes(g["n_layers"], 1, g["seq_len"], g["mha_width"], 0, 1)
+    assert mla == g["mla_elems"] and mha == g["mha_elems"]
+    assert round(2 * mla / 2**20, 1) == g["mla_mib_approx"]
+    assert round(2 * mha / 2**20) == g["mha_mib_approx"]
+
+
+# --------------------------------------------------------------------------
+# O1 (naive) against an independent library attention
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dc,dr,L", [(16, 0, 1), (16, 16, 7), (64, 16, 128), (64, 64, 33),
+                                     (512, 64, 7)])
+def test_naive_matches_torch_sdpa(dc, dr, L):
+    rng = np.random.default_rng(11 + dc + dr + L)
+    B, H, dn, dv = 2, 3, 8, 6
+    q_nope, q_rope, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, L + 3)
+    seqlens = np.array([L, max(L - 1, 0)], dtype=np.int32)
+    scale = 1.0 / math.sqrt(dn + dr)
+    out, psum = oracle.decode_naive(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc],
+                                    cache[:, :, dc:], seqlens, scale)
+    ref = _sdpa_decode(q_nope, q_rope, w_uk, w_uv, cache, seqlens, scale)
+    assert np.max(np.abs(out - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+# --------------------------------------------------------------------------
+# P1: absorbed == naive over latent widths x lengths (incl. 1) x RoPE widths
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dc", [16, 64, 512])
+@pytest.mark.parametrize("L", [1, 7, 128])
+@pytest.mark.parametrize("dr", [0, 16, 64])
+def test_absorbed_equals_naive(dc, L, dr):
+    rng = np.random.default_rng(1000 * dc + 10 * L + dr)
+    B, H, dn, dv = 2, 2, 16, 12
+    q_nope, q_rope, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, L)
+    seqlens = np.array([L, L], dtype=np.int32)
+    scale = 1.0 / math.sqrt(dn + dr)
+    args = (q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc], cache[:, :, dc:], seqlens, scale)
+    naive, _ = oracle.decode_naive(*args)
+    absorbed, _ = oracle.decode_absorbed(*args)
+    assert _rel(absorbed, naive) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# P2: a single cached token -> softmax weight exactly 1 -> out = W_UV c_0
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fn", [oracle.decode_naive, oracle.decode_absorbed])
+def test_single_token_selection_exact(fn):
+    rng = np.random.default_rng(5)
+    B, H, dc, dr, dn, dv = 2, 3, 64, 16, 32, 32
+    q_nope, q_rope, w_uk, _, cache = _rand_case(rng, B, H, dc, dr, dn, dv, 4)
+    # W_UV[h] row i selects latent channel sel[h][i]: out must be c_0[sel] exactly
+    sel = np.stack([rng.permutation(dc)[:dv] for _ in range(H)])
+    w_uv = np.zeros((H, dv, dc))
+    for h in range(H):
+        w_uv[h, np.arange(dv), sel[h]] = 1.0
+    seqlens = np.array([1, 1], dtype=np.int32)
+    out, psum = fn(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc], cache[:, :, dc:], seqlens, 0.3)
+    for b in range(B):
+        for h in range(H):
+            assert np.array_equal(out[b, h], cache[b, 0, sel[h]])
+    assert np.all(psum == 1.0)
+
+
+@pytest.mark.parametrize("fn", [oracle.decode_naive, oracle.decode_absorbed])
+def test_single_token_random_weights(fn):
+    rng = np.random.default_rng(6)
+    B, H, dc, dr, dn, dv = 1, 4, 64, 16, 32, 32
+    q_nope, q_rope, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, 1)
+    out, _ = fn(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc], cache[:, :, dc:],
+                np.array([1], np.int32), 0.25)
+    ref = np.einsum("hij,j->hi", w_uv, cache[0, 0, :dc])
+    assert _rel(out[0], ref) <= 1e-14
+
+
+# --------------------------------------------------------------------------
+# P3: softmax rows sum to one (directly, and through a constant channel)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("L", [1, 2, 77, 500])
+def test_softmax_mass_is_one(L):
+    rng = np.random.default_rng(L)
+    B, H, dc, dr, dn, dv = 1, 2, 16, 8, 8, 4
+    q_nope, q_rope, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, L)
+    q_nope *= 5.0  # sharpen the distribution
+    cache[:, :, 3] = 1.0
+    w_uv[:, 0, :] = 0.0
+    w_uv[:, 0, 3] = 1.0
+    for fn in (oracle.decode_naive, oracle.decode_absorbed):
+        out, psum = fn(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc], cache[:, :, dc:],
+                       np.array([L], np.int32), 0.5)
+        assert np.all(np.abs(psum - 1.0) <= 1e-14)
+        assert np.all(np.abs(out[:, :, 0] - 1.0) <= 1e-14)
+
+
+# --------------------------------------------------------------------------
+# P4: uniform scores -> plain mean of the up-projected latents
+# --------------------------------------------------------------------------
+
+def test_uniform_scores_give_mean():
+    rng = np.random.default_rng(9)
+    B, H, dc, dr, dn, dv, N = 3, 2, 64, 16, 32, 24, 50
+    _, _, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, N)
+    q_nope = np.zeros((B, H, dn))
+    q_rope = np.zeros((B, H, dr))
+    seqlens = np.array([50, 13, 1], dtype=np.int32)
+    for fn in (oracle.decode_naive, oracle.decode_absorbed):
+        out, _ = fn(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc], cache[:, :, dc:], seqlens, 1.0)
+        for b in range(B):
+            mean = cache[b, : seqlens[b], :dc].mean(axis=0)
+            ref = w_uv @ mean
+            assert _rel(out[b], ref) <= 1e-13
+
+
+# --------------------------------------------------------------------------
+# P5: one dominant token (huge logits, no overflow) -> W_UV c_{n*}
+# --------------------------------------------------------------------------
+
+def test_dominant_token_no_overflow():
+    rng = np.random.default_rng(21)
+    B, H, dc, dr, dn, dv, N = 1, 2, 64, 16, 32, 32, 40
+    _, _, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, N)
+    star = 17
+    q_nope = np.zeros((B, H, dn))
+    q_rope = np.stack([1e3 * cache[0, star, dc:]] * H)[None]
+    for fn in (oracle.decode_naive, oracle.decode_absorbed):
+        out, psum = fn(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc], cache[:, :, dc:],
+                       np.array([N], np.int32), 1.0)
+        assert np.all(np.isfinite(out)) and np.all(np.abs(psum - 1) < 1e-14)
+        ref = w_uv @ cache[0, star, :dc]
+        assert _rel(out[0], ref) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# P6/P7: order independence; padding rows beyond the length are never read
+# --------------------------------------------------------------------------
+
+def test_permutation_invariance():
+    rng = np.random.default_rng(31)
+    B, H, dc, dr, dn, dv, N = 1, 3, 64, 16, 32, 32, 61
+    q_nope, q_rope, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, N)
+    perm = rng.permutation(N)
+    c2 = cache[:, perm]
+    args = (q_nope, q_rope, w_uk, w_uv)
+    a, _ = oracle.decode_absorbed(*args, cache[:, :, :dc], cache[:, :, dc:], [N], 0.2)
+    b, _ = oracle.decode_absorbed(*args, c2[:, :, :dc], c2[:, :, dc:], [N], 0.2)
+    assert _rel(a, b) <= 1e-13
+
+
+@pytest.mark.parametrize("fn", [oracle.decode_naive, oracle.decode_absorbed])
+def test_nan_padding_ignored(fn):
+    rng = np.random.default_rng(41)
+    B, H, dc, dr, dn, dv, N = 2, 2, 16, 8, 8, 8, 30
+    q_nope, q_rope, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, N)
+    seqlens = np.array([11, 30], dtype=np.int32)
+    clean, _ = fn(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc], cache[:, :, dc:], seqlens, 0.3)
+    poisoned = cache.copy()
+    poisoned[0, 11:] = np.nan
+    dirty, _ = fn(q_nope, q_rope, w_uk, w_uv, poisoned[:, :, :dc], poisoned[:, :, dc:],
+                  seqlens, 0.3)
+    assert np.array_equal(clean, dirty)
+
+
+def test_zero_length_gives_zero_output():
+    rng = np.random.default_rng(42)
+    q_nope, q_rope, w_uk, w_uv, cache = _rand_case(rng, 2, 2, 16, 8, 8, 8, 5)
+    out, psum = oracle.decode_absorbed(q_nope, q_rope, w_uk, w_uv, cache[:, :, :16],
+                                       cache[:, :, 16:], np.array([0, 5], np.int32), 0.3)
+    assert np.all(out[0] == 0.0) and np.all(psum[0] == 0.0) and np.all(psum[1] != 0.0)
+
+
+def test_pairs_subset_and_thread_count_independence():
+    rng = np.random.default_rng(43)
+    B, H, dc, dr, dn, dv, N = 3, 5, 64, 16, 16, 16, 40
+    q_nope, q_rope, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, N)
+    args = (q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc], cache[:, :, dc:], [40, 3, 17], 0.4)
+    full, _ = oracle.decode_absorbed(*args)
+    pairs = [(2, 4), (0, 0), (1, 3)]
+    sub, _ = oracle.decode_absorbed(*args, pairs=pairs)
+    for k, (b, h) in enumerate(pairs):
+        assert np.array_equal(sub[k], full[b, h])
+    n = oracle.max_threads()
+    oracle.set_threads(1)
+    try:
+        single, _ = oracle.decode_absorbed(*args)
+    finally:
+        oracle.set_threads(n)
+    assert np.array_equal(single, full)
+
+
+def test_bf16_and_f32_storage_widen_exactly():
+    rng = np.random.default_rng(44)
+    B, H, dc, dr, dn, dv, N = 1, 2, 32, 8, 8, 8, 9
+    parts = _rand_case(rng, B, H, dc, dr, dn, dv, N)
+    bits = [datagen.bf16_bits(p.astype(np.float32)) for p in parts]
+    f32 = [datagen.bf16_to_f32(b) for b in bits]
+    f64 = [f.astype(np.float64) for f in f32]
+    res = []
+    for arrs in (bits, f32, f64):
+        q_nope, q_rope, w_uk, w_uv, cache = arrs
+        out, _ = oracle.decode_absorbed(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc],
+                                        cache[:, :, dc:], [N], 0.3)
+        res.append(out)
+    assert np.array_equal(res[0], res[2]) and np.array_equal(res[1], res[2])
+
+
+# --------------------------------------------------------------------------
+# O3: naive causal prefill
+# --------------------------------------------------------------------------
+
+def _sdpa_prefill(q_nope, q_rope, w_uk, w_uv, cache, seqlens, scale, b, rows):
+    T = q_nope.shape[1]
+    H = w_uk.shape[0]
+    dc = w_uk.shape[2]
+    L = int(seqlens[b])
+    c = torch.from_numpy(cache[b, :L, :dc])
+    kr = torch.from_numpy(cache[b, :L, dc:])
+    # bottom-right aligned causal mask: query t sees keys j <= L - T + t
+    t_idx = torch.arange(T)[:, None]
+    j_idx = torch.arange(L)[None, :]
+    mask = j_idx <= (L - T + t_idx)
+    out = np.zeros((len(rows), H, w_uv.shape[1]))
+    for h in range(H):
+        k = torch.cat([c @ torch.from_numpy(w_uk[h]).T, kr], dim=1)
+        v = c @ torch.from_numpy(w_uv[h]).T
+        q = torch.from_numpy(np.concatenate([q_nope[b, :, h], q_rope[b, :, h]], axis=1))
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q[None], k[None], v[None], attn_mask=mask[None], scale=scale)[0]
+        out[:, h] = o.numpy()[rows]
+    return out
+
+
+@pytest.mark.parametrize("T,L", [(1, 1), (5, 5), (9, 9), (4, 11), (16, 16)])
+def test_prefill_matches_masked_sdpa(T, L):
+    rng = np.random.default_rng(100 + T * 7 + L)
+    B, H, dc, dr, dn, dv = 1, 3, 32, 8, 16, 16
+    q_nope = rng.standard_normal((B, T, H, dn))
+    q_rope = rng.standard_normal((B, T, H, dr))
+    w_uk = rng.standard_normal((H, dn, dc)) / math.sqrt(dc)
+    w_uv = rng.standard_normal((H, dv, dc)) / math.sqrt(dc)
+    cache = rng.standard_normal((B, L, dc + dr))
+    seqlens = np.array([L], np.int32)
+    rows = list(range(T))
+    out = oracle.prefill_naive(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc], cache[:, :, dc:],
+                               seqlens, 0.3, [(0, t) for t in rows])
+    ref = _sdpa_prefill(q_nope, q_rope, w_uk, w_uv, cache, seqlens, 0.3, 0, rows)
+    assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+def test_prefill_row_equals_decode_prefix():
+    """P11 on the oracle: query row t equals a decode over the first pos_t+1 keys."""
+    rng = np.random.default_rng(7)
+    B, T, H, dc, dr, dn, dv, L = 1, 6, 2, 32, 8, 16, 16, 10
+    q_nope = rng.standard_normal((B, T, H, dn))
+    q_rope = rng.standard_normal((B, T, H, dr))
+    w_uk = rng.standard_normal((H, dn, dc)) / math.sqrt(dc)
+    w_uv = rng.standard_normal((H, dv, dc)) / math.sqrt(dc)
+    cache = rng.standard_normal((B, L, dc + dr))
+    pre = oracle.prefill_naive(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc], cache[:, :, dc:],
+                               [L], 0.3, [(0, t) for t in range(T)])
+    for t in range(T):
+        dec, _ = oracle.decode_naive(q_nope[:, t], q_rope[:, t], w_uk, w_uv, cache[:, :, :dc],
+                                     cache[:, :, dc:], [L - T + t + 1], 0.3)
+        assert np.array_equal(pre[t], dec[0])
+
+
+# --------------------------------------------------------------------------
+# Mutations: each plausible oracle mistake is caught by the pins above
+# --------------------------------------------------------------------------
+
+def test_pins_catch_plausible_mistakes():
+    """Simulate mistakes by mutating the inputs the oracle sees and check that
+    the independent SDPA reference would flag each of them."""
+    rng = np.random.default_rng(77)
+    B, H, dc, dr, dn, dv, N = 1, 2, 32, 16, 32, 32, 20
+    q_nope, q_rope, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, N)
+    scale = 1.0 / math.sqrt(dn + dr)
+    seq = np.array([N], np.int32)
+    ref = _sdpa_decode(q_nope, q_rope, w_uk, w_uv, cache, seq, scale)
+
+    def run(qn=q_nope, qr=q_rope, wk=w_uk, wv=w_uv, c=cache, L=seq, s=scale):
+        return oracle.decode_absorbed(qn, qr, wk, wv, c[:, :, :dc], c[:, :, dc:], L, s)[0]
+
+    assert _rel(run(), ref) <= 1e-12                      # the unmutated oracle passes
+    mutations = {
+        "transposed W_UK": dict(wk=np.ascontiguousarray(w_uk.transpose(0, 2, 1))),
+        "dropped RoPE term": dict(qr=np.zeros_like(q_rope)),
+        "scale 1/sqrt(d_n)": dict(s=1.0 / math.sqrt(dn)),
+        "length off by one": dict(L=seq - 1),
+        "W_UV of another head": dict(wv=w_uv[::-1].copy()),
+    }
+    for name, kw in mutations.items():
+        assert _rel(run(**kw), ref) > 1e-3, name
