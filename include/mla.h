@@ -1,0 +1,230 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) Multi-Head Latent Attention library.
+ *
+ * The library computes MLA decode over a compressed latent KV cache with
+ * query absorption, and a naive decompress-then-attend causal prefill.
+ *
+ * Notation (the pages' own): each cached token holds a latent row c of d_c
+ * scalars and a decoupled-RoPE key k^R of d_r scalars (512 + 64 = 576 for the
+ * DeepSeek-V3 shape: "mla-from-scratch" README, cache table, and the
+ * eyestech-mla description, "Key Architectural Highlights").  Per head h the
+ * up-projections are W_UK[h] in R^{d_n x d_c} and W_UV[h] in R^{d_v x d_c},
+ * stored row-major as [H][d_n][d_c] and [H][d_v][d_c], so the decompressed
+ * key and value are k = W_UK[h] c and v = W_UV[h] c ("Deep-Dive: Multi-Head
+ * Latent Attention (MLA) and Low-Rank KV Cache Compression in DeepSeek-V3",
+ * section 2).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE memory unless a comment says "host".  The caller
+ *    owns every buffer; the library never allocates, frees or synchronises.
+ *    Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *  - Tensors are row-major and dense unless strides are given.  Cache strides
+ *    are in elements.  The latent and RoPE caches may be two views into one
+ *    [B][n_max][d_c + d_r] buffer (kpe = ckv + d_c, both row strides d_c+d_r).
+ *  - `dtype` is the storage type of q, weights and caches; `out_dtype` that
+ *    of the output.  Arithmetic accumulates in fp32.  bf16 values are
+ *    produced with round-to-nearest-even.
+ *  - `seqlens[b]` (device, int32) is the cached length of sequence b and
+ *    counts the current token: the caller appends the new token's latent
+ *    and RoPE key before calling (songhuiming "MHA vs MLA" walk-through, MLA
+ *    step 2; eyestech-mla quickstart, where the returned cache grows by one
+ *    row).  Values are clamped to [0, n_max] on the device; a sequence with
+ *    length 0 gets an all-zero output row.  Rows at or beyond the length are
+ *    never read, so they may hold anything, NaN included.
+ *  - Functions return an mla_status.  All argument checks run on the host
+ *    before any launch; a rejected call enqueues nothing.  MLA_ERR_HIP means
+ *    a launch failed to enqueue; faults inside kernels surface at the
+ *    caller's next synchronisation.  mla_last_error() gives a per-thread
+ *    message for the last failing call.  The library never aborts and no C++
+ *    exception crosses this interface.  It holds no mutable global state and
+ *    may be called from several threads at once.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mla_status {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad stride or alignment */
+    MLA_ERR_UNSUPPORTED = 2, /* dimensions or dtype outside what the kernels implement   */
+    MLA_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned                */
+    MLA_ERR_HIP = 4          /* the HIP runtime refused a launch                          */
+} mla_status;
+
+typedef enum mla_dtype {
+    MLA_F32 = 0,
+    MLA_BF16 = 1
+} mla_dtype;
+
+/*
+ * Shape of a decode call.
+ *
+ * Supported dimensions:
+ *  - dtype MLA_F32: any heads >= 1, 1 <= d_c <= 1024, 0 <= d_r <= 256,
+ *    1 <= d_n <= 512, 1 <= d_v <= 1024 (scalar fp32 kernels).
+ *  - dtype MLA_BF16: d_c = 512, d_r = 64, d_n = 128, d_v = 128 (the
+ *    DeepSeek-V2/V3 shape) and heads a multiple of 128 (MFMA kernels; one
+ *    workgroup holds 128 heads).  n_max * row stride * 2 bytes of each
+ *    cache must stay below 4 GiB per sequence.
+ *    Cache pointers must be 16-byte aligned and row strides multiples of 8.
+ * Anything else returns MLA_ERR_UNSUPPORTED: the library refuses a shape it
+ * does not implement rather than computing something else (the
+ * "mla-from-scratch" README's absorbed model likewise refuses to build from
+ * a model it cannot fold correctly).
+ */
+typedef struct mla_decode_params {
+    int64_t batch;        /* B >= 1 sequences                                   */
+    int64_t heads;        /* H query heads, all sharing the one latent cache   */
+    int64_t d_c;          /* latent width                                      */
+    int64_t d_r;          /* decoupled RoPE key width                          */
+    int64_t d_n;          /* q_nope / decompressed key width per head          */
+    int64_t d_v;          /* value width per head                              */
+    int64_t n_max;        /* cache capacity (rows) per sequence                */
+    int64_t ckv_stride_b; /* elements between sequences in the latent cache    */
+    int64_t ckv_stride_n; /* elements between rows in the latent cache         */
+    int64_t kpe_stride_b; /* elements between sequences in the RoPE-key cache  */
+    int64_t kpe_stride_n; /* elements between rows in the RoPE-key cache       */
+    float softmax_scale;  /* multiplies the full score; 0 -> 1/sqrt(d_n + d_r) */
+    int32_t dtype;        /* mla_dtype of q_nope, q_rope, weights and caches   */
+    int32_t out_dtype;    /* mla_dtype of out                                   */
+    int32_t num_splits;   /* context splits per sequence; 0 -> chosen by size  */
+} mla_decode_params;
+
+/*
+ * Query absorption: q_abs[b][h][:] = W_UK[h]^T q_nope[b][h][:]
+ * ("DeepSeek MLA Architecture: How It Cuts KV Cache by 93%", section 2, the
+ * absorbed query; "mla-from-scratch" README, "Absorption, and why RoPE
+ * breaks it": the content score q . (W_UK c) equals (W_UK^T q) . c).
+ *   q_nope [B][H][d_n] (dtype), w_uk [H][d_n][d_c] (dtype),
+ *   q_abs  [B][H][d_c] fp32, written.
+ * Only batch, heads, d_c, d_n and dtype of `p` are read.
+ */
+mla_status mla_absorb_q(const mla_decode_params *p, const void *q_nope, const void *w_uk,
+                        float *q_abs, void *stream);
+
+/*
+ * Context splits per sequence that mla_decode will use for `p` (host
+ * function): p->num_splits if set, else the library's choice from the
+ * batch, head count and n_max.  0 if `p` is invalid.
+ */
+int mla_decode_num_splits(const mla_decode_params *p);
+
+/*
+ * Bytes of device workspace mla_decode needs for `p` (host function; 0 if
+ * `p` is invalid).  The size depends on batch, heads, n_max, dims and the
+ * split count, never on the seqlens values.
+ */
+size_t mla_decode_workspace_bytes(const mla_decode_params *p);
+
+/*
+ * Absorbed MLA decode, one new query token per sequence:
+ *   q~      = W_UK[h]^T q_nope[b][h]
+ *   s_n     = scale * (q~ . c[b][n] + q_rope[b][h] . k^R[b][n]),  n < L_b
+ *   p_n     = softmax_n(s)
+ *   o       = sum_n p_n c[b][n]            (attention in latent space)
+ *   out     = W_UV[h] o                    (one up-projection at the end)
+ * which equals softmax attention over the decompressed keys
+ * [W_UK[h] c_n ; k^R_n] and values W_UV[h] c_n ("mla-from-scratch" README,
+ * "Absorption, and why RoPE breaks it"; distaisys deep-dive, section 3).
+ *   q_nope    [B][H][d_n]  dtype
+ *   q_rope    [B][H][d_r]  dtype (already rotated for this position)
+ *   w_uk      [H][d_n][d_c], w_uv [H][d_v][d_c]  dtype
+ *   ckv_cache latent rows, element (b, n, j) at b*ckv_stride_b + n*ckv_stride_n + j
+ *   kpe_cache RoPE keys (already rotated), likewise with the kpe strides
+ *   seqlens   [B] int32 (see the conventions above)
+ *   out       [B][H][d_v]  out_dtype, written
+ *   workspace >= mla_decode_workspace_bytes(p) bytes, 256-byte aligned;
+ *             scratch owned by the caller, contents not preserved.
+ * Results are bitwise reproducible for a fixed split count (fixed-order
+ * reduction, no floating-point atomics).
+ */
+mla_status mla_decode(const mla_decode_params *p, const void *q_nope, const void *q_rope,
+                      const void *w_uk, const void *w_uv, const void *ckv_cache,
+                      const void *kpe_cache, const int32_t *seqlens, void *out,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * mla_decode with stage timing: identical work and results, and in addition
+ * records caller-created HIP events (hipEvent_t, host array of 4 handles, or
+ * NULL for none) on `stream`: events[0] before the absorb kernel, events[1]
+ * between absorb and the split-KV attention kernel, events[2] between that
+ * kernel and the merge/up-projection kernel, events[3] after the last
+ * kernel.  For benchmarks that time the attention kernel on its own.
+ */
+mla_status mla_decode_profiled(const mla_decode_params *p, const void *q_nope,
+                               const void *q_rope, const void *w_uk, const void *w_uv,
+                               const void *ckv_cache, const void *kpe_cache,
+                               const int32_t *seqlens, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream, void *const *events);
+
+/*
+ * Shape of a naive causal prefill call: T new query tokens per sequence,
+ * which are the last T of the L_b cached rows (L_b >= T).
+ * Supported: dtype MLA_BF16 with d_c = 512, d_r = 64, d_n = 128, d_v = 128,
+ * heads >= 1, tokens >= 1; dtype MLA_F32 with the fp32 decode limits.
+ */
+typedef struct mla_prefill_params {
+    int64_t batch;
+    int64_t tokens;       /* T query tokens per sequence                       */
+    int64_t heads;
+    int64_t d_c, d_r, d_n, d_v;
+    int64_t n_max;        /* cache capacity (rows) per sequence, >= tokens     */
+    int64_t ckv_stride_b, ckv_stride_n, kpe_stride_b, kpe_stride_n;
+    float softmax_scale;  /* 0 -> 1/sqrt(d_n + d_r)                             */
+    int32_t dtype;
+    int32_t out_dtype;
+    int32_t reserved;     /* must be 0                                          */
+} mla_prefill_params;
+
+/* Bytes of device workspace mla_prefill_naive needs (host; 0 if invalid). */
+size_t mla_prefill_workspace_bytes(const mla_prefill_params *p);
+
+/*
+ * Naive causal prefill: decompress every cached latent row into
+ * K_nope[b][n][h] = W_UK[h] c[b][n] and V[b][n][h] = W_UV[h] c[b][n] (kept in
+ * the workspace, i.e. materialised in HBM on purpose), then for query t at
+ * position pos = L_b - T + t attend over rows n <= pos with keys
+ * [K_nope ; k^R] and values V (distaisys deep-dive, section 3, with a causal
+ * mask that includes the diagonal; songhuiming walk-through, MLA step 2).
+ *   q_nope [B][T][H][d_n], q_rope [B][T][H][d_r]   dtype
+ *   w_uk, w_uv, ckv_cache, kpe_cache, seqlens        as for mla_decode
+ *   out    [B][T][H][d_v]                            out_dtype, written
+ * L_b is clamped to [0, n_max] on the device.  If L_b < T the leading
+ * queries get pos < 0, see no key, and their output rows are zero.
+ */
+mla_status mla_prefill_naive(const mla_prefill_params *p, const void *q_nope,
+                             const void *q_rope, const void *w_uk, const void *w_uv,
+                             const void *ckv_cache, const void *kpe_cache,
+                             const int32_t *seqlens, void *out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * Latent-cache size (host): n_layers * batch * seq_len * (d_c + d_r) *
+ * bytes_per_elem; 576 scalars per token per layer at the V3 shape
+ * (eyestech-mla description, programmatic memory benchmark API).  Returns 0
+ * for negative arguments.
+ */
+uint64_t mla_kv_cache_bytes(int64_t n_layers, int64_t batch, int64_t seq_len, int64_t d_c,
+                            int64_t d_r, int64_t bytes_per_elem);
+
+/* Static text for a status code (host). */
+const char *mla_status_string(mla_status s);
+
+/* Per-thread message describing the last failing call on this thread (host);
+ * an empty string if none failed.  Valid until the next call on the thread. */
+const char *mla_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

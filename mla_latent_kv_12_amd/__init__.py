@@ -1,0 +1,28 @@
+"""MI355X (gfx950) Multi-Head Latent Attention: absorbed decode over a latent
+KV cache and naive causal prefill, as hand-written HIP kernels behind a C ABI
+(include/mla.h).  This package is the thin Python binding over that library.
+"""
+from .binding import (  # noqa: F401
+    EXPORTS,
+    MLA_BF16,
+    MLA_ERR_HIP,
+    MLA_ERR_INVALID_ARG,
+    MLA_ERR_UNSUPPORTED,
+    MLA_ERR_WORKSPACE,
+    MLA_F32,
+    MLA_OK,
+    DecodeParams,
+    MLAError,
+    PrefillParams,
+    absorb_q,
+    decode,
+    decode_num_splits,
+    decode_params,
+    decode_workspace_bytes,
+    kv_cache_bytes,
+    prefill_naive,
+    prefill_params,
+    prefill_workspace_bytes,
+    status_string,
+    version,
+)

@@ -1,0 +1,266 @@
+"""Thin ctypes binding of ``libmla.so`` (the C ABI in include/mla.h).
+
+Argument marshalling only: every computation runs in the library's HIP
+kernels.  Torch tensors supply device memory and the current stream.  If the
+library is missing this module raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
+MLA_F32, MLA_BF16 = 0, 1
+
+EXPORTS = (
+    "mla_absorb_q",
+    "mla_decode_num_splits",
+    "mla_decode_workspace_bytes",
+    "mla_decode",
+    "mla_decode_profiled",
+    "mla_prefill_workspace_bytes",
+    "mla_prefill_naive",
+    "mla_kv_cache_bytes",
+    "mla_status_string",
+    "mla_last_error",
+    "mla_version",
+)
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("heads", ctypes.c_int64), ("d_c", ctypes.c_int64),
+        ("d_r", ctypes.c_int64), ("d_n", ctypes.c_int64), ("d_v", ctypes.c_int64),
+        ("n_max", ctypes.c_int64),
+        ("ckv_stride_b", ctypes.c_int64), ("ckv_stride_n", ctypes.c_int64),
+        ("kpe_stride_b", ctypes.c_int64), ("kpe_stride_n", ctypes.c_int64),
+        ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+    ]
+
+
+class PrefillParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("tokens", ctypes.c_int64), ("heads", ctypes.c_int64),
+        ("d_c", ctypes.c_int64), ("d_r", ctypes.c_int64), ("d_n", ctypes.c_int64),
+        ("d_v", ctypes.c_int64), ("n_max", ctypes.c_int64),
+        ("ckv_stride_b", ctypes.c_int64), ("ckv_stride_n", ctypes.c_int64),
+        ("kpe_stride_b", ctypes.c_int64), ("kpe_stride_n", ctypes.c_int64),
+        ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libmla.so`` (built by ``mla_latent_kv_12_amd.build``); raises if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MLAError(-1, f"{LIB_PATH} is missing: build it with "
+                               "`python -m mla_latent_kv_12_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.mla_absorb_q.argtypes = [ctypes.POINTER(DecodeParams), vp, vp, vp, vp]
+        L.mla_absorb_q.restype = ctypes.c_int
+        L.mla_decode_num_splits.argtypes = [ctypes.POINTER(DecodeParams)]
+        L.mla_decode_num_splits.restype = ctypes.c_int
+        L.mla_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeParams)]
+        L.mla_decode_workspace_bytes.restype = sz
+        L.mla_decode.argtypes = [ctypes.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp, vp, vp,
+                                 vp, sz, vp]
+        L.mla_decode.restype = ctypes.c_int
+        L.mla_decode_profiled.argtypes = [ctypes.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, sz, vp, vp]
+        L.mla_decode_profiled.restype = ctypes.c_int
+        L.mla_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillParams)]
+        L.mla_prefill_workspace_bytes.restype = sz
+        L.mla_prefill_naive.argtypes = [ctypes.POINTER(PrefillParams), vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, sz, vp]
+        L.mla_prefill_naive.restype = ctypes.c_int
+        L.mla_kv_cache_bytes.argtypes = [ctypes.c_int64] * 6
+        L.mla_kv_cache_bytes.restype = ctypes.c_uint64
+        L.mla_status_string.argtypes = [ctypes.c_int]
+        L.mla_status_string.restype = ctypes.c_char_p
+        L.mla_last_error.argtypes = []
+        L.mla_last_error.restype = ctypes.c_char_p
+        L.mla_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != MLA_OK:
+        raise MLAError(status, lib().mla_last_error().decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return MLA_F32
+    if t == torch.bfloat16:
+        return MLA_BF16
+    raise MLAError(MLA_ERR_UNSUPPORTED, f"dtype {t} is not supported (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _cache_strides(cache: torch.Tensor, width: int, what: str):
+    if cache.dim() != 3 or cache.shape[2] != width or cache.stride(2) != 1:
+        raise MLAError(MLA_ERR_INVALID_ARG, f"{what} must be a [B, N, {width}] view with unit "
+                                            "element stride")
+    return cache.stride(0), cache.stride(1)
+
+
+def decode_params(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, *, softmax_scale=None,
+                  out_dtype=None, num_splits=0) -> DecodeParams:
+    B, H, dn = q_nope.shape
+    dr = q_rope.shape[-1]
+    dc = w_uk.shape[2]
+    dv = w_uv.shape[1]
+    csb, csn = _cache_strides(ckv_cache, dc, "ckv_cache")
+    ksb, ksn = _cache_strides(kpe_cache, dr, "kpe_cache")
+    return DecodeParams(
+        batch=B, heads=H, d_c=dc, d_r=dr, d_n=dn, d_v=dv, n_max=ckv_cache.shape[1],
+        ckv_stride_b=csb, ckv_stride_n=csn, kpe_stride_b=ksb, kpe_stride_n=ksn,
+        softmax_scale=0.0 if softmax_scale is None else float(softmax_scale),
+        dtype=_dtype_code(q_nope.dtype),
+        out_dtype=_dtype_code(out_dtype if out_dtype is not None else q_nope.dtype),
+        num_splits=int(num_splits))
+
+
+def decode_num_splits(params: DecodeParams) -> int:
+    return int(lib().mla_decode_num_splits(ctypes.byref(params)))
+
+
+def decode_workspace_bytes(params: DecodeParams) -> int:
+    return int(lib().mla_decode_workspace_bytes(ctypes.byref(params)))
+
+
+def absorb_q(q_nope: torch.Tensor, w_uk: torch.Tensor, out: torch.Tensor | None = None,
+             stream=None) -> torch.Tensor:
+    """q_abs[b,h,:] = W_UK[h]^T q_nope[b,h,:] in fp32 (``mla_absorb_q``)."""
+    B, H, dn = q_nope.shape
+    dc = w_uk.shape[2]
+    if out is None:
+        out = torch.empty((B, H, dc), dtype=torch.float32, device=q_nope.device)
+    p = DecodeParams(batch=B, heads=H, d_c=dc, d_r=0, d_n=dn, d_v=1, n_max=1,
+                     dtype=_dtype_code(q_nope.dtype), out_dtype=MLA_F32)
+    qn, wk = q_nope.contiguous(), w_uk.contiguous()
+    _check(lib().mla_absorb_q(ctypes.byref(p), _ptr(qn), _ptr(wk), _ptr(out), _stream(stream)))
+    return out
+
+
+def decode(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, out=None,
+           workspace=None, softmax_scale=None, out_dtype=None, num_splits=0, stream=None,
+           params: DecodeParams | None = None, events=None):
+    """Absorbed MLA decode (``mla_decode``).  Shapes as in include/mla.h;
+    caches are [B, N_max, width] views (they may share one buffer).
+    ``events``: optional ctypes array of 4 hipEvent_t handles, recorded around
+    the three kernels (``mla_decode_profiled``)."""
+    if params is None:
+        params = decode_params(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache,
+                               softmax_scale=softmax_scale, out_dtype=out_dtype,
+                               num_splits=num_splits)
+    if out is None:
+        odt = torch.float32 if params.out_dtype == MLA_F32 else torch.bfloat16
+        out = torch.empty((params.batch, params.heads, params.d_v), dtype=odt,
+                          device=q_nope.device)
+    need = decode_workspace_bytes(params)
+    if need == 0:
+        _check(lib().mla_decode(ctypes.byref(params), None, None, None, None, None, None, None,
+                                None, None, 0, None))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
+    if events is None:
+        _check(lib().mla_decode(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                _ptr(w_uv), _ptr(ckv_cache), _ptr(kpe_cache), _ptr(seqlens),
+                                _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    else:
+        _check(lib().mla_decode_profiled(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope),
+                                         _ptr(w_uk), _ptr(w_uv), _ptr(ckv_cache),
+                                         _ptr(kpe_cache), _ptr(seqlens), _ptr(out),
+                                         _ptr(workspace), workspace.numel(), _stream(stream),
+                                         events))
+    return out
+
+
+def prefill_params(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, *, softmax_scale=None,
+                   out_dtype=None) -> PrefillParams:
+    B, T, H, dn = q_nope.shape
+    dr = q_rope.shape[-1]
+    dc = w_uk.shape[2]
+    dv = w_uv.shape[1]
+    csb, csn = _cache_strides(ckv_cache, dc, "ckv_cache")
+    ksb, ksn = _cache_strides(kpe_cache, dr, "kpe_cache")
+    return PrefillParams(
+        batch=B, tokens=T, heads=H, d_c=dc, d_r=dr, d_n=dn, d_v=dv, n_max=ckv_cache.shape[1],
+        ckv_stride_b=csb, ckv_stride_n=csn, kpe_stride_b=ksb, kpe_stride_n=ksn,
+        softmax_scale=0.0 if softmax_scale is None else float(softmax_scale),
+        dtype=_dtype_code(q_nope.dtype),
+        out_dtype=_dtype_code(out_dtype if out_dtype is not None else q_nope.dtype), reserved=0)
+
+
+def prefill_workspace_bytes(params: PrefillParams) -> int:
+    return int(lib().mla_prefill_workspace_bytes(ctypes.byref(params)))
+
+
+def prefill_naive(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, out=None,
+                  workspace=None, softmax_scale=None, out_dtype=None, stream=None,
+                  params: PrefillParams | None = None):
+    """Naive causal prefill (``mla_prefill_naive``): q [B,T,H,*] -> out [B,T,H,d_v]."""
+    if params is None:
+        params = prefill_params(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache,
+                                softmax_scale=softmax_scale, out_dtype=out_dtype)
+    if out is None:
+        odt = torch.float32 if params.out_dtype == MLA_F32 else torch.bfloat16
+        out = torch.empty((params.batch, params.tokens, params.heads, params.d_v), dtype=odt,
+                          device=q_nope.device)
+    need = prefill_workspace_bytes(params)
+    if need == 0:
+        _check(lib().mla_prefill_naive(ctypes.byref(params), None, None, None, None, None, None,
+                                       None, None, None, 0, None))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
+    _check(lib().mla_prefill_naive(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                   _ptr(w_uv), _ptr(ckv_cache), _ptr(kpe_cache), _ptr(seqlens),
+                                   _ptr(out), _ptr(workspace), workspace.numel(),
+                                   _stream(stream)))
+    return out
+
+
+def kv_cache_bytes(n_layers, batch, seq_len, d_c=512, d_r=64, bytes_per_elem=2) -> int:
+    return int(lib().mla_kv_cache_bytes(n_layers, batch, seq_len, d_c, d_r, bytes_per_elem))
+
+
+def status_string(status: int) -> str:
+    return lib().mla_status_string(status).decode()
+
+
+def version() -> int:
+    return int(lib().mla_version())
+
+
+def default_scale(d_n: int, d_r: int) -> float:
+    return 1.0 / math.sqrt(d_n + d_r)

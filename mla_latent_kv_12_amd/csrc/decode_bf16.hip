@@ -1,0 +1,649 @@
+// decode_bf16.hip -- absorbed MLA decode for the DeepSeek-V2/V3 shape on
+// gfx950: d_c = 512 latent, d_r = 64 decoupled RoPE key, d_n = d_v = 128,
+// heads a multiple of 128, bf16 storage, fp32 accumulation.
+//
+// Three kernels on the caller's stream:
+//   1. absorb:  Qa[b][h] = [ W_UK[h]^T q_nope[b][h] ; q_rope[b][h] ]   (bf16, 576 wide)
+//      ("DeepSeek MLA Architecture: How It Cuts KV Cache by 93%", section 2:
+//      the up-projection is folded into the query, so keys are never built.)
+//   2. split-KV flash-decode: one workgroup per (context split, 128 heads,
+//      sequence).  Cache rows (576 bf16 = 1152 B) are streamed into LDS once
+//      and shared by all 128 heads -- the absorbed decode is MQA-shaped.
+//      Scores S^T[token][head] = C . Qa^T and the latent accumulation
+//      O^T[col][head] += C^T . P^T both run on v_mfma_f32_32x32x16_bf16.
+//      Online softmax in log2 units with a lazily raised running max.
+//      ("mla-from-scratch" README, "Absorption, and why RoPE breaks it":
+//      score = absorbed content term + decoupled positional term; attend
+//      over the latents and up-project once at the end.)
+//   3. merge + up-project: fixed-order (ascending split) combination of the
+//      split partials, then out = W_UV[h] o_lat.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int DC = 512, DR = 64, DQK = DC + DR, DN = 128, DV = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// 1. absorb: grid (4 column quarters, H, ceil(B/8)), 256 threads.
+//    Wave w reduces rows i in [32w, 32w+32) of W_UK[h]; lane holds 2 columns.
+// ---------------------------------------------------------------------------
+constexpr int kAbsorbBatch = 8;
+
+__global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, const uint16_t *q_nope,
+                                                          const uint16_t *q_rope,
+                                                          const uint16_t *w_uk, uint16_t *qa)
+{
+    const int qtr = blockIdx.x, h = blockIdx.y, b0 = blockIdx.z * kAbsorbBatch;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int nb = min(kAbsorbBatch, B - b0);
+    __shared__ float qs[kAbsorbBatch][DN];
+    __shared__ float red[4][kAbsorbBatch][128];
+
+    for (int e = tid; e < kAbsorbBatch * DN; e += 256) {
+        const int bb = e / DN, i = e % DN;
+        qs[bb][i] = bb < nb ? bf16lo(q_nope[(static_cast<int64_t>(b0 + bb) * H + h) * DN + i]) : 0.f;
+    }
+    __syncthreads();
+
+    const int col = qtr * 128 + 2 * lane;
+    float acc[kAbsorbBatch][2];
+#pragma unroll
+    for (int bb = 0; bb < kAbsorbBatch; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
+    const uint32_t *wrow = reinterpret_cast<const uint32_t *>(w_uk + (static_cast<int64_t>(h) * DN + 32 * w) * DC + col);
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) {
+        const uint32_t wv = wrow[i * (DC / 2)];
+        const float w0 = bf16lo(wv), w1 = bf16hi(wv);
+#pragma unroll
+        for (int bb = 0; bb < kAbsorbBatch; ++bb) {
+            const float q = qs[bb][32 * w + i];
+            acc[bb][0] = fmaf(w0, q, acc[bb][0]);
+            acc[bb][1] = fmaf(w1, q, acc[bb][1]);
+        }
+    }
+#pragma unroll
+    for (int bb = 0; bb < kAbsorbBatch; ++bb) {
+        red[w][bb][2 * lane] = acc[bb][0];
+        red[w][bb][2 * lane + 1] = acc[bb][1];
+    }
+    __syncthreads();
+    // 8 batches x 128 columns = 1024 outputs, 4 per thread, summed in wave order.
+    for (int e = tid; e < kAbsorbBatch * 128; e += 256) {
+        const int bb = e / 128, c = e % 128;
+        if (bb >= nb) continue;
+        const float v = ((red[0][bb][c] + red[1][bb][c]) + red[2][bb][c]) + red[3][bb][c];
+        reinterpret_cast<__bf16 *>(qa)[(static_cast<int64_t>(b0 + bb) * H + h) * DQK + qtr * 128 + c] =
+            static_cast<__bf16>(v);
+    }
+    if (qtr == 0) {  // RoPE query channels are copied unchanged
+        for (int e = tid; e < nb * DR; e += 256) {
+            const int bb = e / DR, r = e % DR;
+            qa[(static_cast<int64_t>(b0 + bb) * H + h) * DQK + DC + r] =
+                q_rope[(static_cast<int64_t>(b0 + bb) * H + h) * DR + r];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 2. split-KV flash-decode
+//
+// Workgroup = 4 waves = 128 heads of one sequence over one context split.
+// Cache tiles of 32 rows x 576 bf16 (36 KiB) are copied HBM -> LDS with
+// direct-to-LDS 16-byte buffer loads (buffer_load_dwordx4 ... lds) into three
+// LDS buffers, so two tiles are in flight while one is consumed.  The buffer
+// descriptor's range ends at the split's last row: rows past it arrive as
+// zeros (weight zero, and they can never inject NaN/Inf).  The three buffers
+// rotate; the cross-wave hand-off is an explicit "wait for my tile loads,
+// then s_barrier".
+//
+// LDS tile layout: latent rows (1024 B) then RoPE-key rows (128 B), each row's
+// 16-byte chunks XOR-swizzled (latent: chunk ^ (row & 15) inside aligned
+// groups of 16; RoPE: chunk ^ (row & 7)) so that the 32 rows the score MFMA
+// reads at one column land in distinct banks.
+//
+// Registers: the absorbed query's 512 latent channels stay in VGPRs as the
+// score MFMA's B operand (128 per lane); its 64 RoPE channels live in LDS;
+// the 512 x 32 fp32 latent accumulator of the wave's heads fills the 256
+// AGPRs.
+//
+// Softmax: scores are kept in log2 units (scale * log2(e) folded in).  The
+// reference maximum m_ref of each head is fixed by the split's first tile;
+// later weights are exp2(s - m_ref) <= 2^64, which bf16 and the fp32
+// accumulators hold without overflow, so the accumulators are never
+// rescaled.  Should a later score exceed m_ref + 64, the head's partial is
+// marked (NaN maximum) and the merge kernel recomputes that (split, head)
+// with the split's true maximum; ordinary inputs never take that path.
+// ---------------------------------------------------------------------------
+constexpr int kTile = 32;                      // tokens per LDS tile (== split granule)
+constexpr int kLatRow = DC * 2;                // 1024 B
+constexpr int kRopeRow = DR * 2;               // 128 B
+constexpr int kRopeBase = kTile * kLatRow;     // 32768: RoPE rows follow the latent rows
+constexpr int kTileBytes = kTile * (kLatRow + kRopeRow);  // 36864
+constexpr int kThreadsDec = 256;               // 4 waves x 32 heads
+constexpr int kLoadsPerWave = 9;               // 8 latent rows + 1/4 of the RoPE rows
+constexpr int kQRopeBytes = 32 * kRopeRow;     // one wave's 32 heads x 64 RoPE channels
+static_assert(kTile == 4 * 8, "each wave loads 8 latent rows per tile");
+static_assert(kTile * kRopeRow == 4 * 64 * 16, "each wave loads one quarter of the RoPE rows");
+static_assert(kTile == kSplitGranule, "split boundaries must align to tiles");
+static_assert(3 * kTileBytes + 4 * kQRopeBytes + 16 <= 160 * 1024, "LDS budget");
+constexpr float kRefSlack = 64.0f;             // log2 headroom above the reference maximum
+
+// Wait until at most N of this wave's vector-memory operations are in flight
+// and its LDS operations are done, then meet the other waves at the barrier.
+// The "memory" clobber keeps the compiler from moving LDS accesses across.
+template <int N>
+__device__ __forceinline__ void wait_then_barrier()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const unsigned char lds_byte;
+
+// Buffer descriptor (gfx9 layout) over [base, base + range): 48-bit base,
+// stride 0, byte range, and the raw 32-bit data-format word.  Loads past the
+// range return zeros.  Every field is wave-uniform (SGPRs).
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t range)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+    r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(range));
+    r[3] = 0x00020000;
+    return r;
+}
+
+// One wave-wide direct-to-LDS load: lane i's 16 bytes at byte offset voff of
+// the buffer land at LDS address lds_dst + 16 i.  Issued as inline assembly
+// so that the compiler does not track it: it would otherwise make every later
+// LDS read wait for all loads in flight.  Completion is awaited explicitly
+// (wait_then_barrier) before any wave reads the destination.  M0 carries the
+// LDS base; this kernel has no other M0 user.  The instruction has no
+// register result.
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, const unsigned char *lds_dst, unsigned voff)
+{
+    const unsigned m0v = __builtin_amdgcn_readfirstlane(
+        static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_byte *)lds_dst)));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(m0v), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// Opaque copy: the compiler must recompute what depends on the result inside
+// the loop instead of keeping it live across the whole loop in a register.
+__device__ __forceinline__ int opaque(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+__global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
+    int H, int S, int64_t n_max, const uint16_t *__restrict__ ckv, int64_t ckv_sb, int ckv_rowb,
+    const uint16_t *__restrict__ kpe, int64_t kpe_sb, int kpe_rowb,
+    const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ qa, float c2,
+    float *__restrict__ part_o, float *__restrict__ part_ml)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char tiles[3 * kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char qrope_lds[4 * kQRopeBytes];
+
+    const int sp = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int half = lane >> 5, l32 = lane & 31;
+    const int hq = hg * 128 + w * 32 + l32;  // this lane's head (score column)
+
+    const int L = static_cast<int>(min<int64_t>(max(seqlens[b], 0), n_max));
+    const int ntiles_seq = (L + kTile - 1) / kTile;
+    const int tps = (ntiles_seq + S - 1) / S;
+    const int start = sp * tps * kTile;
+    const int end = min(L, start + tps * kTile);
+    const int64_t prow = (static_cast<int64_t>(b) * S + sp) * H + hq;
+
+    if (start >= end) {  // empty split: weight zero in the merge, O never read
+        if (half == 0) {
+            part_ml[prow * 2 + 0] = -INFINITY;
+            part_ml[prow * 2 + 1] = 0.f;
+        }
+        return;
+    }
+    const int ntiles = (end - start + kTile - 1) / kTile;
+
+    // Absorbed query of this lane's head as the score MFMA's B operand:
+    // B[k][j = head], lane holds k = 16 s + 8 half + 0..7.  Latent channels
+    // (s < 32) in registers; RoPE channels (s = 32..35) in this wave's LDS
+    // slice, row l32, chunks swizzled by (l32 & 7).
+    const uint16_t *qrow = qa + (static_cast<int64_t>(b) * H + hq) * DQK + 8 * half;
+    u32x4 qreg[DC / 16];
+#pragma unroll
+    for (int s = 0; s < DC / 16; ++s) qreg[s] = *reinterpret_cast<const u32x4 *>(qrow + 16 * s);
+    unsigned char *qr = qrope_lds + w * kQRopeBytes;
+#pragma unroll
+    for (int s = 0; s < DR / 16; ++s)
+        *reinterpret_cast<u32x4 *>(qr + l32 * kRopeRow + 16 * ((2 * s + half) ^ (l32 & 7))) =
+            *reinterpret_cast<const u32x4 *>(qrow + DC + 16 * s);
+    // Let the query loads land here, once: the compiler then knows they are
+    // complete and puts no wait on them inside the tile loop (where any
+    // vector-memory wait would also wait for the tile loads in flight).
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // Buffer descriptors covering rows [0, end) of this sequence.
+    const i32x4 rs_lat =
+        make_rsrc(ckv + static_cast<int64_t>(b) * ckv_sb, static_cast<uint32_t>(end) * ckv_rowb);
+    const i32x4 rs_rope =
+        make_rsrc(kpe + static_cast<int64_t>(b) * kpe_sb, static_cast<uint32_t>(end) * kpe_rowb);
+
+    // Issue this wave's nine loads of the tile starting at token n0.
+    // Latent load k fills LDS row r = 8 w + k: LDS chunk = lane, holding the
+    // source chunk lane ^ (r & 15).  The RoPE load fills RoPE rows 8 w .. 8 w + 7:
+    // lane -> row 8 w + lane / 8, LDS chunk lane % 8 holding source chunk
+    // (lane % 8) ^ (row & 7).
+    auto issue_tile = [&](int n0, unsigned char *dst) {
+        const int ln = opaque(lane);
+        const unsigned base = static_cast<unsigned>(n0) * static_cast<unsigned>(ckv_rowb);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int r = 8 * w + k;
+            const unsigned src = base + static_cast<unsigned>(r * ckv_rowb + 16 * (ln ^ (r & 15)));
+            lds_dma16(rs_lat, dst + r * kLatRow, src);
+        }
+        const int rr = 8 * w + (ln >> 3);
+        const unsigned rsrc_off = static_cast<unsigned>(n0) * static_cast<unsigned>(kpe_rowb) +
+                                  static_cast<unsigned>(rr * kpe_rowb + 16 * ((ln & 7) ^ (rr & 7)));
+        lds_dma16(rs_rope, dst + kRopeBase + w * 8 * kRopeRow, rsrc_off);
+    };
+
+    f32x16 oacc[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[q][r] = 0.f;
+    float m_ref = -INFINITY;  // per head (lane column): the first tile's maximum
+    float l_run = 0.f;
+    bool over = false;        // a later score exceeded m_ref + 64 for this head
+
+    // One tile: wait for it, hand the next-but-one tile's loads to the
+    // hardware, then scores, softmax weights and the latent accumulation.
+    auto tile_step = [&](int t, const unsigned char *tb, unsigned char *next_dst) {
+        const int n0 = start + t * kTile;
+        if (t + 1 < ntiles)
+            wait_then_barrier<kLoadsPerWave>();
+        else
+            wait_then_barrier<0>();
+        if (t + 2 < ntiles) issue_tile(n0 + 2 * kTile, next_dst);
+
+        // ---- scores: S^T[token i][head j] = sum_k C[i][k] Qa[j][k] ----
+        const int ln = opaque(lane);
+        const int l3 = ln & 31, hf = ln >> 5;
+        const int g16 = (hf ^ l3) & 15;
+        const unsigned char *arow = tb + l3 * kLatRow;
+        const unsigned char *rrow = tb + kRopeBase + l3 * kRopeRow;
+        const unsigned char *qrr = qr + l3 * kRopeRow;
+        auto a_at = [&](int s) -> u32x4 {
+            if (s < DC / 16)
+                return *reinterpret_cast<const u32x4 *>(arow + 256 * (s >> 3) + 16 * ((2 * (s & 7)) ^ g16));
+            return *reinterpret_cast<const u32x4 *>(rrow + 16 * ((2 * (s - DC / 16) + hf) ^ (l3 & 7)));
+        };
+        f32x16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        u32x4 abuf[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) abuf[s] = a_at(s);
+#pragma unroll
+        for (int s = 0; s < DQK / 16; ++s) {
+            u32x4 bq;
+            if (s < DC / 16)
+                bq = qreg[s];
+            else
+                bq = *reinterpret_cast<const u32x4 *>(qrr + 16 * ((2 * (s - DC / 16) + hf) ^ (l3 & 7)));
+            sacc = mfma32(abuf[s & 3], bq, sacc);
+            if (s + 4 < DQK / 16) abuf[s & 3] = a_at(s + 4);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // sacc[r] is token 8 (r/4) + 4 half + r%4 of the tile, head l32.
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int tok = n0 + 8 * (r >> 2) + 4 * half + (r & 3);
+            sacc[r] = tok < end ? sacc[r] * c2 : -INFINITY;
+            tmax = fmaxf(tmax, sacc[r]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        if (t == 0) m_ref = tmax;
+        over |= tmax > m_ref + kRefSlack;
+
+        u32x4 pk[2];
+        float psum = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float p0 = exp2f(sacc[8 * ks + 2 * p] - m_ref);
+                const float p1 = exp2f(sacc[8 * ks + 2 * p + 1] - m_ref);
+                const uint32_t wpk = pack_bf16(p0, p1);
+                psum += bf16lo(wpk) + bf16hi(wpk);  // mass of the rounded weights
+                pk[ks][p] = wpk;
+            }
+        l_run += psum;
+
+        // ---- O^T[col][head] += C^T[col][token] P^T[token][head] ----
+        // K step ks covers tokens 16 ks + {0..3, 8..11} + 4 half for this
+        // lane, where the score accumulator left them.  j-block q = 4u + v
+        // holds latent column 128 u + 4 i + v in its row i; lane l32 reads
+        // columns 128 u + 4 l32 .. + 3 = logical chunk 16 u + l32 / 2.
+        auto v_at = [&](int e, int ks, int u) -> u32x2 {
+            const int rl = 8 * (e >> 2) + 4 * hf + (e & 3);  // row within a 16-row half tile
+            const int off = rl * kLatRow + 16 * (((l3 >> 1) ^ rl) & 15) + 8 * (l3 & 1);
+            return *reinterpret_cast<const u32x2 *>(tb + off + 16 * ks * kLatRow + 256 * u);
+        };
+        u32x2 R[8], Rn[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) R[e] = v_at(e, 0, 0);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {  // g = 4 ks + u: one group of four j-blocks
+            const int ks = g >> 2, u = g & 3;
+            if (g + 1 < 8) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) Rn[e] = v_at(e, (g + 1) >> 2, (g + 1) & 3);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint32_t sel = (v & 1) ? 0x07060302u : 0x05040100u;
+                u32x4 a;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t x = (v < 2) ? R[2 * p][0] : R[2 * p][1];
+                    const uint32_t y = (v < 2) ? R[2 * p + 1][0] : R[2 * p + 1][1];
+                    a[p] = __builtin_amdgcn_perm(y, x, sel);  // {x.half(v), y.half(v)}
+                }
+                oacc[4 * u + v] = mfma32(a, pk[ks], oacc[4 * u + v]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) R[e] = Rn[e];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    issue_tile(start, tiles);
+    if (ntiles > 1) issue_tile(start + kTile, tiles + kTileBytes);
+    int buf = 0;  // tile t lives in buffer t % 3
+    for (int t = 0; t < ntiles; ++t) {
+        const int nxt = buf == 0 ? 2 : buf - 1;  // (t + 2) % 3
+        tile_step(t, tiles + buf * kTileBytes, tiles + nxt * kTileBytes);
+        buf = buf == 2 ? 0 : buf + 1;
+    }
+
+    // ---- write the split partial: un-normalised O, reference max, mass ----
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    float *orow = part_o + prow * DC;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = 8 * (r >> 2) + 4 * half + (r & 3);
+            f32x4 v4 = {oacc[4 * u + 0][r], oacc[4 * u + 1][r], oacc[4 * u + 2][r], oacc[4 * u + 3][r]};
+            *reinterpret_cast<f32x4 *>(orow + 128 * u + 4 * i) = v4;
+        }
+    if (half == 0) {
+        // NaN marks a head whose weights could overflow: the merge kernel
+        // recomputes that (split, head) with the split's true maximum.
+        part_ml[prow * 2 + 0] = over ? __builtin_nanf("") : m_ref;
+        part_ml[prow * 2 + 1] = l_tot;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. merge + up-project: grid (H, ceil(B/4)), 256 threads.
+//    For each sequence: M = max_s m_s, w_s = 2^(m_s - M),
+//    o_lat = sum_s w_s O_s / sum_s w_s l_s in ascending s, then
+//    out = W_UV[h] o_lat.  A split marked with a NaN maximum (its weights
+//    could have overflowed) is first recomputed here for this head with the
+//    split's true maximum, in plain fp32.
+// ---------------------------------------------------------------------------
+constexpr int kMergeBatch = 4;
+
+struct CacheView {
+    int64_t n_max;
+    const uint16_t *ckv;
+    int64_t ckv_sb, ckv_sn;  // elements
+    const uint16_t *kpe;
+    int64_t kpe_sb, kpe_sn;
+    const int32_t *seqlens;
+    const uint16_t *qa;      // [B][H][576] absorbed queries (bf16)
+    float c2;                // softmax scale * log2(e)
+};
+
+__device__ float block_reduce(float v, float *red, bool is_max)
+{
+    for (int o = 32; o > 0; o >>= 1) {
+        const float u = __shfl_xor(v, o);
+        v = is_max ? fmaxf(v, u) : v + u;
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int i = 1; i < 4; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+    return r;
+}
+
+// Recompute one (sequence, split, head) partial: scores against the split's
+// rows, their maximum, then weights, mass and the weighted latent sum.
+__device__ void recompute_partial(const CacheView &cv, int H, int S, int b, int sp, int h,
+                                  float *part_o, float *part_ml)
+{
+    __shared__ float q[DQK];
+    __shared__ float pw[256];
+    __shared__ float red[4];
+    const int tid = threadIdx.x;
+    const int L = static_cast<int>(min<int64_t>(max(cv.seqlens[b], 0), cv.n_max));
+    const int ntiles_seq = (L + kSplitGranule - 1) / kSplitGranule;
+    const int tps = (ntiles_seq + S - 1) / S;
+    const int start = sp * tps * kSplitGranule;
+    const int end = min(L, start + tps * kSplitGranule);
+    const uint16_t *qrow = cv.qa + (static_cast<int64_t>(b) * H + h) * DQK;
+    for (int k = tid; k < DQK; k += 256) q[k] = bf16lo(qrow[k]);
+    __syncthreads();
+    auto score = [&](int n) {
+        const uint16_t *c = cv.ckv + static_cast<int64_t>(b) * cv.ckv_sb + static_cast<int64_t>(n) * cv.ckv_sn;
+        const uint16_t *r = cv.kpe + static_cast<int64_t>(b) * cv.kpe_sb + static_cast<int64_t>(n) * cv.kpe_sn;
+        float d = 0.f;
+        for (int k = 0; k < DC; ++k) d = fmaf(q[k], bf16lo(c[k]), d);
+        for (int k = 0; k < DR; ++k) d = fmaf(q[DC + k], bf16lo(r[k]), d);
+        return d * cv.c2;
+    };
+    float m = -INFINITY;
+    for (int n = start + tid; n < end; n += 256) m = fmaxf(m, score(n));
+    m = block_reduce(m, red, true);
+    float l = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int n0 = start; n0 < end; n0 += 256) {
+        const int n = n0 + tid;
+        const float p = n < end ? exp2f(score(n) - m) : 0.f;
+        pw[tid] = p;
+        l += block_reduce(p, red, false);  // its barriers also publish pw[]
+        const int cnt = min(256, end - n0);
+        for (int t = 0; t < cnt; ++t) {
+            const uint16_t *c = cv.ckv + static_cast<int64_t>(b) * cv.ckv_sb + static_cast<int64_t>(n0 + t) * cv.ckv_sn;
+            const uint32_t two = *reinterpret_cast<const uint32_t *>(c + 2 * tid);
+            o0 = fmaf(pw[t], bf16lo(two), o0);
+            o1 = fmaf(pw[t], bf16hi(two), o1);
+        }
+        __syncthreads();
+    }
+    const int64_t prow = (static_cast<int64_t>(b) * S + sp) * H + h;
+    part_o[prow * DC + 2 * tid] = o0;
+    part_o[prow * DC + 2 * tid + 1] = o1;
+    if (tid == 0) {
+        part_ml[prow * 2 + 0] = m;
+        part_ml[prow * 2 + 1] = l;
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int B, int H, int S,
+                                                                float *__restrict__ part_o,
+                                                                float *__restrict__ part_ml,
+                                                                const uint16_t *__restrict__ w_uv,
+                                                                void *__restrict__ out, int out_bf16,
+                                                                CacheView cv)
+{
+    const int h = blockIdx.x, b0 = blockIdx.y * kMergeBatch, tid = threadIdx.x;
+    const int nb = min(kMergeBatch, B - b0);
+    __shared__ float wt[kMergeBatch][kMaxSplits];
+    __shared__ float inv_l[kMergeBatch];
+    __shared__ float wmax[4];
+    __shared__ int any_nan;
+    __shared__ __attribute__((aligned(16))) float ol[kMergeBatch][DC];
+
+    for (int bb = 0; bb < nb; ++bb) {
+        const int b = b0 + bb;
+        const int64_t base = static_cast<int64_t>(b) * S * H + h;
+        // marked (NaN) splits are recomputed first, in ascending order
+        if (tid == 0) any_nan = 0;
+        __syncthreads();
+        for (int sp = tid; sp < S; sp += 256)
+            if (__builtin_isnan(part_ml[(base + static_cast<int64_t>(sp) * H) * 2])) any_nan = 1;
+        __syncthreads();
+        if (any_nan) {
+            for (int sp = 0; sp < S; ++sp)
+                if (__builtin_isnan(part_ml[(base + static_cast<int64_t>(sp) * H) * 2]))
+                    recompute_partial(cv, H, S, b, sp, h, part_o, part_ml);
+        }
+        // max over splits (each split's m read by one thread, then a fixed tree)
+        float mx = -INFINITY;
+        for (int sp = tid; sp < S; sp += 256) mx = fmaxf(mx, part_ml[(base + static_cast<int64_t>(sp) * H) * 2]);
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+        __syncthreads();
+        mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+        for (int sp = tid; sp < S; sp += 256) {
+            const float ms = part_ml[(base + static_cast<int64_t>(sp) * H) * 2];
+            wt[bb][sp] = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float ls = 0.f;  // ascending split order
+            for (int sp = 0; sp < S; ++sp)
+                if (wt[bb][sp] != 0.f) ls = fmaf(wt[bb][sp], part_ml[(base + static_cast<int64_t>(sp) * H) * 2 + 1], ls);
+            inv_l[bb] = ls > 0.f ? 1.f / ls : 0.f;
+        }
+        // o_lat columns 2 tid, 2 tid + 1
+        float a0 = 0.f, a1 = 0.f;
+        for (int sp = 0; sp < S; ++sp) {
+            const float ws = wt[bb][sp];
+            if (ws != 0.f) {
+                const float2 v = *reinterpret_cast<const float2 *>(part_o + (base + static_cast<int64_t>(sp) * H) * DC + 2 * tid);
+                a0 = fmaf(ws, v.x, a0);
+                a1 = fmaf(ws, v.y, a1);
+            }
+        }
+        __syncthreads();
+        ol[bb][2 * tid] = a0 * inv_l[bb];
+        ol[bb][2 * tid + 1] = a1 * inv_l[bb];
+    }
+    __syncthreads();
+
+    // out[b][h][v]: thread handles row v = tid / 2 for batches of its parity.
+    const int v = tid >> 1, par = tid & 1;
+    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(w_uv + (static_cast<int64_t>(h) * DV + v) * DC);
+    float acc[kMergeBatch / 2] = {0.f, 0.f};
+    for (int c = 0; c < DC / 8; ++c) {
+        const u32x4 wv = wrow[c];
+        float wf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wf[2 * e] = bf16lo(wv[e]);
+            wf[2 * e + 1] = bf16hi(wv[e]);
+        }
+#pragma unroll
+        for (int k = 0; k < kMergeBatch / 2; ++k) {
+            const float *o = &ol[2 * k + par][8 * c];
+            float sacc = acc[k];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sacc = fmaf(wf[e], o[e], sacc);
+            acc[k] = sacc;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeBatch / 2; ++k) {
+        const int bb = 2 * k + par;
+        if (bb < nb) {
+            const int64_t oi = (static_cast<int64_t>(b0 + bb) * H + h) * DV + v;
+            if (out_bf16)
+                reinterpret_cast<__bf16 *>(out)[oi] = static_cast<__bf16>(acc[k]);
+            else
+                reinterpret_cast<float *>(out)[oi] = acc[k];
+        }
+    }
+}
+
+}  // namespace
+
+int decode_bf16_heads_per_block(int H) { return H % 128 == 0 ? 128 : 0; }
+
+hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const void *q_rope,
+                              const void *w_uk, const void *w_uv, const void *ckv,
+                              const void *kpe, const int32_t *seqlens, void *out,
+                              const DecodeWorkspace &ws, hipStream_t st, hipEvent_t const *events)
+{
+    uint16_t *qa = static_cast<uint16_t *>(ws.q);
+    if (events) (void)hipEventRecord(events[0], st);
+    {
+        dim3 grid(4, s.H, (s.B + kAbsorbBatch - 1) / kAbsorbBatch);
+        absorb_bf16_kernel<<<grid, 256, 0, st>>>(s.B, s.H, static_cast<const uint16_t *>(q_nope),
+                                                 static_cast<const uint16_t *>(q_rope),
+                                                 static_cast<const uint16_t *>(w_uk), qa);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (events) (void)hipEventRecord(events[1], st);
+    {
+        dim3 grid(s.S, s.H / 128, s.B);
+        decode_splitkv_bf16_kernel<<<grid, kThreadsDec, 0, st>>>(
+            s.H, s.S, s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb,
+            static_cast<int>(s.ckv_sn * 2), static_cast<const uint16_t *>(kpe), s.kpe_sb,
+            static_cast<int>(s.kpe_sn * 2), seqlens, qa, s.scale * kLog2e, ws.part_o, ws.part_ml);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (events) (void)hipEventRecord(events[2], st);
+    dim3 grid(s.H, (s.B + kMergeBatch - 1) / kMergeBatch);
+    CacheView cv{s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb, s.ckv_sn,
+                 static_cast<const uint16_t *>(kpe), s.kpe_sb, s.kpe_sn, seqlens, qa,
+                 s.scale * kLog2e};
+    merge_upproj_bf16_kernel<<<grid, 256, 0, st>>>(s.B, s.H, s.S, ws.part_o, ws.part_ml,
+                                                   static_cast<const uint16_t *>(w_uv), out, s.out_bf16,
+                                                   cv);
+    hipError_t e = hipGetLastError();
+    if (events) (void)hipEventRecord(events[3], st);
+    return e;
+}
+
+}  // namespace mla

@@ -1,0 +1,431 @@
+// mla_api.hip -- the library's C ABI (declared in include/mla.h): host-side
+// validation, workspace carving and kernel dispatch.  Nothing here allocates,
+// frees or synchronises (except the opt-in MLA_DEBUG_CHECKS seqlens check).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mla_status fail(mla_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+mla_status ok()
+{
+    g_err[0] = '\0';
+    return MLA_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool debug_checks()
+{
+    const char *e = getenv("MLA_DEBUG_CHECKS");
+    return e && e[0] && strcmp(e, "0") != 0;
+}
+
+// ---------------------------------------------------------------------------
+// decode
+// ---------------------------------------------------------------------------
+
+bool f32_dims_ok(int64_t dc, int64_t dr, int64_t dn, int64_t dv)
+{
+    return dc >= 1 && dc <= 1024 && dr >= 0 && dr <= 256 && dn >= 1 && dn <= 512 && dv >= 1 &&
+           dv <= 1024;
+}
+
+bool bf16_dims_ok(int64_t H, int64_t dc, int64_t dr, int64_t dn, int64_t dv)
+{
+    return dc == 512 && dr == 64 && dn == 128 && dv == 128 && H % 128 == 0;
+}
+
+int auto_splits(const mla_decode_params *p)
+{
+    // Enough (sequence, split) blocks to cover the 256 compute units about
+    // once, but at least four 32-token tiles of context per split so the
+    // split partials stay small next to the cache rows they summarise.
+    const int64_t tiles = (p->n_max + mla::kSplitGranule - 1) / mla::kSplitGranule;
+    int64_t groups;
+    int64_t target;
+    if (p->dtype == MLA_BF16) {
+        groups = p->batch * (p->heads / mla::decode_bf16_heads_per_block((int)p->heads));
+        target = 256;
+    } else {
+        groups = p->batch * p->heads;
+        target = 256;
+    }
+    int64_t s = (target + groups - 1) / groups;
+    int64_t cap = tiles / 4;
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+    if (s > mla::kMaxSplits) s = mla::kMaxSplits;
+    return (int)s;
+}
+
+// Structural validation shared by the workspace query and the decode call.
+mla_status check_decode_params(const mla_decode_params *p)
+{
+    if (!p) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+    if (p->batch < 1 || p->heads < 1 || p->n_max < 1 || p->d_c < 1 || p->d_n < 1 || p->d_v < 1 ||
+        p->d_r < 0)
+        return fail(MLA_ERR_INVALID_ARG,
+                    "non-positive size (batch=%lld heads=%lld n_max=%lld d_c=%lld d_r=%lld d_n=%lld d_v=%lld)",
+                    (long long)p->batch, (long long)p->heads, (long long)p->n_max, (long long)p->d_c,
+                    (long long)p->d_r, (long long)p->d_n, (long long)p->d_v);
+    if (p->batch > 65535 || p->heads > 65535 || p->n_max > (int64_t)1 << 30)
+        return fail(MLA_ERR_UNSUPPORTED, "batch, heads or n_max beyond the supported range");
+    if ((p->dtype != MLA_F32 && p->dtype != MLA_BF16) ||
+        (p->out_dtype != MLA_F32 && p->out_dtype != MLA_BF16))
+        return fail(MLA_ERR_UNSUPPORTED, "unknown dtype %d / out_dtype %d", p->dtype, p->out_dtype);
+    if (p->dtype == MLA_F32 && !f32_dims_ok(p->d_c, p->d_r, p->d_n, p->d_v))
+        return fail(MLA_ERR_UNSUPPORTED,
+                    "fp32 kernels support d_c<=1024, d_r<=256, d_n<=512, d_v<=1024");
+    if (p->dtype == MLA_BF16 && !bf16_dims_ok(p->heads, p->d_c, p->d_r, p->d_n, p->d_v))
+        return fail(MLA_ERR_UNSUPPORTED,
+                    "bf16 kernels support d_c=512, d_r=64, d_n=d_v=128 and heads %% 128 == 0 "
+                    "(got d_c=%lld d_r=%lld d_n=%lld d_v=%lld heads=%lld)",
+                    (long long)p->d_c, (long long)p->d_r, (long long)p->d_n, (long long)p->d_v,
+                    (long long)p->heads);
+    if (p->ckv_stride_n < p->d_c || (p->d_r > 0 && p->kpe_stride_n < p->d_r))
+        return fail(MLA_ERR_INVALID_ARG, "cache row stride smaller than the row width");
+    if (p->dtype == MLA_BF16 && (p->n_max * p->ckv_stride_n * 2 >= ((int64_t)1 << 32) ||
+                                 p->n_max * p->kpe_stride_n * 2 >= ((int64_t)1 << 32)))
+        return fail(MLA_ERR_UNSUPPORTED, "bf16 decode addresses one sequence's cache with 32-bit offsets");
+    if (p->batch > 1 && (p->ckv_stride_b < p->n_max * p->ckv_stride_n ||
+                         (p->d_r > 0 && p->kpe_stride_b < p->n_max * p->kpe_stride_n)))
+        return fail(MLA_ERR_INVALID_ARG, "cache sequence stride smaller than n_max rows");
+    if (p->ckv_stride_b < 0 || p->kpe_stride_b < 0)
+        return fail(MLA_ERR_INVALID_ARG, "negative cache stride");
+    if (p->num_splits < 0 || p->num_splits > mla::kMaxSplits)
+        return fail(MLA_ERR_INVALID_ARG, "num_splits must be in [0, %d]", mla::kMaxSplits);
+    if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
+        return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    return MLA_OK;
+}
+
+mla::DecodeShape make_shape(const mla_decode_params *p)
+{
+    mla::DecodeShape s;
+    s.B = (int)p->batch;
+    s.H = (int)p->heads;
+    s.dc = (int)p->d_c;
+    s.dr = (int)p->d_r;
+    s.dn = (int)p->d_n;
+    s.dv = (int)p->d_v;
+    s.n_max = p->n_max;
+    s.ckv_sb = p->ckv_stride_b;
+    s.ckv_sn = p->ckv_stride_n;
+    s.kpe_sb = p->kpe_stride_b;
+    s.kpe_sn = p->kpe_stride_n;
+    s.scale = p->softmax_scale > 0.f ? p->softmax_scale
+                                     : (float)(1.0 / sqrt((double)(p->d_n + p->d_r)));
+    s.S = p->num_splits > 0 ? p->num_splits : auto_splits(p);
+    s.out_bf16 = p->out_dtype == MLA_BF16;
+    return s;
+}
+
+mla_status check_seqlens_debug(const int32_t *seqlens, int64_t B, int64_t n_max, hipStream_t st,
+                               int64_t min_len)
+{
+    std::vector<int32_t> h((size_t)B);
+    if (hipMemcpyAsync(h.data(), seqlens, sizeof(int32_t) * (size_t)B, hipMemcpyDeviceToHost, st) !=
+            hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return fail(MLA_ERR_HIP, "MLA_DEBUG_CHECKS: could not read seqlens");
+    for (int64_t b = 0; b < B; ++b)
+        if (h[(size_t)b] < min_len || h[(size_t)b] > n_max)
+            return fail(MLA_ERR_INVALID_ARG, "MLA_DEBUG_CHECKS: seqlens[%lld]=%d outside [%lld, %lld]",
+                        (long long)b, h[(size_t)b], (long long)min_len, (long long)n_max);
+    return MLA_OK;
+}
+
+}  // namespace
+
+namespace mla {
+
+size_t decode_workspace_layout(const DecodeShape &s, bool bf16, DecodeWorkspace *ws, void *base)
+{
+    const size_t rows = (size_t)s.B * s.H;
+    const size_t qbytes = bf16 ? rows * (size_t)(s.dc + s.dr) * 2 : rows * (size_t)s.dc * 4;
+    const size_t obytes = rows * (size_t)s.S * (size_t)s.dc * 4;
+    const size_t mlbytes = rows * (size_t)s.S * 2 * 4;
+    const size_t off_o = round_up(qbytes, kAlign);
+    const size_t off_ml = off_o + round_up(obytes, kAlign);
+    const size_t total = off_ml + round_up(mlbytes, kAlign);
+    if (ws) {
+        char *b = static_cast<char *>(base);
+        ws->q = b;
+        ws->part_o = reinterpret_cast<float *>(b + off_o);
+        ws->part_ml = reinterpret_cast<float *>(b + off_ml);
+    }
+    return total;
+}
+
+}  // namespace mla
+
+extern "C" {
+
+int mla_decode_num_splits(const mla_decode_params *p)
+{
+    if (check_decode_params(p) != MLA_OK) return 0;
+    return make_shape(p).S;
+}
+
+size_t mla_decode_workspace_bytes(const mla_decode_params *p)
+{
+    if (check_decode_params(p) != MLA_OK) return 0;
+    mla::DecodeShape s = make_shape(p);
+    return mla::decode_workspace_layout(s, p->dtype == MLA_BF16, nullptr, nullptr);
+}
+
+mla_status mla_absorb_q(const mla_decode_params *p, const void *q_nope, const void *w_uk,
+                        float *q_abs, void *stream)
+{
+    if (!p) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+    if (p->batch < 1 || p->heads < 1 || p->d_c < 1 || p->d_n < 1)
+        return fail(MLA_ERR_INVALID_ARG, "non-positive size");
+    if (p->batch > 65535 || p->heads > 65535 || p->d_c > 1 << 20 || p->d_n > 512)
+        return fail(MLA_ERR_UNSUPPORTED, "absorb supports d_n <= 512 and batch, heads <= 65535");
+    if (p->dtype != MLA_F32 && p->dtype != MLA_BF16)
+        return fail(MLA_ERR_UNSUPPORTED, "unknown dtype %d", p->dtype);
+    if (!q_nope || !w_uk || !q_abs) return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+    hipError_t e = mla::launch_absorb_f32((int)p->batch, (int)p->heads, (int)p->d_n, (int)p->d_c,
+                                          p->dtype == MLA_BF16, q_nope, w_uk, q_abs,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "absorb launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+mla_status mla_decode_profiled(const mla_decode_params *p, const void *q_nope,
+                               const void *q_rope, const void *w_uk, const void *w_uv,
+                               const void *ckv_cache, const void *kpe_cache,
+                               const int32_t *seqlens, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream, void *const *events)
+{
+    mla_status st = check_decode_params(p);
+    if (st != MLA_OK) return st;
+    if (!q_nope || !w_uk || !w_uv || !ckv_cache || !seqlens || !out)
+        return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (p->d_r > 0 && (!q_rope || !kpe_cache))
+        return fail(MLA_ERR_INVALID_ARG, "NULL q_rope or kpe_cache with d_r > 0");
+    const bool bf16 = p->dtype == MLA_BF16;
+    if (bf16) {
+        if (!aligned(ckv_cache, 16) || !aligned(kpe_cache, 16) || p->ckv_stride_n % 8 ||
+            p->kpe_stride_n % 8 || p->ckv_stride_b % 8 || p->kpe_stride_b % 8)
+            return fail(MLA_ERR_INVALID_ARG,
+                        "bf16 caches need 16-byte aligned rows (pointers %% 16, strides %% 8 elements)");
+        if (!aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(w_uk, 16) ||
+            !aligned(w_uv, 16) || !aligned(out, 16))
+            return fail(MLA_ERR_INVALID_ARG, "bf16 path needs 16-byte aligned q, weights and out");
+    } else {
+        if (!aligned(q_nope, 4) || (q_rope && !aligned(q_rope, 4)) || !aligned(w_uk, 4) ||
+            !aligned(w_uv, 4) || !aligned(ckv_cache, 4) || (kpe_cache && !aligned(kpe_cache, 4)) ||
+            !aligned(out, 4))
+            return fail(MLA_ERR_INVALID_ARG, "fp32 tensors must be 4-byte aligned");
+    }
+    mla::DecodeShape s = make_shape(p);
+    mla::DecodeWorkspace ws;
+    const size_t need = mla::decode_workspace_layout(s, bf16, &ws, workspace);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign))
+        return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu at %p)",
+                    need, workspace_bytes, workspace);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (debug_checks()) {
+        st = check_seqlens_debug(seqlens, p->batch, p->n_max, hs, 1);
+        if (st != MLA_OK) return st;
+    }
+    hipError_t e;
+    hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
+    if (bf16)
+        e = mla::launch_decode_bf16(s, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens,
+                                    out, ws, hs, ev);
+    else
+        e = mla::launch_decode_f32(s, static_cast<const float *>(q_nope),
+                                   static_cast<const float *>(q_rope), static_cast<const float *>(w_uk),
+                                   static_cast<const float *>(w_uv), static_cast<const float *>(ckv_cache),
+                                   static_cast<const float *>(kpe_cache), seqlens, out, ws, hs, ev);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+mla_status mla_decode(const mla_decode_params *p, const void *q_nope, const void *q_rope,
+                      const void *w_uk, const void *w_uv, const void *ckv_cache,
+                      const void *kpe_cache, const int32_t *seqlens, void *out, void *workspace,
+                      size_t workspace_bytes, void *stream)
+{
+    return mla_decode_profiled(p, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, out,
+                               workspace, workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// prefill
+// ---------------------------------------------------------------------------
+namespace {
+
+mla_status check_prefill_params(const mla_prefill_params *p)
+{
+    if (!p) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+    if (p->batch < 1 || p->tokens < 1 || p->heads < 1 || p->n_max < 1 || p->d_c < 1 ||
+        p->d_n < 1 || p->d_v < 1 || p->d_r < 0)
+        return fail(MLA_ERR_INVALID_ARG, "non-positive size");
+    if (p->tokens > p->n_max) return fail(MLA_ERR_INVALID_ARG, "tokens exceeds n_max");
+    if (p->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "reserved field must be 0");
+    if (p->batch > 65535 || p->heads > 65535 || p->tokens > (1 << 24) || p->n_max > (1 << 24))
+        return fail(MLA_ERR_UNSUPPORTED, "sizes beyond the supported range");
+    if ((p->dtype != MLA_F32 && p->dtype != MLA_BF16) ||
+        (p->out_dtype != MLA_F32 && p->out_dtype != MLA_BF16))
+        return fail(MLA_ERR_UNSUPPORTED, "unknown dtype");
+    if (p->dtype == MLA_F32 && !f32_dims_ok(p->d_c, p->d_r, p->d_n, p->d_v))
+        return fail(MLA_ERR_UNSUPPORTED, "fp32 kernels support d_c<=1024, d_r<=256, d_n<=512, d_v<=1024");
+    if (p->dtype == MLA_BF16 && !(p->d_c == 512 && p->d_r == 64 && p->d_n == 128 && p->d_v == 128))
+        return fail(MLA_ERR_UNSUPPORTED, "bf16 prefill supports d_c=512, d_r=64, d_n=d_v=128");
+    if (p->ckv_stride_n < p->d_c || (p->d_r > 0 && p->kpe_stride_n < p->d_r))
+        return fail(MLA_ERR_INVALID_ARG, "cache row stride smaller than the row width");
+    if (p->batch > 1 && (p->ckv_stride_b < p->n_max * p->ckv_stride_n ||
+                         (p->d_r > 0 && p->kpe_stride_b < p->n_max * p->kpe_stride_n)))
+        return fail(MLA_ERR_INVALID_ARG, "cache sequence stride smaller than n_max rows");
+    if (p->ckv_stride_b < 0 || p->kpe_stride_b < 0)
+        return fail(MLA_ERR_INVALID_ARG, "negative cache stride");
+    if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
+        return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    return MLA_OK;
+}
+
+mla::PrefillShape make_pshape(const mla_prefill_params *p)
+{
+    mla::PrefillShape s;
+    s.B = (int)p->batch;
+    s.T = (int)p->tokens;
+    s.H = (int)p->heads;
+    s.dc = (int)p->d_c;
+    s.dr = (int)p->d_r;
+    s.dn = (int)p->d_n;
+    s.dv = (int)p->d_v;
+    s.n_max = p->n_max;
+    s.ckv_sb = p->ckv_stride_b;
+    s.ckv_sn = p->ckv_stride_n;
+    s.kpe_sb = p->kpe_stride_b;
+    s.kpe_sn = p->kpe_stride_n;
+    s.scale = p->softmax_scale > 0.f ? p->softmax_scale
+                                     : (float)(1.0 / sqrt((double)(p->d_n + p->d_r)));
+    s.out_bf16 = p->out_dtype == MLA_BF16;
+    return s;
+}
+
+}  // namespace
+
+namespace mla {
+
+size_t prefill_workspace_layout(const PrefillShape &s, bool bf16, void *base, void **k_out,
+                                void **v_out)
+{
+    const size_t elt = bf16 ? 2 : 4;
+    const size_t rows = (size_t)s.B * (size_t)s.n_max * (size_t)s.H;
+    const size_t kb = round_up(rows * (size_t)s.dn * elt, kAlign);
+    const size_t vb = round_up(rows * (size_t)s.dv * elt, kAlign);
+    if (k_out) *k_out = base;
+    if (v_out) *v_out = static_cast<char *>(base) + kb;
+    return kb + vb;
+}
+
+}  // namespace mla
+
+extern "C" {
+
+size_t mla_prefill_workspace_bytes(const mla_prefill_params *p)
+{
+    if (check_prefill_params(p) != MLA_OK) return 0;
+    mla::PrefillShape s = make_pshape(p);
+    return mla::prefill_workspace_layout(s, p->dtype == MLA_BF16, nullptr, nullptr, nullptr);
+}
+
+mla_status mla_prefill_naive(const mla_prefill_params *p, const void *q_nope, const void *q_rope,
+                             const void *w_uk, const void *w_uv, const void *ckv_cache,
+                             const void *kpe_cache, const int32_t *seqlens, void *out,
+                             void *workspace, size_t workspace_bytes, void *stream)
+{
+    mla_status st = check_prefill_params(p);
+    if (st != MLA_OK) return st;
+    if (!q_nope || !w_uk || !w_uv || !ckv_cache || !seqlens || !out)
+        return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (p->d_r > 0 && (!q_rope || !kpe_cache))
+        return fail(MLA_ERR_INVALID_ARG, "NULL q_rope or kpe_cache with d_r > 0");
+    const bool bf16 = p->dtype == MLA_BF16;
+    const size_t a = bf16 ? 16 : 4;
+    if (!aligned(q_nope, a) || !aligned(q_rope, a) || !aligned(w_uk, a) || !aligned(w_uv, a) ||
+        !aligned(ckv_cache, a) || !aligned(kpe_cache, a) || !aligned(out, a))
+        return fail(MLA_ERR_INVALID_ARG, "tensors must be %zu-byte aligned", a);
+    if (bf16 && (p->ckv_stride_n % 8 || p->kpe_stride_n % 8 || p->ckv_stride_b % 8 ||
+                 p->kpe_stride_b % 8))
+        return fail(MLA_ERR_INVALID_ARG, "bf16 cache strides must be multiples of 8 elements");
+    mla::PrefillShape s = make_pshape(p);
+    void *kbuf = nullptr, *vbuf = nullptr;
+    const size_t need = mla::prefill_workspace_layout(s, bf16, workspace, &kbuf, &vbuf);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign))
+        return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu)",
+                    need, workspace_bytes);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (debug_checks()) {
+        st = check_seqlens_debug(seqlens, p->batch, p->n_max, hs, p->tokens);
+        if (st != MLA_OK) return st;
+    }
+    hipError_t e;
+    if (bf16)
+        e = mla::launch_prefill_bf16(s, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens,
+                                     out, kbuf, vbuf, hs);
+    else
+        e = mla::launch_prefill_f32(s, static_cast<const float *>(q_nope),
+                                    static_cast<const float *>(q_rope), static_cast<const float *>(w_uk),
+                                    static_cast<const float *>(w_uv), static_cast<const float *>(ckv_cache),
+                                    static_cast<const float *>(kpe_cache), seqlens, out, kbuf, vbuf, hs);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+uint64_t mla_kv_cache_bytes(int64_t n_layers, int64_t batch, int64_t seq_len, int64_t d_c,
+                            int64_t d_r, int64_t bytes_per_elem)
+{
+    if (n_layers < 0 || batch < 0 || seq_len < 0 || d_c < 0 || d_r < 0 || bytes_per_elem < 0)
+        return 0;
+    return (uint64_t)n_layers * (uint64_t)batch * (uint64_t)seq_len * (uint64_t)(d_c + d_r) *
+           (uint64_t)bytes_per_elem;
+}
+
+const char *mla_status_string(mla_status s)
+{
+    switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape or dtype not implemented";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime error";
+    }
+    return "unknown mla_status";
+}
+
+const char *mla_last_error(void) { return g_err; }
+
+int mla_version(void) { return 10000; }
+
+}  // extern "C"

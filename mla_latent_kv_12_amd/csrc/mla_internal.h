@@ -1,0 +1,77 @@
+// mla_internal.h -- declarations shared by the library's own translation units
+// (host API <-> kernel launchers).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Token granularity at which a sequence is cut into context splits.  Both the
+// fp32 and the bf16 decode kernels use it, so a split boundary never falls
+// inside an MFMA token tile.
+constexpr int kSplitGranule = 32;
+constexpr int kMaxSplits = 256;
+
+struct DecodeShape {
+    int B, H, dc, dr, dn, dv;
+    int64_t n_max;
+    int64_t ckv_sb, ckv_sn, kpe_sb, kpe_sn;
+    float scale;     // softmax scale (natural-log units)
+    int S;           // context splits per sequence
+    int out_bf16;    // output stored as bf16 (else fp32)
+};
+
+// Workspace carving, identical for the fp32 and bf16 paths except for the
+// query buffer's element type and width.
+struct DecodeWorkspace {
+    void *q;          // bf16 path: [B][H][dc+dr] bf16 pre-absorbed query; fp32: [B][H][dc] fp32
+    float *part_o;    // [B][S][H][dc]   un-normalised latent accumulators per split
+    float *part_ml;   // [B][S][H][2]    running max (log2 units) and softmax mass per split
+};
+
+size_t decode_workspace_layout(const DecodeShape &s, bool bf16, DecodeWorkspace *ws_or_null,
+                               void *base);
+
+// fp32 path (any supported small shape)
+hipError_t launch_absorb_f32(int B, int H, int dn, int dc, bool in_bf16, const void *q_nope,
+                             const void *w_uk, float *q_abs, hipStream_t st);
+hipError_t launch_decode_f32(const DecodeShape &s, const float *q_nope, const float *q_rope,
+                             const float *w_uk, const float *w_uv, const float *ckv,
+                             const float *kpe, const int32_t *seqlens, void *out,
+                             const DecodeWorkspace &ws, hipStream_t st,
+                             hipEvent_t const *events);
+
+// Fixed-order split merge + W_UV up-projection (scalar; any shape).
+hipError_t launch_merge_upproj_generic(const DecodeShape &s, const DecodeWorkspace &ws,
+                                       const void *w_uv, bool w_bf16, void *out, hipStream_t st);
+
+// bf16 MFMA path (d_c = 512, d_r = 64, d_n = d_v = 128, H % 128 == 0)
+// `events` (may be null): 4 hipEvent_t recorded before, between and after
+// the three kernels.
+hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const void *q_rope,
+                              const void *w_uk, const void *w_uv, const void *ckv,
+                              const void *kpe, const int32_t *seqlens, void *out,
+                              const DecodeWorkspace &ws, hipStream_t st,
+                              hipEvent_t const *events);
+int decode_bf16_heads_per_block(int H);
+
+struct PrefillShape {
+    int B, T, H, dc, dr, dn, dv;
+    int64_t n_max;
+    int64_t ckv_sb, ckv_sn, kpe_sb, kpe_sn;
+    float scale;
+    int out_bf16;
+};
+size_t prefill_workspace_layout(const PrefillShape &s, bool bf16, void *base, void **k_out,
+                                void **v_out);
+hipError_t launch_prefill_f32(const PrefillShape &s, const float *q_nope, const float *q_rope,
+                              const float *w_uk, const float *w_uv, const float *ckv,
+                              const float *kpe, const int32_t *seqlens, void *out, void *kbuf,
+                              void *vbuf, hipStream_t st);
+hipError_t launch_prefill_bf16(const PrefillShape &s, const void *q_nope, const void *q_rope,
+                               const void *w_uk, const void *w_uv, const void *ckv,
+                               const void *kpe, const int32_t *seqlens, void *out, void *kbuf,
+                               void *vbuf, hipStream_t st);
+
+}  // namespace mla

@@ -6,6 +6,7 @@ never imports, loads or calls anything in this package.
 """
 from .oracle import (  # noqa: F401
     OracleError,
+    absorb_q,
     build,
     decode_absorbed,
     decode_naive,

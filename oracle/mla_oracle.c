@@ -241,6 +241,28 @@ int oracle_decode_absorbed(const oracle_dims *d, const void *q_nope, const void 
 }
 
 /*
+ * Query absorption alone: q~[b][h][j] = sum_i W_UK[h][i][j] q_nope[b][h][i]
+ * ("DeepSeek MLA Architecture: How It Cuts KV Cache by 93%", section 2).
+ * out is [B][H][dc].
+ */
+int oracle_absorb_q(const oracle_dims *d, const void *q_nope, const void *w_uk, double *out)
+{
+    if (check_dims(d) || !out) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < d->B * d->H; ++k) {
+        const int64_t h = k % d->H;
+        for (int64_t j = 0; j < d->dc; ++j) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < d->dn; ++i)
+                acc += widen(w_uk, d->dtype, (h * d->dn + i) * d->dc + j) *
+                       widen(q_nope, d->dtype, k * d->dn + i);
+            out[k * d->dc + j] = acc;
+        }
+    }
+    return 0;
+}
+
+/*
  * O3 -- naive causal prefill.  T queries per sequence, q_nope [B][T][H][dn],
  * q_rope [B][T][H][dr].  Query t of sequence b sits at position
  * pos = L_b - T + t (the queries are the last T cached rows) and attends to

@@ -8,6 +8,7 @@ Parity status of each function (the pins live in ``tests/test_oracle_pins.py``):
   decode_naive     pinned: torch fp64 scaled-dot-product attention over
                    explicitly decompressed K/V, closed forms at L=1, uniform
                    scores, softmax mass, cache permutation, padding.
+  absorb_q         pinned: the content-score identity q~ . c == q . (W_UK c).
   decode_absorbed  pinned: equals decode_naive on the latent-width x length x
                    RoPE-width grid, plus the same closed forms.
   prefill_naive    pinned: torch fp64 attention with an explicit bottom-right
@@ -68,6 +69,8 @@ def _load():
             f = getattr(lib, name)
             f.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, vp, vp, vp, vp, vp, i64, dp, dp]
             f.restype = ctypes.c_int
+        lib.oracle_absorb_q.argtypes = [ctypes.POINTER(_Dims), vp, vp, dp]
+        lib.oracle_absorb_q.restype = ctypes.c_int
         lib.oracle_prefill_naive.argtypes = [ctypes.POINTER(_Dims), i64, vp, vp, vp, vp, vp, vp,
                                              vp, vp, i64, dp]
         lib.oracle_prefill_naive.restype = ctypes.c_int
@@ -167,6 +170,21 @@ def decode_absorbed(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, pairs=
     W_UV up-projection).  Same arguments and returns as :func:`decode_naive`."""
     return _decode("oracle_decode_absorbed", q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens,
                    scale, pairs)
+
+
+def absorb_q(q_nope, w_uk):
+    """q~[b,h,:] = W_UK[h]^T q_nope[b,h,:] in fp64.  q_nope [B,H,dn], w_uk [H,dn,dc]."""
+    q_nope = np.ascontiguousarray(q_nope)
+    w_uk = np.ascontiguousarray(w_uk)
+    if _code(q_nope) != _code(w_uk):
+        raise OracleError("all inputs must share one storage dtype")
+    B, H, dn = q_nope.shape
+    dc = w_uk.shape[2]
+    d = _Dims(B=B, H=H, dc=dc, dr=0, dn=dn, dv=1, dtype=_code(q_nope), scale=1.0)
+    out = np.zeros((B, H, dc), dtype=np.float64)
+    if _load().oracle_absorb_q(ctypes.byref(d), _ptr(q_nope), _ptr(w_uk), _ptr(out)) != 0:
+        raise OracleError("oracle_absorb_q rejected its arguments")
+    return out
 
 
 def prefill_naive(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, rows):

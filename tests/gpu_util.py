@@ -1,0 +1,72 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+on a generated workload, run the fp64 oracle on the same stored values, and
+compare with the documented tolerances."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import mla_latent_kv_12_amd as mla
+import oracle
+from mla_latent_kv_12_amd.tensors import decode_tensors, to_device, to_host_f64
+
+# fp32 workloads: max-abs error bound.
+F32_TOL = 1e-4
+# bf16 workloads (fp32 accumulation): max-abs <= 2e-2, and max-abs <= 2e-2 of
+# the reference's rms (the same bound for outputs of unit scale).
+BF16_ABS = 2e-2
+BF16_REL_RMS = 2e-2
+
+
+def say(*args):
+    print(*args, flush=True)
+    sys.stdout.flush()
+
+
+def run_decode(case, *, num_splits=0, out_dtype=None, tensors=None):
+    t = tensors if tensors is not None else decode_tensors(case)
+    odt = {None: None, "f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    out = mla.decode(t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv_cache"],
+                     t["kpe_cache"], t["seqlens"], softmax_scale=case.scale,
+                     num_splits=num_splits, out_dtype=odt)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_decode(case, pairs=None, naive=False):
+    fn = oracle.decode_naive if naive else oracle.decode_absorbed
+    out, _ = fn(case.q_nope, case.q_rope, case.w_uk, case.w_uv, case.ckv, case.kpe,
+                case.seqlens, case.scale, pairs=pairs)
+    return out
+
+
+def metrics(gpu: np.ndarray, ref: np.ndarray) -> dict:
+    err = np.abs(gpu - ref)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    return dict(max_abs=float(err.max()) if err.size else 0.0, rms_ref=rms,
+                rel_rms=float(np.sqrt(np.mean(err * err)) / rms) if rms > 0 else 0.0,
+                max_over_rms=float(err.max() / rms) if rms > 0 else 0.0,
+                finite=bool(np.all(np.isfinite(gpu))))
+
+
+def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
+    m = metrics(gpu, ref)
+    say(f"  parity {what}: {m}")
+    assert m["finite"], f"{what}: non-finite output"
+    if dtype == "f32":
+        assert m["max_abs"] <= F32_TOL, f"{what}: {m}"
+    else:
+        assert m["max_abs"] <= BF16_ABS, f"{what}: {m}"
+        assert m["max_abs"] <= BF16_REL_RMS * m["rms_ref"], f"{what}: {m}"
+    return m
+
+
+def gather_pairs(out: torch.Tensor, pairs) -> np.ndarray:
+    o = to_host_f64(out)
+    return np.stack([o[b, h] for b, h in pairs])
+
+
+__all__ = ["say", "run_decode", "oracle_decode", "metrics", "assert_close", "gather_pairs",
+           "to_device", "to_host_f64", "decode_tensors", "F32_TOL"]

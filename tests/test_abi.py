@@ -1,0 +1,204 @@
+"""Host-side tests of the C ABI: the library loads and exports every declared
+symbol, size arithmetic, workspace queries, and argument validation (every
+rejected call returns before any launch, so these run without a GPU)."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mla_latent_kv_12_amd as mla
+from mla_latent_kv_12_amd import binding, datagen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "cache_tables.json")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_struct_layouts_match_header():
+    # field order and C sizes (int64 x 11, float, int32 x 3 -> 104 bytes)
+    assert ctypes.sizeof(binding.DecodeParams) == 104
+    assert ctypes.sizeof(binding.PrefillParams) == 12 * 8 + 4 * 4
+
+
+def test_kv_cache_bytes_reproduces_the_pages():
+    g = json.load(open(GOLDEN))
+    for row in g["eyestech_telemetry"]["rows"]:
+        w = row["elems_per_token"]
+        for s, gib in zip(g["eyestech_telemetry"]["seq_lens"], row["gib"]):
+            assert round(mla.kv_cache_bytes(60, 8, s, row.get("d_c", w), row.get("d_r", 0), 2)
+                         / 2**30, 2) == gib
+    assert mla.kv_cache_bytes(1, 1, 1, 512, 64, 1) == 576
+    assert mla.kv_cache_bytes(60, 1, 131072, 512, 64, 2) / 2**30 == pytest.approx(8.4375)
+    assert mla.kv_cache_bytes(-1, 1, 1, 1, 1, 1) == 0
+
+
+def test_status_strings_and_version():
+    for s in range(5):
+        assert mla.status_string(s).startswith("MLA_")
+    assert mla.version() >= 10000
+
+
+def _v3_params(**kw):
+    base = dict(batch=8, heads=128, d_c=512, d_r=64, d_n=128, d_v=128, n_max=131072,
+                ckv_stride_b=131072 * 576, ckv_stride_n=576, kpe_stride_b=131072 * 576,
+                kpe_stride_n=576, softmax_scale=0.0, dtype=mla.MLA_BF16, out_dtype=mla.MLA_BF16,
+                num_splits=0)
+    base.update(kw)
+    return binding.DecodeParams(**base)
+
+
+def test_decode_workspace_size():
+    p = _v3_params(num_splits=32)
+    ws = mla.decode_workspace_bytes(p)
+    q = 8 * 128 * 576 * 2
+    o = 8 * 32 * 128 * 512 * 4
+    ml = 8 * 32 * 128 * 2 * 4
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert ws == rnd(q) + rnd(o) + rnd(ml)
+    assert mla.decode_workspace_bytes(_v3_params()) > 0            # auto split count
+    assert mla.decode_workspace_bytes(_v3_params(d_c=256)) == 0    # unsupported -> 0
+    assert mla.decode_workspace_bytes(_v3_params(batch=0)) == 0
+
+
+def _call_decode(p, ptrs=None, ws_bytes=1 << 40, ws=0x100000):
+    lib = binding.lib()
+    fake = ptrs or dict(q_nope=0x1000, q_rope=0x2000, w_uk=0x3000, w_uv=0x4000, ckv=0x5000,
+                        kpe=0x5400, seqlens=0x6000, out=0x7000)
+    vp = ctypes.c_void_p
+    return lib.mla_decode(ctypes.byref(p), vp(fake["q_nope"]), vp(fake["q_rope"]),
+                          vp(fake["w_uk"]), vp(fake["w_uv"]), vp(fake["ckv"]), vp(fake["kpe"]),
+                          vp(fake["seqlens"]), vp(fake["out"]), vp(ws), ws_bytes, None)
+
+
+def _msg():
+    return binding.lib().mla_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(heads=0), mla.MLA_ERR_INVALID_ARG),
+    (dict(d_r=-1), mla.MLA_ERR_INVALID_ARG),
+    (dict(d_c=256), mla.MLA_ERR_UNSUPPORTED),
+    (dict(heads=96), mla.MLA_ERR_UNSUPPORTED),
+    (dict(d_n=64), mla.MLA_ERR_UNSUPPORTED),
+    (dict(dtype=7), mla.MLA_ERR_UNSUPPORTED),
+    (dict(out_dtype=3), mla.MLA_ERR_UNSUPPORTED),
+    (dict(ckv_stride_n=500), mla.MLA_ERR_INVALID_ARG),
+    (dict(ckv_stride_b=576), mla.MLA_ERR_INVALID_ARG),
+    (dict(num_splits=-1), mla.MLA_ERR_INVALID_ARG),
+    (dict(num_splits=100000), mla.MLA_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), mla.MLA_ERR_INVALID_ARG),
+    (dict(ckv_stride_n=580, kpe_stride_n=580, ckv_stride_b=131072 * 580,
+          kpe_stride_b=131072 * 580), mla.MLA_ERR_INVALID_ARG),  # rows not 16-byte aligned
+])
+def test_decode_rejects_bad_params_before_launch(kw, status):
+    assert _call_decode(_v3_params(**kw)) == status
+    assert _msg() != ""
+
+
+def test_decode_rejects_null_and_misaligned_pointers():
+    p = _v3_params()
+    ptrs = dict(q_nope=0x1000, q_rope=0x2000, w_uk=0x3000, w_uv=0x4000, ckv=0x5000, kpe=0x5400,
+                seqlens=0x6000, out=0x7000)
+    for k in ("q_nope", "w_uk", "w_uv", "ckv", "seqlens", "out", "q_rope", "kpe"):
+        bad = dict(ptrs, **{k: 0})
+        assert _call_decode(p, bad) == mla.MLA_ERR_INVALID_ARG, k
+    assert _call_decode(p, dict(ptrs, ckv=0x5002)) == mla.MLA_ERR_INVALID_ARG
+    assert "aligned" in _msg()
+
+
+def test_decode_rejects_bad_workspace():
+    p = _v3_params(num_splits=8)
+    need = mla.decode_workspace_bytes(p)
+    assert _call_decode(p, ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE
+    assert _call_decode(p, ws=0) == mla.MLA_ERR_WORKSPACE
+    assert _call_decode(p, ws=0x100010) == mla.MLA_ERR_WORKSPACE   # not 256-byte aligned
+    assert str(need) in _msg()
+
+
+def test_absorb_rejects_bad_args():
+    lib = binding.lib()
+    vp = ctypes.c_void_p
+    p = _v3_params()
+    assert lib.mla_absorb_q(None, vp(1), vp(1), vp(1), None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(ctypes.byref(p), vp(0), vp(0x1000), vp(0x2000), None) == \
+        mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_absorb_q(ctypes.byref(_v3_params(dtype=5)), vp(0x1000), vp(0x1000),
+                            vp(0x2000), None) == mla.MLA_ERR_UNSUPPORTED
+
+
+def _prefill_params(**kw):
+    base = dict(batch=1, tokens=4096, heads=128, d_c=512, d_r=64, d_n=128, d_v=128, n_max=4096,
+                ckv_stride_b=4096 * 576, ckv_stride_n=576, kpe_stride_b=4096 * 576,
+                kpe_stride_n=576, softmax_scale=0.0, dtype=mla.MLA_BF16, out_dtype=mla.MLA_BF16,
+                reserved=0)
+    base.update(kw)
+    return binding.PrefillParams(**base)
+
+
+def test_prefill_workspace_and_validation():
+    p = _prefill_params()
+    assert mla.prefill_workspace_bytes(p) == 2 * 4096 * 128 * 128 * 2
+    assert mla.prefill_workspace_bytes(_prefill_params(tokens=5000)) == 0   # T > n_max
+    assert mla.prefill_workspace_bytes(_prefill_params(reserved=1)) == 0
+    lib = binding.lib()
+    vp = ctypes.c_void_p
+    args = [vp(0x1000)] * 8
+
+    def call(pp, ws=0x100000, nbytes=1 << 40, ptrs=args):
+        return lib.mla_prefill_naive(ctypes.byref(pp), *ptrs, vp(ws), nbytes, None)
+
+    assert call(_prefill_params(d_c=128)) == mla.MLA_ERR_UNSUPPORTED
+    assert call(_prefill_params(tokens=0)) == mla.MLA_ERR_INVALID_ARG
+    assert call(p, nbytes=10) == mla.MLA_ERR_WORKSPACE
+    assert call(p, ptrs=[vp(0)] + args[1:]) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.0e-41, 65504.0, 1.0 + 2**-8 + 2**-20],
+                 dtype=np.float32)
+    bits = datagen.bf16_bits(x)
+    back = datagen.bf16_to_f32(bits)
+    # 1 + 2^-8 is a tie -> even (1.0); 1 + 3*2^-8 is a tie -> even (1 + 2^-6)
+    assert back[0] == 1.0 and back[1] == 1.0 and back[2] == np.float32(1.015625)
+    assert back[3] == -2.5
+    assert back[6] == np.float32(1.0078125)  # just above the tie rounds up
+    # every normal value is within half a bf16 ulp (8 significant bits)
+    norm = np.abs(x) > 1e-37
+    _, e = np.frexp(x[norm])
+    half_ulp = np.ldexp(1.0, e - 9)
+    assert np.all(np.abs(back[norm] - x[norm]) <= half_ulp)
+
+
+def test_datagen_is_seeded_and_shaped():
+    a = datagen.make_config(0)
+    b = datagen.make_config(0)
+    assert np.array_equal(a.cache, b.cache) and np.array_equal(a.w_uk, b.w_uk)
+    assert a.cache.shape == (1, 128, 80) and a.dtype == "f32"
+    assert a.scale == pytest.approx(1 / np.sqrt(48))
+    c = datagen.make_decode_case(B=4, H=128, dc=512, dr=64, dn=128, dv=128, n_max=64,
+                                 ragged=True, seed=3)
+    assert c.cache.dtype == np.uint16 and c.cache.shape == (4, 64, 576)
+    assert np.all((c.seqlens >= 1) & (c.seqlens <= 64))
+    # weights have std 1/sqrt(d_c)
+    w = datagen.bf16_to_f32(c.w_uk)
+    assert abs(w.std() * np.sqrt(512) - 1) < 0.02

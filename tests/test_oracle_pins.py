@@ -385,3 +385,23 @@ def test_pins_catch_plausible_mistakes():
     }
     for name, kw in mutations.items():
         assert _rel(run(**kw), ref) > 1e-3, name
+
+
+# --------------------------------------------------------------------------
+# absorb_q: the content score through the absorbed query equals the score
+# against the decompressed key ("mla-from-scratch" README, absorption)
+# --------------------------------------------------------------------------
+
+def test_absorb_content_score_identity():
+    rng = np.random.default_rng(55)
+    B, H, dn, dc = 2, 3, 16, 40
+    q = rng.standard_normal((B, H, dn))
+    w = rng.standard_normal((H, dn, dc))
+    c = rng.standard_normal(dc)
+    qa = oracle.absorb_q(q, w)
+    for b in range(B):
+        for h in range(H):
+            k = w[h] @ c                     # decompressed key W_UK c
+            assert abs(qa[b, h] @ c - q[b, h] @ k) <= 1e-12 * max(1.0, abs(q[b, h] @ k))
+    # a transposed weight would not even have the right length
+    assert qa.shape == (B, H, dc)
