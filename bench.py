@@ -97,6 +97,10 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0, help="context splits (0 = library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["decode", "copy"], default="decode",
+                    help="copy: a plain device-to-device copy of --copy-bytes, the reference "
+                         "that scales the profiler's byte counters")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--rotate", type=int, default=1,
                     help="distinct input copies cycled through (>1 defeats the 256 MB MALL "
                          "for the small workloads)")
@@ -110,6 +114,25 @@ def main(argv=None):
 
     import numpy as np
     import torch
+
+    if args.mode == "copy":
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        print(json.dumps({"mode": "copy", "bytes_read": args.copy_bytes,
+                          "bytes_written": args.copy_bytes, "ms_per_copy": ms,
+                          "gbps": 2 * args.copy_bytes / (ms * 1e-3) / 1e9}), flush=True)
+        return 0
 
     import mla_latent_kv_12_amd as mla
     from mla_latent_kv_12_amd import datagen

@@ -77,9 +77,12 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, const ui
 #pragma unroll
     for (int bb = 0; bb < kAbsorbBatch; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
     const uint32_t *wrow = reinterpret_cast<const uint32_t *>(w_uk + (static_cast<int64_t>(h) * DN + 32 * w) * DC + col);
-#pragma unroll 8
+    uint32_t wvals[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) wvals[i] = wrow[i * (DC / 2)];  // 32 loads in flight
+#pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const uint32_t wv = wrow[i * (DC / 2)];
+        const uint32_t wv = wvals[i];
         const float w0 = bf16lo(wv), w1 = bf16hi(wv);
 #pragma unroll
         for (int bb = 0; bb < kAbsorbBatch; ++bb) {
@@ -516,7 +519,8 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int B, int H, in
 {
     const int h = blockIdx.x, b0 = blockIdx.y * kMergeBatch, tid = threadIdx.x;
     const int nb = min(kMergeBatch, B - b0);
-    __shared__ float wt[kMergeBatch][kMaxSplits];
+    __shared__ float wt[kMergeBatch][kMaxSplits];  // split weights 2^(m_s - M), 0 for empty
+    __shared__ float ls[kMaxSplits];               // split softmax mass
     __shared__ float inv_l[kMergeBatch];
     __shared__ float wmax[4];
     __shared__ int any_nan;
@@ -524,44 +528,55 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int B, int H, in
 
     for (int bb = 0; bb < nb; ++bb) {
         const int b = b0 + bb;
-        const int64_t base = static_cast<int64_t>(b) * S * H + h;
+        const int64_t base = static_cast<int64_t>(b) * S * H + h;  // row of split 0
         // marked (NaN) splits are recomputed first, in ascending order
         if (tid == 0) any_nan = 0;
         __syncthreads();
-        for (int sp = tid; sp < S; sp += 256)
-            if (__builtin_isnan(part_ml[(base + static_cast<int64_t>(sp) * H) * 2])) any_nan = 1;
+        float ms = -INFINITY;
+        if (tid < S) {
+            ms = part_ml[(base + static_cast<int64_t>(tid) * H) * 2];
+            if (__builtin_isnan(ms)) any_nan = 1;
+        }
         __syncthreads();
         if (any_nan) {
             for (int sp = 0; sp < S; ++sp)
                 if (__builtin_isnan(part_ml[(base + static_cast<int64_t>(sp) * H) * 2]))
                     recompute_partial(cv, H, S, b, sp, h, part_o, part_ml);
+            if (tid < S) ms = part_ml[(base + static_cast<int64_t>(tid) * H) * 2];
         }
-        // max over splits (each split's m read by one thread, then a fixed tree)
-        float mx = -INFINITY;
-        for (int sp = tid; sp < S; sp += 256) mx = fmaxf(mx, part_ml[(base + static_cast<int64_t>(sp) * H) * 2]);
+        // M = max_s m_s (wave tree, then the four wave results in order)
+        float mx = ms;
         for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
         if ((tid & 63) == 0) wmax[tid >> 6] = mx;
         __syncthreads();
         mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-        for (int sp = tid; sp < S; sp += 256) {
-            const float ms = part_ml[(base + static_cast<int64_t>(sp) * H) * 2];
-            wt[bb][sp] = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
+        if (tid < S) {
+            wt[bb][tid] = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
+            ls[tid] = part_ml[(base + static_cast<int64_t>(tid) * H) * 2 + 1];
         }
         __syncthreads();
         if (tid == 0) {
-            float ls = 0.f;  // ascending split order
+            float l = 0.f;  // ascending split order
             for (int sp = 0; sp < S; ++sp)
-                if (wt[bb][sp] != 0.f) ls = fmaf(wt[bb][sp], part_ml[(base + static_cast<int64_t>(sp) * H) * 2 + 1], ls);
-            inv_l[bb] = ls > 0.f ? 1.f / ls : 0.f;
+                if (wt[bb][sp] != 0.f) l = fmaf(wt[bb][sp], ls[sp], l);
+            inv_l[bb] = l > 0.f ? 1.f / l : 0.f;
         }
-        // o_lat columns 2 tid, 2 tid + 1
+        // o_lat columns 2 tid, 2 tid + 1: splits in groups of 8 loads in flight;
+        // empty splits (weight 0, O never written) are selected away, not multiplied.
         float a0 = 0.f, a1 = 0.f;
-        for (int sp = 0; sp < S; ++sp) {
-            const float ws = wt[bb][sp];
-            if (ws != 0.f) {
-                const float2 v = *reinterpret_cast<const float2 *>(part_o + (base + static_cast<int64_t>(sp) * H) * DC + 2 * tid);
-                a0 = fmaf(ws, v.x, a0);
-                a1 = fmaf(ws, v.y, a1);
+        const float *po = part_o + base * DC + 2 * tid;
+        for (int sp0 = 0; sp0 < S; sp0 += 8) {
+            float2 v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (sp0 + k < S) v[k] = *reinterpret_cast<const float2 *>(po + static_cast<int64_t>(sp0 + k) * H * DC);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (sp0 + k < S) {
+                    const float wk = wt[bb][sp0 + k];
+                    a0 = fmaf(wk, wk != 0.f ? v[k].x : 0.f, a0);
+                    a1 = fmaf(wk, wk != 0.f ? v[k].y : 0.f, a1);
+                }
             }
         }
         __syncthreads();
@@ -570,36 +585,41 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int B, int H, in
     }
     __syncthreads();
 
-    // out[b][h][v]: thread handles row v = tid / 2 for batches of its parity.
-    const int v = tid >> 1, par = tid & 1;
-    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(w_uv + (static_cast<int64_t>(h) * DV + v) * DC);
-    float acc[kMergeBatch / 2] = {0.f, 0.f};
-    for (int c = 0; c < DC / 8; ++c) {
-        const u32x4 wv = wrow[c];
+    // out[b][h][v] = W_UV[h][v] . o_lat[b]: wave w takes rows 32 w .. 32 w + 31;
+    // lane (row 32 w + l % 32, column half l / 32) sums 256 columns, 32 loads
+    // of 16 bytes in flight, then the two halves are added.
+    const int lane = tid & 63, v = 32 * (tid >> 6) + (lane & 31), hc = lane >> 5;
+    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(w_uv + (static_cast<int64_t>(h) * DV + v) * DC + 256 * hc);
+    u32x4 wv[32];
+#pragma unroll
+    for (int c = 0; c < 32; ++c) wv[c] = wrow[c];
+    float acc[kMergeBatch] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
         float wf[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            wf[2 * e] = bf16lo(wv[e]);
-            wf[2 * e + 1] = bf16hi(wv[e]);
+            wf[2 * e] = bf16lo(wv[c][e]);
+            wf[2 * e + 1] = bf16hi(wv[c][e]);
         }
 #pragma unroll
-        for (int k = 0; k < kMergeBatch / 2; ++k) {
-            const float *o = &ol[2 * k + par][8 * c];
-            float sacc = acc[k];
+        for (int bb = 0; bb < kMergeBatch; ++bb) {
+            const float *o = &ol[bb][256 * hc + 8 * c];
+            float sacc = acc[bb];
 #pragma unroll
             for (int e = 0; e < 8; ++e) sacc = fmaf(wf[e], o[e], sacc);
-            acc[k] = sacc;
+            acc[bb] = sacc;
         }
     }
 #pragma unroll
-    for (int k = 0; k < kMergeBatch / 2; ++k) {
-        const int bb = 2 * k + par;
-        if (bb < nb) {
+    for (int bb = 0; bb < kMergeBatch; ++bb) acc[bb] += __shfl_xor(acc[bb], 32);
+    if (hc == 0) {
+        for (int bb = 0; bb < nb; ++bb) {
             const int64_t oi = (static_cast<int64_t>(b0 + bb) * H + h) * DV + v;
             if (out_bf16)
-                reinterpret_cast<__bf16 *>(out)[oi] = static_cast<__bf16>(acc[k]);
+                reinterpret_cast<__bf16 *>(out)[oi] = static_cast<__bf16>(acc[bb]);
             else
-                reinterpret_cast<float *>(out)[oi] = acc[k];
+                reinterpret_cast<float *>(out)[oi] = acc[bb];
         }
     }
 }

@@ -102,7 +102,11 @@ def test_prefill_single_token_equals_decode():
 def test_prefill_config4_full():
     case = datagen.make_config(4)
     say(f"config4 prefill T=4096 H=128 seed={datagen.SEED_BASE + 4}")
-    out = run_prefill(case)
+    t = prefill_tensors(case)
+    out16 = run_prefill(case, t)              # the benchmark's launch: bf16 output
+    out = run_prefill(case, t, out_dtype="f32")
+    # the bf16 output is the fp32 result rounded to nearest-even, bit for bit
+    assert np.array_equal(out16, torch.from_numpy(out).to(torch.bfloat16).double().numpy())
     rows = [(0, t) for t in (0, 1, 31, 32, 2047, 4095)]
     heads = [0, 77, 127]
     ref = oracle_rows(case, rows, heads=heads)
