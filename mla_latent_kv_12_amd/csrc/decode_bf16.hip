@@ -122,19 +122,27 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, const ui
 // direct-to-LDS 16-byte buffer loads (buffer_load_dwordx4 ... lds) into three
 // LDS buffers, so two tiles are in flight while one is consumed.  The buffer
 // descriptor's range ends at the split's last row: rows past it arrive as
-// zeros (weight zero, and they can never inject NaN/Inf).  The three buffers
-// rotate; the cross-wave hand-off is an explicit "wait for my tile loads,
-// then s_barrier".
+// zeros (weight zero, and they can never inject NaN/Inf).  The cross-wave
+// hand-off is an explicit "wait for my tile loads, then s_barrier".
 //
-// LDS tile layout: latent rows (1024 B) then RoPE-key rows (128 B), each row's
-// 16-byte chunks XOR-swizzled (latent: chunk ^ (row & 15) inside aligned
-// groups of 16; RoPE: chunk ^ (row & 7)) so that the 32 rows the score MFMA
-// reads at one column land in distinct banks.
+// LDS tile layout: latent row r (one 1-KiB load each, so its placement is
+// free) sits at r * 1280 + 16 * f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1) +
+// 8 ((r >> 3) & 1) < 16: 1280-byte slots keep the staggered rows from
+// overlapping and leave the bank phase to f alone.  That stagger keeps both
+// access patterns free of bank
+// conflicts (for 32 or 64 four-byte banks): the score MFMA's lanes read 16
+// consecutive rows at one column (f distinct mod 16, and mod 8 within 8 rows),
+// and each transposing read takes 32 bytes from 4 consecutive rows r = 4m..4m+3
+// (f = 2k + const, so their windows are 32 bytes apart).  Then come 32
+// RoPE-key rows of 128 bytes, 16-byte chunks XOR-swizzled by (row & 7).
+// Every read address is a per-lane base plus an immediate.
 //
-// Registers: the absorbed query's 512 latent channels stay in VGPRs as the
-// score MFMA's B operand (128 per lane); its 64 RoPE channels live in LDS;
-// the 512 x 32 fp32 latent accumulator of the wave's heads fills the 256
-// AGPRs.
+// Score  S^T[token][head] = C . Qa^T  (A = cache rows, B = absorbed query)
+// Accum  O^T[col][head] += C^T . P^T  (A = cache columns, read with the
+//        transposing ds_read_b64_tr_b16, B = softmax weights from registers)
+// both on v_mfma_f32_32x32x16_bf16.  The absorbed query's 512 latent channels
+// stay in VGPRs (128 per lane), its 64 RoPE channels in LDS; the 512 x 32 fp32
+// accumulator of the wave's heads fills the 256 AGPRs.
 //
 // Softmax: scores are kept in log2 units (scale * log2(e) folded in).  The
 // reference maximum m_ref of each head is fixed by the split's first tile;
@@ -144,19 +152,29 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, const ui
 // marked (NaN maximum) and the merge kernel recomputes that (split, head)
 // with the split's true maximum; ordinary inputs never take that path.
 // ---------------------------------------------------------------------------
-constexpr int kTile = 32;                      // tokens per LDS tile (== split granule)
-constexpr int kLatRow = DC * 2;                // 1024 B
-constexpr int kRopeRow = DR * 2;               // 128 B
-constexpr int kRopeBase = kTile * kLatRow;     // 32768: RoPE rows follow the latent rows
-constexpr int kTileBytes = kTile * (kLatRow + kRopeRow);  // 36864
-constexpr int kThreadsDec = 256;               // 4 waves x 32 heads
-constexpr int kLoadsPerWave = 9;               // 8 latent rows + 1/4 of the RoPE rows
-constexpr int kQRopeBytes = 32 * kRopeRow;     // one wave's 32 heads x 64 RoPE channels
+constexpr int kTile = 32;                       // tokens per LDS tile (== split granule)
+constexpr int kLatRow = DC * 2;                 // 1024 B per latent row
+constexpr int kLatSlot = kLatRow + 256;         // 1280 B LDS slot per latent row
+constexpr int kRopeRow = DR * 2;                // 128 B
+constexpr int kRopeBase = kTile * kLatSlot;     // 40960: RoPE rows follow the latent slots
+constexpr int kTileBytes = kRopeBase + kTile * kRopeRow;  // 45056
+constexpr int kThreadsDec = 256;                // 4 waves x 32 heads
+constexpr int kLoadsPerWave = 9;                // 8 latent rows + 1/4 of the RoPE rows
+constexpr int kQRopeStride = kRopeRow + 16;     // 144 B per head row (bank stagger)
+constexpr int kQRopeBytes = 32 * kQRopeStride;  // one wave's 32 heads
 static_assert(kTile == 4 * 8, "each wave loads 8 latent rows per tile");
 static_assert(kTile * kRopeRow == 4 * 64 * 16, "each wave loads one quarter of the RoPE rows");
 static_assert(kTile == kSplitGranule, "split boundaries must align to tiles");
-static_assert(3 * kTileBytes + 4 * kQRopeBytes + 16 <= 160 * 1024, "LDS budget");
-constexpr float kRefSlack = 64.0f;             // log2 headroom above the reference maximum
+static_assert(3 * kTileBytes + 4 * kQRopeBytes <= 160 * 1024, "LDS budget");
+
+// Byte offset of latent row r inside a tile.
+__host__ __device__ constexpr int lat_slot(int r)
+{
+    return r * kLatSlot + 16 * (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1));
+}
+static_assert(lat_slot(kTile - 1) + kLatRow <= kRopeBase, "staggered rows fit before the RoPE rows");
+static_assert(16 * 15 + kLatRow <= kLatSlot, "a staggered row stays inside its slot");
+constexpr float kRefSlack = 64.0f;              // log2 headroom above the reference maximum
 
 // Wait until at most N of this wave's vector-memory operations are in flight
 // and its LDS operations are done, then meet the other waves at the barrier.
@@ -169,7 +187,9 @@ __device__ __forceinline__ void wait_then_barrier()
 }
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const unsigned char lds_byte;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Buffer descriptor (gfx9 layout) over [base, base + range): 48-bit base,
 // stride 0, byte range, and the raw 32-bit data-format word.  Loads past the
@@ -200,12 +220,13 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, const unsigned char *lds_d
                  :: "s"(m0v), "v"(voff), "s"(rsrc) : "memory");
 }
 
-// Opaque copy: the compiler must recompute what depends on the result inside
-// the loop instead of keeping it live across the whole loop in a register.
-__device__ __forceinline__ int opaque(int x)
+// Transposing LDS read (gfx950): within each group of 16 lanes, lane j gets
+// element (j & 3) of the 4 consecutive bf16 that lanes 4k + (j >> 2) address,
+// for k = 0..3.  Packed two per dword, k = 0 in the low half of dword 0.
+__device__ __forceinline__ u32x2 lds_read_tr4(const unsigned char *p)
 {
-    asm volatile("" : "+v"(x));
-    return x;
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lds_byte *)p);
+    return __builtin_bit_cast(u32x2, v);
 }
 
 __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
@@ -241,15 +262,15 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     // Absorbed query of this lane's head as the score MFMA's B operand:
     // B[k][j = head], lane holds k = 16 s + 8 half + 0..7.  Latent channels
     // (s < 32) in registers; RoPE channels (s = 32..35) in this wave's LDS
-    // slice, row l32, chunks swizzled by (l32 & 7).
+    // slice (head row l32 at a 144-byte stride).
     const uint16_t *qrow = qa + (static_cast<int64_t>(b) * H + hq) * DQK + 8 * half;
     u32x4 qreg[DC / 16];
 #pragma unroll
     for (int s = 0; s < DC / 16; ++s) qreg[s] = *reinterpret_cast<const u32x4 *>(qrow + 16 * s);
-    unsigned char *qr = qrope_lds + w * kQRopeBytes;
+    const unsigned char *qr = qrope_lds + w * kQRopeBytes + l32 * kQRopeStride + 16 * half;
 #pragma unroll
     for (int s = 0; s < DR / 16; ++s)
-        *reinterpret_cast<u32x4 *>(qr + l32 * kRopeRow + 16 * ((2 * s + half) ^ (l32 & 7))) =
+        *reinterpret_cast<u32x4 *>(const_cast<unsigned char *>(qr) + 32 * s) =
             *reinterpret_cast<const u32x4 *>(qrow + DC + 16 * s);
     // Let the query loads land here, once: the compiler then knows they are
     // complete and puts no wait on them inside the tile loop (where any
@@ -262,25 +283,33 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     const i32x4 rs_rope =
         make_rsrc(kpe + static_cast<int64_t>(b) * kpe_sb, static_cast<uint32_t>(end) * kpe_rowb);
 
-    // Issue this wave's nine loads of the tile starting at token n0.
-    // Latent load k fills LDS row r = 8 w + k: LDS chunk = lane, holding the
-    // source chunk lane ^ (r & 15).  The RoPE load fills RoPE rows 8 w .. 8 w + 7:
-    // lane -> row 8 w + lane / 8, LDS chunk lane % 8 holding source chunk
-    // (lane % 8) ^ (row & 7).
+    // This wave's nine loads of the tile starting at token n0: latent rows
+    // 8 w .. 8 w + 7 (one 1-KiB load each), and RoPE rows 8 w .. 8 w + 7 in
+    // one load (lane -> row 8 w + lane / 8, LDS chunk lane % 8 holding source
+    // chunk (lane % 8) ^ (row & 7)).
+    const unsigned lat_src = static_cast<unsigned>(8 * w * ckv_rowb + 16 * lane);
+    const int rr = 8 * w + (lane >> 3);
+    const unsigned rope_src = static_cast<unsigned>(rr * kpe_rowb + 16 * ((lane & 7) ^ (rr & 7)));
     auto issue_tile = [&](int n0, unsigned char *dst) {
-        const int ln = opaque(lane);
-        const unsigned base = static_cast<unsigned>(n0) * static_cast<unsigned>(ckv_rowb);
+        const unsigned lat_base = static_cast<unsigned>(n0) * static_cast<unsigned>(ckv_rowb);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int r = 8 * w + k;
-            const unsigned src = base + static_cast<unsigned>(r * ckv_rowb + 16 * (ln ^ (r & 15)));
-            lds_dma16(rs_lat, dst + r * kLatRow, src);
-        }
-        const int rr = 8 * w + (ln >> 3);
-        const unsigned rsrc_off = static_cast<unsigned>(n0) * static_cast<unsigned>(kpe_rowb) +
-                                  static_cast<unsigned>(rr * kpe_rowb + 16 * ((ln & 7) ^ (rr & 7)));
-        lds_dma16(rs_rope, dst + kRopeBase + w * 8 * kRopeRow, rsrc_off);
+        for (int k = 0; k < 8; ++k)
+            lds_dma16(rs_lat, dst + lat_slot(8 * w + k),
+                      lat_src + lat_base + static_cast<unsigned>(k * ckv_rowb));
+        lds_dma16(rs_rope, dst + kRopeBase + w * 8 * kRopeRow,
+                  rope_src + static_cast<unsigned>(n0) * static_cast<unsigned>(kpe_rowb));
     };
+
+    // Per-lane LDS offsets within a tile (immediates are added per access).
+    // Score A operand, latent step s: row l32, byte 32 s + 16 half.
+    const int s_lat = lat_slot(l32) + 16 * half;
+    // P.C A operand via the transposing read, K step ks, j-block q, read r:
+    // source lane 4 k + c of each 16-lane group g addresses token (row)
+    // 16 ks + 8 r + 4 (g >> 1) + k, latent columns 32 q + 16 (g & 1) + 4 c.
+    // lat_slot of that row = its lane part lat_slot(4 (g >> 1) + k) plus
+    // (16 ks + 8 r) * 1280 + 128 r, an immediate.
+    const int g16 = lane >> 4, k4 = (lane >> 2) & 3, c4 = lane & 3;
+    const int pv_base = lat_slot(4 * (g16 >> 1) + k4) + 2 * (16 * (g16 & 1) + 4 * c4);
 
     f32x16 oacc[16];
 #pragma unroll
@@ -302,16 +331,11 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
         if (t + 2 < ntiles) issue_tile(n0 + 2 * kTile, next_dst);
 
         // ---- scores: S^T[token i][head j] = sum_k C[i][k] Qa[j][k] ----
-        const int ln = opaque(lane);
-        const int l3 = ln & 31, hf = ln >> 5;
-        const int g16 = (hf ^ l3) & 15;
-        const unsigned char *arow = tb + l3 * kLatRow;
-        const unsigned char *rrow = tb + kRopeBase + l3 * kRopeRow;
-        const unsigned char *qrr = qr + l3 * kRopeRow;
+        const unsigned char *sa = tb + s_lat;
+        const unsigned char *sr = tb + kRopeBase + l32 * kRopeRow;
         auto a_at = [&](int s) -> u32x4 {
-            if (s < DC / 16)
-                return *reinterpret_cast<const u32x4 *>(arow + 256 * (s >> 3) + 16 * ((2 * (s & 7)) ^ g16));
-            return *reinterpret_cast<const u32x4 *>(rrow + 16 * ((2 * (s - DC / 16) + hf) ^ (l3 & 7)));
+            if (s < DC / 16) return *reinterpret_cast<const u32x4 *>(sa + 32 * s);
+            return *reinterpret_cast<const u32x4 *>(sr + 16 * ((2 * (s - DC / 16) + half) ^ (l32 & 7)));
         };
         f32x16 sacc;
 #pragma unroll
@@ -321,22 +345,27 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
         for (int s = 0; s < 4; ++s) abuf[s] = a_at(s);
 #pragma unroll
         for (int s = 0; s < DQK / 16; ++s) {
-            u32x4 bq;
-            if (s < DC / 16)
-                bq = qreg[s];
-            else
-                bq = *reinterpret_cast<const u32x4 *>(qrr + 16 * ((2 * (s - DC / 16) + hf) ^ (l3 & 7)));
+            const u32x4 bq = s < DC / 16 ? qreg[s]
+                                         : *reinterpret_cast<const u32x4 *>(qr + 32 * (s - DC / 16));
             sacc = mfma32(abuf[s & 3], bq, sacc);
             if (s + 4 < DQK / 16) abuf[s & 3] = a_at(s + 4);
             __builtin_amdgcn_sched_barrier(0);
         }
         // sacc[r] is token 8 (r/4) + 4 half + r%4 of the tile, head l32.
         float tmax = -INFINITY;
+        if (n0 + kTile <= end) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int tok = n0 + 8 * (r >> 2) + 4 * half + (r & 3);
-            sacc[r] = tok < end ? sacc[r] * c2 : -INFINITY;
-            tmax = fmaxf(tmax, sacc[r]);
+            for (int r = 0; r < 16; ++r) {
+                sacc[r] *= c2;
+                tmax = fmaxf(tmax, sacc[r]);
+            }
+        } else {  // the split's last, partial tile
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int tok = n0 + 8 * (r >> 2) + 4 * half + (r & 3);
+                sacc[r] = tok < end ? sacc[r] * c2 : -INFINITY;
+                tmax = fmaxf(tmax, sacc[r]);
+            }
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
         if (t == 0) m_ref = tmax;
@@ -348,48 +377,31 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const float p0 = exp2f(sacc[8 * ks + 2 * p] - m_ref);
-                const float p1 = exp2f(sacc[8 * ks + 2 * p + 1] - m_ref);
-                const uint32_t wpk = pack_bf16(p0, p1);
-                psum += bf16lo(wpk) + bf16hi(wpk);  // mass of the rounded weights
-                pk[ks][p] = wpk;
+                const float p0 = __builtin_amdgcn_exp2f(sacc[8 * ks + 2 * p] - m_ref);
+                const float p1 = __builtin_amdgcn_exp2f(sacc[8 * ks + 2 * p + 1] - m_ref);
+                psum += p0 + p1;
+                pk[ks][p] = pack_bf16(p0, p1);
             }
         l_run += psum;
 
         // ---- O^T[col][head] += C^T[col][token] P^T[token][head] ----
-        // K step ks covers tokens 16 ks + {0..3, 8..11} + 4 half for this
-        // lane, where the score accumulator left them.  j-block q = 4u + v
-        // holds latent column 128 u + 4 i + v in its row i; lane l32 reads
-        // columns 128 u + 4 l32 .. + 3 = logical chunk 16 u + l32 / 2.
-        auto v_at = [&](int e, int ks, int u) -> u32x2 {
-            const int rl = 8 * (e >> 2) + 4 * hf + (e & 3);  // row within a 16-row half tile
-            const int off = rl * kLatRow + 16 * (((l3 >> 1) ^ rl) & 15) + 8 * (l3 & 1);
-            return *reinterpret_cast<const u32x2 *>(tb + off + 16 * ks * kLatRow + 256 * u);
+        // K step ks covers tokens 16 ks + 8 (e / 4) + 4 half + e % 4 (e = 0..7
+        // across the two transposing reads), where the score accumulator left
+        // them; j-block q holds latent columns 32 q .. 32 q + 31.
+        const unsigned char *pv = tb + pv_base;
+        auto a_tr = [&](int ks, int q) -> u32x4 {
+            const u32x2 lo = lds_read_tr4(pv + (16 * ks) * kLatSlot + 64 * q);
+            const u32x2 hi = lds_read_tr4(pv + (16 * ks + 8) * kLatSlot + 128 + 64 * q);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
         };
-        u32x2 R[8], Rn[8];
+        u32x4 av[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) R[e] = v_at(e, 0, 0);
+        for (int i = 0; i < 4; ++i) av[i] = a_tr(0, i);
 #pragma unroll
-        for (int g = 0; g < 8; ++g) {  // g = 4 ks + u: one group of four j-blocks
-            const int ks = g >> 2, u = g & 3;
-            if (g + 1 < 8) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) Rn[e] = v_at(e, (g + 1) >> 2, (g + 1) & 3);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint32_t sel = (v & 1) ? 0x07060302u : 0x05040100u;
-                u32x4 a;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t x = (v < 2) ? R[2 * p][0] : R[2 * p][1];
-                    const uint32_t y = (v < 2) ? R[2 * p + 1][0] : R[2 * p + 1][1];
-                    a[p] = __builtin_amdgcn_perm(y, x, sel);  // {x.half(v), y.half(v)}
-                }
-                oacc[4 * u + v] = mfma32(a, pk[ks], oacc[4 * u + v]);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) R[e] = Rn[e];
+        for (int i = 0; i < 32; ++i) {  // i = 16 ks + q
+            const int ks = i >> 4, q = i & 15;
+            oacc[q] = mfma32(av[i & 3], pk[ks], oacc[q]);
+            if (i + 4 < 32) av[i & 3] = a_tr((i + 4) >> 4, (i + 4) & 15);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -404,15 +416,15 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     }
 
     // ---- write the split partial: un-normalised O, reference max, mass ----
+    // Accumulator q, element r is latent column 32 q + 8 (r/4) + 4 half + r%4.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     float *orow = part_o + prow * DC;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int q = 0; q < 16; ++q)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = 8 * (r >> 2) + 4 * half + (r & 3);
-            f32x4 v4 = {oacc[4 * u + 0][r], oacc[4 * u + 1][r], oacc[4 * u + 2][r], oacc[4 * u + 3][r]};
-            *reinterpret_cast<f32x4 *>(orow + 128 * u + 4 * i) = v4;
+        for (int m = 0; m < 4; ++m) {
+            f32x4 v4 = {oacc[q][4 * m], oacc[q][4 * m + 1], oacc[q][4 * m + 2], oacc[q][4 * m + 3]};
+            *reinterpret_cast<f32x4 *>(orow + 32 * q + 8 * m + 4 * half) = v4;
         }
     if (half == 0) {
         // NaN marks a head whose weights could overflow: the merge kernel
