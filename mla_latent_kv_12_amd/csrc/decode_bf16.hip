@@ -167,13 +167,24 @@ static_assert(kTile * kRopeRow == 4 * 64 * 16, "each wave loads one quarter of t
 static_assert(kTile == kSplitGranule, "split boundaries must align to tiles");
 static_assert(3 * kTileBytes + 4 * kQRopeBytes <= 160 * 1024, "LDS budget");
 
-// Byte offset of latent row r inside a tile.
+// Byte offset of latent row r inside a tile.  Each row starts 16 B times a
+// stagger in 0..15 into its slot: 4 (r mod 4) + (r div 4 mod 4).  Rows that
+// one score read touches together (consecutive r) then start in distinct
+// 16-byte bank groups, and so do the rows of one transposing read.
 __host__ __device__ constexpr int lat_slot(int r)
 {
-    return r * kLatSlot + 16 * (2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1));
+    return r * kLatSlot + 16 * (4 * (r & 3) + ((r >> 2) & 3));
 }
 static_assert(lat_slot(kTile - 1) + kLatRow <= kRopeBase, "staggered rows fit before the RoPE rows");
 static_assert(16 * 15 + kLatRow <= kLatSlot, "a staggered row stays inside its slot");
+// Rows 16 ks + 8 + j and 16 ks + j differ by 8 * 1280 plus this stagger delta,
+// the same for every j in 0..7 and every ks, so the second transposing read
+// of a K step is the first one's address plus an immediate.
+constexpr int kTrHiStagger = lat_slot(8) - 8 * kLatSlot;
+static_assert(kTrHiStagger == lat_slot(9) - lat_slot(1) - 8 * kLatSlot &&
+              kTrHiStagger == lat_slot(15) - lat_slot(7) - 8 * kLatSlot &&
+              kTrHiStagger == lat_slot(31) - lat_slot(23) - 8 * kLatSlot,
+              "uniform stagger delta between the two halves of a K step");
 constexpr float kRefSlack = 64.0f;              // log2 headroom above the reference maximum
 
 // Wait until at most N of this wave's vector-memory operations are in flight
@@ -307,7 +318,7 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     // source lane 4 k + c of each 16-lane group g addresses token (row)
     // 16 ks + 8 r + 4 (g >> 1) + k, latent columns 32 q + 16 (g & 1) + 4 c.
     // lat_slot of that row = its lane part lat_slot(4 (g >> 1) + k) plus
-    // (16 ks + 8 r) * 1280 + 128 r, an immediate.
+    // (16 ks + 8 r) * 1280 + r * kTrHiStagger, an immediate.
     const int g16 = lane >> 4, k4 = (lane >> 2) & 3, c4 = lane & 3;
     const int pv_base = lat_slot(4 * (g16 >> 1) + k4) + 2 * (16 * (g16 & 1) + 4 * c4);
 
@@ -391,7 +402,7 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
         const unsigned char *pv = tb + pv_base;
         auto a_tr = [&](int ks, int q) -> u32x4 {
             const u32x2 lo = lds_read_tr4(pv + (16 * ks) * kLatSlot + 64 * q);
-            const u32x2 hi = lds_read_tr4(pv + (16 * ks + 8) * kLatSlot + 128 + 64 * q);
+            const u32x2 hi = lds_read_tr4(pv + (16 * ks + 8) * kLatSlot + kTrHiStagger + 64 * q);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
         };
         u32x4 av[4];
