@@ -58,6 +58,32 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "decode_splitkv_bf16_V3_B8_L131072_hbm_traffic.txt")
+
+
+def measured_traffic(workload_is_profiled: bool):
+    """HBM bytes per launch of the split-KV kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (copy-calibrated), or None when the kernel
+    source has changed since they were taken or the workload differs."""
+    import hashlib
+
+    if not workload_is_profiled or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("#") or "=" not in line:
+            continue
+        k, v = line.split("=", 1)
+        kv[k.strip()] = v.strip()
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), kv.get("kernel_source", ""))
+    if not os.path.isfile(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("kernel_source_sha256"):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(case, seconds: float):
     """fp64 oracle (absorbed form) on a bounded sample of (sequence, head) pairs
     of the same workload, all host threads; scaled to tokens/s of a full step."""
@@ -87,6 +113,65 @@ def cpu_baseline(case, seconds: float):
                       f"{ts:.1f} s, extrapolated to a full step ({t_step:.1f} s)"}
 
 
+def bench_prefill(args, mla, datagen):
+    """Naive causal prefill (decompress K/V for every cached row, then causal
+    attention) on the V3 shape, batch 1, 4096 tokens; one JSON line with the
+    whole call's bf16 MFMA throughput against the dense peak."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_12_amd.tensors import to_device
+
+    case = datagen.make_config(4)
+    dt = case.dtype
+    cache = to_device(case.cache, dt)
+    q_nope, q_rope = to_device(case.q_nope, dt), to_device(case.q_rope, dt)
+    w_uk, w_uv = to_device(case.w_uk, dt), to_device(case.w_uv, dt)
+    ckv, kpe = cache[:, :, : case.dc], cache[:, :, case.dc:]
+    seqlens = torch.from_numpy(case.seqlens.astype(np.int32)).cuda()
+    params = mla.prefill_params(q_nope, q_rope, w_uk, w_uv, ckv, kpe, softmax_scale=case.scale)
+    ws = torch.empty(mla.prefill_workspace_bytes(params), dtype=torch.uint8, device="cuda")
+    out = torch.empty((case.B, case.T, case.H, case.dv), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        mla.prefill_naive(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, out=out, workspace=ws,
+                          params=params)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    ms = float(np.mean(per))
+    L = case.seqlens.astype(np.int64)
+    rows = int(L.sum())
+    # causal (query, key) pairs: query t at position L - T + t sees keys 0..pos
+    pairs = int(sum(int(l) * case.T - case.T * (case.T - 1) // 2 for l in L))
+    f_decomp = 2 * rows * case.H * case.dc * (case.dn + case.dv)
+    f_attn = 2 * pairs * case.H * (case.dn + case.dr + case.dv)
+    flops = f_decomp + f_attn
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "mode": "prefill", "metric": "naive causal prefill bf16 MFMA TFLOP/s (% of dense peak)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic (seeded normals; c = W_DKV x from x of width 7168)",
+        "config": {"workload": case.name, "batch": case.B, "tokens": case.T, "heads": case.H,
+                   "cached_tokens_total": rows},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "algorithmic_flops_per_call": flops, "decompress_flops": f_decomp,
+                     "attention_flops": f_attn},
+        "ms_p10_p90": [float(np.percentile(per, 10)), float(np.percentile(per, 90))]}),
+        flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,9 +182,10 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0, help="context splits (0 = library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["decode", "copy"], default="decode",
-                    help="copy: a plain device-to-device copy of --copy-bytes, the reference "
-                         "that scales the profiler's byte counters")
+    ap.add_argument("--mode", choices=["decode", "prefill", "copy"], default="decode",
+                    help="prefill: the naive causal prefill (V3 shape, T=4096) against the bf16 "
+                         "MFMA peak; copy: a plain device-to-device copy of --copy-bytes, the "
+                         "reference that scales the profiler's byte counters")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--rotate", type=int, default=1,
                     help="distinct input copies cycled through (>1 defeats the 256 MB MALL "
@@ -137,6 +223,9 @@ def main(argv=None):
     import mla_latent_kv_12_amd as mla
     from mla_latent_kv_12_amd import datagen
     from mla_latent_kv_12_amd.tensors import decode_tensors
+
+    if args.mode == "prefill":
+        return bench_prefill(args, mla, datagen)
 
     t_gen = time.perf_counter()
     case = datagen.make_config(args.config)
@@ -218,7 +307,8 @@ def main(argv=None):
                       "splitkv_p10_p90": [1e3 * float(np.percentile(attn, 10)),
                                           1e3 * float(np.percentile(attn, 90))]},
         "roofline": {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": attn_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": attn_gbps / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(args.config == 3 and args.splits in (0, 32)),
                      "kernel": "decode_splitkv_bf16_kernel",
                      "algorithmic_bytes_per_launch": cache_bytes},
     }

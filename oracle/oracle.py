@@ -58,27 +58,32 @@ def build(force: bool = True) -> str:
 _lib = None
 
 
+def _open(path: str) -> ctypes.CDLL:
+    """Load a build of ``mla_oracle.c`` and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    vp, i64, dp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p
+    for name in ("oracle_decode_naive", "oracle_decode_absorbed"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, vp, vp, vp, vp, vp, i64, dp, dp]
+        f.restype = ctypes.c_int
+    lib.oracle_absorb_q.argtypes = [ctypes.POINTER(_Dims), vp, vp, dp]
+    lib.oracle_absorb_q.restype = ctypes.c_int
+    lib.oracle_prefill_naive.argtypes = [ctypes.POINTER(_Dims), i64, vp, vp, vp, vp, vp, vp,
+                                         vp, vp, i64, dp]
+    lib.oracle_prefill_naive.restype = ctypes.c_int
+    lib.oracle_kv_cache_bytes.argtypes = [i64] * 6
+    lib.oracle_kv_cache_bytes.restype = ctypes.c_uint64
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
-        lib = ctypes.CDLL(_LIB)
-        vp, i64, dp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p
-        for name in ("oracle_decode_naive", "oracle_decode_absorbed"):
-            f = getattr(lib, name)
-            f.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, vp, vp, vp, vp, vp, i64, dp, dp]
-            f.restype = ctypes.c_int
-        lib.oracle_absorb_q.argtypes = [ctypes.POINTER(_Dims), vp, vp, dp]
-        lib.oracle_absorb_q.restype = ctypes.c_int
-        lib.oracle_prefill_naive.argtypes = [ctypes.POINTER(_Dims), i64, vp, vp, vp, vp, vp, vp,
-                                             vp, vp, i64, dp]
-        lib.oracle_prefill_naive.restype = ctypes.c_int
-        lib.oracle_kv_cache_bytes.argtypes = [i64] * 6
-        lib.oracle_kv_cache_bytes.restype = ctypes.c_uint64
-        lib.oracle_max_threads.restype = ctypes.c_int
-        lib.oracle_set_threads.argtypes = [ctypes.c_int]
-        _lib = lib
+        _lib = _open(_LIB)
     return _lib
 
 

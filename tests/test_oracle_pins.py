@@ -210,11 +210,11 @@ def test_uniform_scores_give_mean():
 # P5: one dominant token (huge logits, no overflow) -> W_UV c_{n*}
 # --------------------------------------------------------------------------
 
-def test_dominant_token_no_overflow():
+@pytest.mark.parametrize("star", [0, 17, 39])   # first, middle and last cached row
+def test_dominant_token_no_overflow(star):
     rng = np.random.default_rng(21)
     B, H, dc, dr, dn, dv, N = 1, 2, 64, 16, 32, 32, 40
     _, _, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, N)
-    star = 17
     q_nope = np.zeros((B, H, dn))
     q_rope = np.stack([1e3 * cache[0, star, dc:]] * H)[None]
     for fn in (oracle.decode_naive, oracle.decode_absorbed):
