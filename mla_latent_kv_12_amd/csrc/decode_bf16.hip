@@ -20,35 +20,15 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include "cdna4.h"
 #include "mla_internal.h"
 
 namespace mla {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace cdna4;
 
 constexpr int DC = 512, DR = 64, DQK = DC + DR, DN = 128, DV = 128;
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
-{
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
 
 // ---------------------------------------------------------------------------
 // 1. absorb: grid (4 column quarters, H, ceil(B/8)), 256 threads.
@@ -126,14 +106,13 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, const ui
 // hand-off is an explicit "wait for my tile loads, then s_barrier".
 //
 // LDS tile layout: latent row r (one 1-KiB load each, so its placement is
-// free) sits at r * 1280 + 16 * f(r), f(r) = 2 (r & 3) + ((r >> 2) & 1) +
-// 8 ((r >> 3) & 1) < 16: 1280-byte slots keep the staggered rows from
-// overlapping and leave the bank phase to f alone.  That stagger keeps both
-// access patterns free of bank
-// conflicts (for 32 or 64 four-byte banks): the score MFMA's lanes read 16
-// consecutive rows at one column (f distinct mod 16, and mod 8 within 8 rows),
-// and each transposing read takes 32 bytes from 4 consecutive rows r = 4m..4m+3
-// (f = 2k + const, so their windows are 32 bytes apart).  Then come 32
+// free) sits at r * 1280 + 16 * f(r), f(r) = 4 (r & 3) + ((r >> 2) & 3) < 16:
+// 1280-byte slots keep the staggered rows from overlapping and leave the bank
+// phase to f alone.  The stagger keeps both access patterns nearly free of
+// bank conflicts: the score MFMA's lanes read 16 consecutive rows at one
+// column (f distinct over any 16 consecutive rows), and each 16-lane group of
+// a transposing read takes 32 bytes from 4 consecutive rows r = 4m..4m+3
+// (f = 4k + const, so their windows start 64 bytes apart).  Then come 32
 // RoPE-key rows of 128 bytes, 16-byte chunks XOR-swizzled by (row & 7).
 // Every read address is a per-lane base plus an immediate.
 //
@@ -186,59 +165,6 @@ static_assert(kTrHiStagger == lat_slot(9) - lat_slot(1) - 8 * kLatSlot &&
               kTrHiStagger == lat_slot(31) - lat_slot(23) - 8 * kLatSlot,
               "uniform stagger delta between the two halves of a K step");
 constexpr float kRefSlack = 64.0f;              // log2 headroom above the reference maximum
-
-// Wait until at most N of this wave's vector-memory operations are in flight
-// and its LDS operations are done, then meet the other waves at the barrier.
-// The "memory" clobber keeps the compiler from moving LDS accesses across.
-template <int N>
-__device__ __forceinline__ void wait_then_barrier()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) const unsigned char lds_byte;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// Buffer descriptor (gfx9 layout) over [base, base + range): 48-bit base,
-// stride 0, byte range, and the raw 32-bit data-format word.  Loads past the
-// range return zeros.  Every field is wave-uniform (SGPRs).
-__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t range)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    i32x4 r;
-    r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
-    r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
-    r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(range));
-    r[3] = 0x00020000;
-    return r;
-}
-
-// One wave-wide direct-to-LDS load: lane i's 16 bytes at byte offset voff of
-// the buffer land at LDS address lds_dst + 16 i.  Issued as inline assembly
-// so that the compiler does not track it: it would otherwise make every later
-// LDS read wait for all loads in flight.  Completion is awaited explicitly
-// (wait_then_barrier) before any wave reads the destination.  M0 carries the
-// LDS base; this kernel has no other M0 user.  The instruction has no
-// register result.
-__device__ __forceinline__ void lds_dma16(i32x4 rsrc, const unsigned char *lds_dst, unsigned voff)
-{
-    const unsigned m0v = __builtin_amdgcn_readfirstlane(
-        static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_byte *)lds_dst)));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(m0v), "v"(voff), "s"(rsrc) : "memory");
-}
-
-// Transposing LDS read (gfx950): within each group of 16 lanes, lane j gets
-// element (j & 3) of the 4 consecutive bf16 that lanes 4k + (j >> 2) address,
-// for k = 0..3.  Packed two per dword, k = 0 in the low half of dword 0.
-__device__ __forceinline__ u32x2 lds_read_tr4(const unsigned char *p)
-{
-    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lds_byte *)p);
-    return __builtin_bit_cast(u32x2, v);
-}
 
 __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     int H, int S, int64_t n_max, const uint16_t *__restrict__ ckv, int64_t ckv_sb, int ckv_rowb,

@@ -302,6 +302,10 @@ mla_status check_prefill_params(const mla_prefill_params *p)
         return fail(MLA_ERR_UNSUPPORTED, "bf16 prefill supports d_c=512, d_r=64, d_n=d_v=128");
     if (p->ckv_stride_n < p->d_c || (p->d_r > 0 && p->kpe_stride_n < p->d_r))
         return fail(MLA_ERR_INVALID_ARG, "cache row stride smaller than the row width");
+    if (p->dtype == MLA_BF16 &&
+        ((uint64_t)(p->n_max + 256) * (uint64_t)p->ckv_stride_n * 2 >= (1ull << 32) ||
+         (uint64_t)p->n_max * (uint64_t)p->kpe_stride_n * 2 >= (1ull << 32)))
+        return fail(MLA_ERR_UNSUPPORTED, "bf16 prefill: one sequence's cache rows must span < 4 GiB");
     if (p->batch > 1 && (p->ckv_stride_b < p->n_max * p->ckv_stride_n ||
                          (p->d_r > 0 && p->kpe_stride_b < p->n_max * p->kpe_stride_n)))
         return fail(MLA_ERR_INVALID_ARG, "cache sequence stride smaller than n_max rows");

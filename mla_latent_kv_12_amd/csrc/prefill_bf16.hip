@@ -1,76 +1,119 @@
 // prefill_bf16.hip -- naive (decompress-then-attend) causal MLA prefill for
 // the DeepSeek-V2/V3 shape on gfx950, bf16 storage, fp32 accumulation.
 //
-//   1. decompress: K_nope[b][n][h] = W_UK[h] c[b][n] and V[b][n][h] = W_UV[h] c[b][n]
+//   1. decompress: K_nope[b][h][n] = W_UK[h] c[b][n] and V[b][h][n] = W_UV[h] c[b][n]
 //      for every cached row, written to the workspace (materialised on
 //      purpose: this is the naive form the pages contrast with absorption --
 //      distaisys deep-dive, section 3; songhuiming walk-through, MLA step 2,
-//      "up-project ALL cached latents to K, V").  One MFMA GEMM
-//      [rows x 512] . [512 x H*128] per weight.
+//      where all cached latents are up-projected to K and V).  One MFMA GEMM
+//      per (head, 256-token block, weight), head-major output so that each
+//      head's keys and values are contiguous.
 //   2. causal attention: query t (position L - T + t) attends over rows
 //      n <= its position with key [K_nope ; k^R] (k^R shared by all heads)
-//      and value V.  Scores and P.V on v_mfma_f32_32x32x16_bf16 with an
-//      online softmax; one workgroup per (128 queries, head, sequence).
+//      and value V.  One workgroup of 8 waves per (256 queries, head,
+//      sequence); key tiles of 64 rows stream HBM -> LDS with direct-to-LDS
+//      loads, three tiles deep; scores and P.V on v_mfma_f32_32x32x16_bf16
+//      with an online softmax.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include "cdna4.h"
 #include "mla_internal.h"
 
 namespace mla {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace cdna4;
 
 constexpr int DC = 512, DR = 64, DN = 128, DV = 128, DQK = DN + DR;
-constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+__device__ __forceinline__ int clamp_len(int32_t v, int64_t n_max)
 {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    return static_cast<int>(min<int64_t>(max<int64_t>(v, 0), n_max));
 }
 
 // ---------------------------------------------------------------------------
-// 1. decompress GEMM.  D[feature][token] = W[feature][:] . c[token][:], i.e.
-//    out[token][feature] for feature = h*128 + i over all heads.
-//    Workgroup tile: 128 features x 128 tokens, 4 waves as 2 x 2 of 64 x 64.
+// 1. decompress GEMM: D[token][feature] = c[token][:] . W[feature][:] for the
+//    128 features of one head and 256 tokens.  8 waves as 2 (features) x 4
+//    (tokens) of 64 x 64.  K (the 512 latent channels) in chunks of 64: each
+//    chunk is 128 W rows + 256 c rows of 128 bytes, loaded direct-to-LDS,
+//    three chunks deep.  Row r's 16-byte pieces are XOR-swizzled by
+//    (r >> 1) & 7, so the MFMA operand reads (16 consecutive rows at one
+//    piece) touch 16 distinct bank groups.  The bf16 result is staged in LDS
+//    and written as whole 256-byte rows of the head-major output.
 // ---------------------------------------------------------------------------
-constexpr int GT = 128;            // tile edge (features and tokens)
-constexpr int GK = 32;             // K chunk per LDS stage
-constexpr int GRow = GK * 2 + 16;  // 80-byte padded LDS row
-constexpr int kGemmThreads = 256;
+constexpr int kGF = 128;                                // features per workgroup (one head)
+constexpr int kGN = 256;                                // tokens per workgroup
+constexpr int kGK = 64;                                 // K chunk
+constexpr int kGWaves = 8;
+constexpr int kGThreads = 64 * kGWaves;
+constexpr int kGRowB = kGK * 2;                         // 128 B per LDS row of a chunk
+constexpr int kGWBytes = kGF * kGRowB;                  // 16 KiB
+constexpr int kGStage = kGWBytes + kGN * kGRowB;        // 48 KiB
+constexpr int kGDmaPerWave = kGStage / 1024 / kGWaves;  // 6
+constexpr int kGChunks = DC / kGK;                      // 8
+constexpr int kGOutRow = DN * 2 + 16;                   // 272 B epilogue staging row
+static_assert(kGF == DN && kGF == DV, "one workgroup covers one head's features");
+static_assert(kGDmaPerWave * 1024 * kGWaves == kGStage, "whole loads per wave");
+static_assert(kGWBytes / 1024 == 2 * kGWaves, "the first two loads of each wave are W rows");
+static_assert(3 * kGStage <= 160 * 1024, "LDS budget");
+static_assert(kGN * kGOutRow <= 3 * kGStage, "epilogue staging fits in the chunk buffers");
 
-__global__ __launch_bounds__(kGemmThreads) void decompress_gemm_bf16_kernel(
-    int64_t n_max, int n_feat, const uint16_t *__restrict__ w, const uint16_t *__restrict__ ckv,
-    int64_t ckv_sb, int64_t ckv_sn, const int32_t *__restrict__ seqlens, uint16_t *__restrict__ dst)
+__global__ __launch_bounds__(kGThreads, 1) void decompress_gemm_bf16_kernel(
+    int H, int64_t n_max, const uint16_t *__restrict__ w_uk, const uint16_t *__restrict__ w_uv,
+    const uint16_t *__restrict__ ckv, int64_t ckv_sb, int ckv_rowb,
+    const int32_t *__restrict__ seqlens, uint16_t *__restrict__ kbuf, uint16_t *__restrict__ vbuf)
 {
-    __shared__ __attribute__((aligned(16))) unsigned char sw[GT * GRow];
-    __shared__ __attribute__((aligned(16))) unsigned char sc[GT * GRow];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[3 * kGStage];
 
-    const int f0 = blockIdx.x * GT;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.y) * GT;
-    const int b = blockIdx.z;
-    const int L = static_cast<int>(min<int64_t>(max(seqlens[b], 0), n_max));
+    const int h = blockIdx.x;
+    const int n0 = blockIdx.y * kGN;
+    const int b = blockIdx.z >> 1, which = blockIdx.z & 1;
+    const int L = clamp_len(seqlens[b], n_max);
     if (n0 >= L) return;  // rows past the cached length are never attended to
+    const uint16_t *w = which ? w_uv : w_uk;
+    uint16_t *dst = which ? vbuf : kbuf;
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     const int half = lane >> 5, l32 = lane & 31;
-    const int wf = (wv >> 1) * 64, wt = (wv & 1) * 64;
+    const int wf = (wv & 1) * 64, wt = (wv >> 1) * 64;
 
-    const uint16_t *cb = ckv + static_cast<int64_t>(b) * ckv_sb;
+    const i32x4 rs_w = make_rsrc(w + static_cast<int64_t>(h) * DN * DC, DN * DC * 2);
+    const i32x4 rs_c = make_rsrc(ckv + static_cast<int64_t>(b) * ckv_sb,
+                                 static_cast<uint32_t>(L) * static_cast<uint32_t>(ckv_rowb));
+
+    // Load d = wv + 8 e of a chunk (e = 0..5): d < 16 are W rows 8 d .. 8 d + 7,
+    // the rest c rows 8 (d - 16) .. + 7.  Lane -> row 8 i + lane / 8, LDS piece
+    // lane % 8 holding source piece (lane % 8) ^ ((row >> 1) & 7).
+    unsigned voff[kGDmaPerWave];
+#pragma unroll
+    for (int e = 0; e < kGDmaPerWave; ++e) {
+        const int d = wv + kGWaves * e;
+        const int i = d < 16 ? d : d - 16;
+        const int row = 8 * i + (lane >> 3);
+        const int piece = (lane & 7) ^ ((row >> 1) & 7);
+        voff[e] = d < 16 ? static_cast<unsigned>(row * DC * 2 + 16 * piece)
+                         : static_cast<unsigned>((n0 + row) * ckv_rowb + 16 * piece);
+    }
+    auto issue_chunk = [&](int kc, unsigned char *stage) {
+        const unsigned k_byte = static_cast<unsigned>(kc * kGK * 2);
+#pragma unroll
+        for (int e = 0; e < kGDmaPerWave; ++e) {
+            const int d = wv + kGWaves * e;
+            if (e < 2)
+                lds_dma16(rs_w, stage + 1024 * d, voff[e] + k_byte);
+            else
+                lds_dma16(rs_c, stage + kGWBytes + 1024 * (d - 16), voff[e] + k_byte);
+        }
+    };
+
+    // Operand reads: row base + 32 rows * 128 B per block (immediate), piece
+    // (2 ks + half) ^ ((l32 >> 1) & 7).
+    int aoff[kGK / 16];
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks)
+        aoff[ks] = l32 * kGRowB + 16 * ((2 * ks + half) ^ ((l32 >> 1) & 7));
+
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -79,99 +122,133 @@ __global__ __launch_bounds__(kGemmThreads) void decompress_gemm_bf16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // per K chunk: 128 rows x 64 B of each operand = 512 16-byte pieces, 2 per thread
-    u32x4 pw[2], pc[2];
-    auto load = [&](int k0) {
+    issue_chunk(0, lds);
+    issue_chunk(1, lds + kGStage);
+    int buf = 0;
+    for (int kc = 0; kc < kGChunks; ++kc) {
+        if (kc + 1 < kGChunks)
+            wait_then_barrier<kGDmaPerWave>();
+        else
+            wait_then_barrier<0>();
+        if (kc + 2 < kGChunks) issue_chunk(kc + 2, lds + (buf == 0 ? 2 : buf - 1) * kGStage);
+        const unsigned char *st = lds + buf * kGStage;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int c = tid + kGemmThreads * e, row = c >> 2, cc = c & 3;
-            pw[e] = *reinterpret_cast<const u32x4 *>(w + static_cast<int64_t>(f0 + row) * DC + k0 + 8 * cc);
-            const int64_t n = n0 + row;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (n < L) v = *reinterpret_cast<const u32x4 *>(cb + n * ckv_sn + k0 + 8 * cc);
-            pc[e] = v;
-        }
-    };
-    load(0);
-    for (int k0 = 0; k0 < DC; k0 += GK) {
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int c = tid + kGemmThreads * e, row = c >> 2, cc = c & 3;
-            *reinterpret_cast<u32x4 *>(sw + row * GRow + 16 * cc) = pw[e];
-            *reinterpret_cast<u32x4 *>(sc + row * GRow + 16 * cc) = pc[e];
-        }
-        __syncthreads();
-        if (k0 + GK < DC) load(k0 + GK);
-#pragma unroll
-        for (int ks = 0; ks < GK / 16; ++ks) {
-            u32x4 a[2], bb[2];
+        for (int ks = 0; ks < kGK / 16; ++ks) {
+            u32x4 a[2], c[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                a[i] = *reinterpret_cast<const u32x4 *>(sw + (wf + 32 * i + l32) * GRow + 32 * ks + 16 * half);
-                bb[i] = *reinterpret_cast<const u32x4 *>(sc + (wt + 32 * i + l32) * GRow + 32 * ks + 16 * half);
+                a[i] = *reinterpret_cast<const u32x4 *>(st + (wf + 32 * i) * kGRowB + aoff[ks]);
+                c[i] = *reinterpret_cast<const u32x4 *>(st + kGWBytes + (wt + 32 * i) * kGRowB + aoff[ks]);
             }
+            // D^T[feature][token]: A = W rows, B = c rows
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], bb[j], acc[i][j]);
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], c[j], acc[i][j]);
         }
+        buf = buf == 2 ? 0 : buf + 1;
     }
 
-    // D[feature i][token j]: lane holds token j = l32, features 8(r/4)+4half+r%4
+    // Epilogue: stage [token][feature] bf16 rows, then whole-row stores.
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int64_t n = n0 + wt + 32 * j + l32;
-        if (n >= L) continue;
-        uint16_t *drow = dst + (static_cast<int64_t>(b) * n_max + n) * n_feat;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) {
+            unsigned char *row = lds + (wt + 32 * j + l32) * kGOutRow;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int feat = f0 + wf + 32 * i + 8 * g + 4 * half;
-                u32x2 v = {pack_bf16(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]),
-                           pack_bf16(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
-                *reinterpret_cast<u32x2 *>(drow + feat) = v;
+                const int feat = wf + 32 * i + 8 * g + 4 * half;
+                const u32x2 v = {pack_bf16(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]),
+                                 pack_bf16(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
+                *reinterpret_cast<u32x2 *>(row + 2 * feat) = v;
             }
+        }
+    __syncthreads();
+    uint16_t *dbase = dst + ((static_cast<int64_t>(b) * H + h) * n_max + n0) * DN;
+#pragma unroll
+    for (int e = 0; e < kGN * 16 / kGThreads; ++e) {
+        const int id = tid + kGThreads * e, row = id >> 4, piece = id & 15;
+        if (n0 + row < L)
+            *reinterpret_cast<u32x4 *>(dbase + static_cast<int64_t>(row) * DN + 8 * piece) =
+                *reinterpret_cast<const u32x4 *>(lds + row * kGOutRow + 16 * piece);
     }
 }
 
 // ---------------------------------------------------------------------------
 // 2. causal attention over the materialised K/V.
+//
+// Workgroup = 8 waves x 32 queries of one (sequence, head).  Key tiles of 64
+// rows: K_nope (64 x 256 B), k^R (64 x 128 B) and V (64 x 256 B), 40 KiB,
+// loaded direct-to-LDS (5 loads per wave) into three buffers, so two tiles
+// are in flight while one is consumed.  Loads past the sequence's length
+// read zeros (buffer range), and those keys are masked anyway.
+//
+// LDS swizzles (16-byte pieces p of a row; every access pattern below
+// touches distinct bank groups within 16 lanes):
+//   K_nope row r: piece p at p ^ (r & 15)        (score reads: 16 rows, one piece)
+//   k^R    row r: piece p at p ^ ((r >> 1) & 7)  (same, with 128-byte rows)
+//   V      row r: piece p at p ^ (4 (r & 3))     (transposing reads: 4 rows x 64 B)
+//
+// Score  S^T[key][query] = K . Q^T   (A = key rows, B = the wave's queries in VGPRs)
+// Accum  O^T[dim][query] += V^T . P^T (A = V read with ds_read_b64_tr_b16,
+//        B = softmax weights repacked from the score accumulators)
+// Softmax in log2 units, running maximum raised lazily: the accumulators
+// are rescaled only when a query's maximum grows by more than 2^8.
 // ---------------------------------------------------------------------------
-constexpr int kQB = 128;                   // queries per workgroup (4 waves x 32)
-constexpr int kKT = 32;                    // keys per tile
-constexpr int kKRow = DQK * 2 + 16;        // 400 B: K tile row (k_nope | k^R) + pad
-constexpr int kVRow = DV * 2 + 16;         // 272 B
-constexpr int kAttnThreads = 256;
-constexpr int kKChunks = DQK * 2 / 16;     // 24 per key row
-constexpr int kVChunks = DV * 2 / 16;      // 16 per value row
-constexpr int kChunksPerThreadA = kKT * (kKChunks + kVChunks) / kAttnThreads;  // 5
-static_assert(kKT * (kKChunks + kVChunks) % kAttnThreads == 0, "tile split");
+constexpr int kAW = 8;                                  // waves per workgroup
+constexpr int kAThreads = 64 * kAW;
+constexpr int kAQ = 32 * kAW;                           // 256 queries per workgroup
+constexpr int kAT = 64;                                 // keys per tile
+constexpr int kKnOff = 0;
+constexpr int kKrOff = kAT * DN * 2;                    // 16 KiB
+constexpr int kVOff = kKrOff + kAT * DR * 2;            // 24 KiB
+constexpr int kATile = kVOff + kAT * DV * 2;            // 40 KiB
+constexpr int kADmaPerWave = kATile / 1024 / kAW;       // 5
 constexpr float kRescaleThreshold = 8.0f;
+static_assert(kADmaPerWave * 1024 * kAW == kATile, "whole loads per wave");
+static_assert(kKrOff / 1024 == 2 * kAW && (kVOff - kKrOff) / 1024 == kAW &&
+              (kATile - kVOff) / 1024 == 2 * kAW, "load d = w + 8 e: e 0-1 K, 2 k^R, 3-4 V");
+static_assert(3 * kATile <= 160 * 1024, "LDS budget");
 
-__global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_bf16_kernel(
-    int T, int H, int64_t n_max, const uint16_t *__restrict__ q_nope,
+__global__ __launch_bounds__(kAThreads, 1) void prefill_attn_bf16_kernel(
+    int T, int H, int B, int nqb, int64_t n_max, const uint16_t *__restrict__ q_nope,
     const uint16_t *__restrict__ q_rope, const uint16_t *__restrict__ kpe, int64_t kpe_sb,
-    int64_t kpe_sn, const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ K,
+    int kpe_rowb, const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, float c2, void *__restrict__ out, int out_bf16)
 {
-    __shared__ __attribute__((aligned(16))) unsigned char ks_lds[2][kKT * kKRow];
-    __shared__ __attribute__((aligned(16))) unsigned char vs_lds[2][kKT * kVRow];
+    __shared__ __attribute__((aligned(1024))) unsigned char tiles[3 * kATile];
 
-    // heaviest (latest) query blocks first
-    const int qb = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    // Work item: (query block, sequence, head).  Workgroups are dispatched
+    // round-robin over the 8 XCDs; when the (sequence, head) pairs divide by
+    // 8, XCD x serves the pairs x, x + 8, ..., so each pair's keys and values
+    // are fetched into one XCD's L2.  Heaviest (latest) query blocks first.
+    const int npairs = B * H;
+    int qb, pair;
+    if ((npairs & 7) == 0) {
+        const int i = blockIdx.x, x = i & 7, j = i >> 3, ppx = npairs >> 3;
+        qb = nqb - 1 - j / ppx;
+        pair = x + 8 * (j % ppx);
+    } else {
+        qb = nqb - 1 - static_cast<int>(blockIdx.x) / npairs;
+        pair = static_cast<int>(blockIdx.x) % npairs;
+    }
+    const int b = pair / H, h = pair % H;
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int half = lane >> 5, l32 = lane & 31;
-    const int L = static_cast<int>(min<int64_t>(max(seqlens[b], 0), n_max));
-    const int off = L - T;  // position of query t is off + t
-    const int t = qb * kQB + wv * 32 + l32;
-    const int pos = off + t;  // keys n <= pos are visible
-    const int wave_last = off + qb * kQB + wv * 32 + 31;  // largest position in this wave
-    const int blk_last = min(L - 1, off + min(T - 1, qb * kQB + kQB - 1));
-    const int nkt = blk_last < 0 ? 0 : blk_last / kKT + 1;
+    const int L = clamp_len(seqlens[b], n_max);
+    const int off = L - T;                   // position of query t is off + t
+    const int q0 = qb * kAQ + 32 * w;        // this wave's first query
+    const int t = q0 + l32;
+    const int pos = t < T ? off + t : -1;    // keys n <= pos are visible
+    // smallest visible-key bound in the wave (-1 when it holds padding queries)
+    const int wave_min_pos = q0 + 31 < T ? off + q0 : -1;
+    const int wave_last = q0 < T ? min(L - 1, off + min(T - 1, q0 + 31)) : -1;
+    const int blk_last = min(L - 1, off + min(T - 1, qb * kAQ + kAQ - 1));
+    const int ntiles = blk_last < 0 ? 0 : blk_last / kAT + 1;
 
-    // query row of this lane's column as the B operand: k = 16 s + 8 half + 0..7
+    // The lane's query row as the score MFMA's B operand: k = 16 s + 8 half + 0..7.
     u32x4 qreg[DQK / 16];
     {
         const bool tv = t < T;
@@ -187,6 +264,59 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_bf16_kernel(
             qreg[s] = v;
         }
     }
+    // Let the query loads land here: no vector-memory wait inside the tile loop.
+    __builtin_amdgcn_s_waitcnt(0);
+
+    const i32x4 rs_k = make_rsrc(K + static_cast<int64_t>(pair) * n_max * DN,
+                                 static_cast<uint32_t>(L) * (DN * 2));
+    const i32x4 rs_v = make_rsrc(V + static_cast<int64_t>(pair) * n_max * DV,
+                                 static_cast<uint32_t>(L) * (DV * 2));
+    const i32x4 rs_r = make_rsrc(kpe + static_cast<int64_t>(b) * kpe_sb,
+                                 static_cast<uint32_t>(L) * static_cast<uint32_t>(kpe_rowb));
+
+    // This wave's 5 loads of a tile (load d = w + 8 e):
+    //   e = 0, 1: K_nope rows 4 i .. 4 i + 3 (i = d), lane -> row 4 i + lane / 16
+    //   e = 2:    k^R rows 8 w .. 8 w + 7,            lane -> row 8 w + lane / 8
+    //   e = 3, 4: V rows 4 i .. 4 i + 3 (i = d - 24)
+    // each lane fetching the source piece that its LDS piece holds.
+    unsigned voff[kADmaPerWave];
+    {
+        const int rk0 = 4 * w + (lane >> 4), rk1 = 4 * (w + 8) + (lane >> 4);
+        voff[0] = static_cast<unsigned>(rk0 * DN * 2 + 16 * ((lane & 15) ^ (rk0 & 15)));
+        voff[1] = static_cast<unsigned>(rk1 * DN * 2 + 16 * ((lane & 15) ^ (rk1 & 15)));
+        const int rr = 8 * w + (lane >> 3);
+        voff[2] = static_cast<unsigned>(rr * kpe_rowb + 16 * ((lane & 7) ^ ((rr >> 1) & 7)));
+        voff[3] = static_cast<unsigned>(rk0 * DV * 2 + 16 * ((lane & 15) ^ (4 * (rk0 & 3))));
+        voff[4] = static_cast<unsigned>(rk1 * DV * 2 + 16 * ((lane & 15) ^ (4 * (rk1 & 3))));
+    }
+    auto issue_tile = [&](int n0, unsigned char *dst) {
+        const unsigned kb = static_cast<unsigned>(n0) * (DN * 2);
+        const unsigned rb = static_cast<unsigned>(n0) * static_cast<unsigned>(kpe_rowb);
+        lds_dma16(rs_k, dst + kKnOff + 1024 * w, voff[0] + kb);
+        lds_dma16(rs_k, dst + kKnOff + 1024 * (w + 8), voff[1] + kb);
+        lds_dma16(rs_r, dst + kKrOff + 1024 * w, voff[2] + rb);
+        lds_dma16(rs_v, dst + kVOff + 1024 * w, voff[3] + kb);
+        lds_dma16(rs_v, dst + kVOff + 1024 * (w + 8), voff[4] + kb);
+    };
+
+    // Score A operand (key row 32 kb + l32, K elements 16 s + 8 half + 0..7):
+    // per-lane offsets for the 8 K_nope and 4 k^R steps; + kb * rows (immediate).
+    int sk[DQK / 16];
+#pragma unroll
+    for (int s = 0; s < DN / 16; ++s)
+        sk[s] = kKnOff + l32 * (DN * 2) + 16 * ((2 * s + half) ^ (l32 & 15));
+#pragma unroll
+    for (int s = DN / 16; s < DQK / 16; ++s)
+        sk[s] = kKrOff + l32 * (DR * 2) + 16 * ((2 * (s - DN / 16) + half) ^ ((l32 >> 1) & 7));
+    // P.V A operand via the transposing read: source lane 4 k + c of 16-lane
+    // group g addresses key 16 ks + 8 r + 4 (g >> 1) + k (r = 0, 1: the two
+    // reads of a K step), value dims 32 q + 16 (g & 1) + 4 c .. + 3; with the
+    // V swizzle that is byte 64 (q ^ k) + 32 (g & 1) + 8 c of the row.
+    const int g16 = lane >> 4, k4 = (lane >> 2) & 3, c4 = lane & 3;
+    int pv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        pv[q] = kVOff + (4 * (g16 >> 1) + k4) * (DV * 2) + 64 * (q ^ k4) + 32 * (g16 & 1) + 8 * c4;
 
     f32x16 oacc[4];
 #pragma unroll
@@ -195,78 +325,57 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_bf16_kernel(
         for (int r = 0; r < 16; ++r) oacc[q][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int64_t rowstride = static_cast<int64_t>(H) * DN;  // K and V rows: [b][n][h][128]
-    u32x4 stage[kChunksPerThreadA];
-    auto load_tile = [&](int k0) {
+    auto tile_step = [&](int it, const unsigned char *tb, unsigned char *next_dst) {
+        const int n0 = it * kAT;
+        if (it + 1 < ntiles)
+            wait_then_barrier<kADmaPerWave>();
+        else
+            wait_then_barrier<0>();
+        if (it + 2 < ntiles) issue_tile(n0 + 2 * kAT, next_dst);
+        if (n0 > wave_last) return;  // every key of the tile is in this wave's future
+
+        // ---- scores: two 32-key blocks, interleaved accumulation chains ----
+        f32x16 sacc[2];
 #pragma unroll
-        for (int e = 0; e < kChunksPerThreadA; ++e) {
-            const int c = tid + kAttnThreads * e;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (c < kKT * kKChunks) {
-                const int row = c / kKChunks, cc = c % kKChunks;
-                const int n = k0 + row;
-                if (n < L) {
-                    const uint16_t *src = cc < DN / 8
-                        ? K + (static_cast<int64_t>(b) * n_max + n) * rowstride + static_cast<int64_t>(h) * DN + 8 * cc
-                        : kpe + static_cast<int64_t>(b) * kpe_sb + static_cast<int64_t>(n) * kpe_sn + 8 * (cc - DN / 8);
-                    v = *reinterpret_cast<const u32x4 *>(src);
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        auto a_at = [&](int i) -> u32x4 {  // i = 2 s + kb
+            const int s = i >> 1, kb = i & 1;
+            const int rowb = s < DN / 16 ? DN * 2 : DR * 2;
+            return *reinterpret_cast<const u32x4 *>(tb + sk[s] + 32 * kb * rowb);
+        };
+        u32x4 abuf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) abuf[i] = a_at(i);
+#pragma unroll
+        for (int i = 0; i < 2 * (DQK / 16); ++i) {
+            sacc[i & 1] = mfma32(abuf[i & 3], qreg[i >> 1], sacc[i & 1]);
+            if (i + 4 < 2 * (DQK / 16)) abuf[i & 3] = a_at(i + 4);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // ---- online softmax (lane = query column; sacc[kb][r] is key
+        //      n0 + 32 kb + 8 (r / 4) + 4 half + r % 4) ----
+        if (n0 + kAT - 1 > wave_min_pos) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int n = n0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (n > pos) sacc[kb][r] = -INFINITY;
                 }
-            } else {
-                const int c2i = c - kKT * kKChunks;
-                const int row = c2i / kVChunks, cc = c2i % kVChunks;
-                const int n = k0 + row;
-                if (n < L)
-                    v = *reinterpret_cast<const u32x4 *>(
-                        V + (static_cast<int64_t>(b) * n_max + n) * rowstride + static_cast<int64_t>(h) * DV + 8 * cc);
-            }
-            stage[e] = v;
         }
-    };
-    auto store_tile = [&](int buf) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < kChunksPerThreadA; ++e) {
-            const int c = tid + kAttnThreads * e;
-            if (c < kKT * kKChunks) {
-                const int row = c / kKChunks, cc = c % kKChunks;
-                *reinterpret_cast<u32x4 *>(ks_lds[buf] + row * kKRow + 16 * cc) = stage[e];
-            } else {
-                const int c2i = c - kKT * kKChunks;
-                const int row = c2i / kVChunks, cc = c2i % kVChunks;
-                *reinterpret_cast<u32x4 *>(vs_lds[buf] + row * kVRow + 16 * cc) = stage[e];
-            }
-        }
-    };
-
-    if (nkt > 0) load_tile(0);
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1, k0 = kt * kKT;
-        store_tile(buf);
-        __syncthreads();
-        if (kt + 1 < nkt) load_tile(k0 + kKT);
-        if (k0 > wave_last) continue;  // every key of the tile is in this wave's future
-
-        f32x16 sacc;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-        const unsigned char *krow = ks_lds[buf] + l32 * kKRow + 16 * half;
-#pragma unroll
-        for (int s = 0; s < DQK / 16; ++s)
-            sacc = mfma32(*reinterpret_cast<const u32x4 *>(krow + 32 * s), qreg[s], sacc);
-
-        float sv[16];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int n = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
-            sv[r] = (n <= pos && t < T) ? sacc[r] * c2 : -INFINITY;
-            tmax = fmaxf(tmax, sv[r]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const bool need = tmax > m_run + kRescaleThreshold;
-        if (__ballot(need) != 0) {
-            const float m_new = fmaxf(m_run, tmax);
-            const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-            // a column with no visible key yet keeps m = -inf and weights 0
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mt = mx * c2;  // log2 units; -inf stays -inf
+        if (__ballot(mt > m_run + kRescaleThreshold) != 0) {
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
@@ -274,62 +383,70 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_bf16_kernel(
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[q][r] *= alpha;
         }
-        u32x4 pk[2];
+        // a query with no visible key yet keeps m = -inf: its scores are -inf, weights 0
+        const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+        u32x4 pk[4];
         float psum = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const float x0 = sv[8 * kk + 2 * p], x1 = sv[8 * kk + 2 * p + 1];
-                const float p0 = x0 == -INFINITY ? 0.f : exp2f(x0 - m_run);
-                const float p1 = x1 == -INFINITY ? 0.f : exp2f(x1 - m_run);
-                const uint32_t wpk = pack_bf16(p0, p1);
-                psum += bf16lo(wpk) + bf16hi(wpk);
-                pk[kk][p] = wpk;
+                const int kb = ks >> 1, r = 8 * (ks & 1) + 2 * p;
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], c2, neg_m));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r + 1], c2, neg_m));
+                psum += p0 + p1;
+                pk[ks][p] = pack_bf16(p0, p1);
             }
         l_run += psum;
 
-        const unsigned char *vt = vs_lds[buf];
+        // ---- O^T[dim][query] += V^T[dim][key] P^T[key][query] ----
+        // K step ks covers keys 16 ks + 8 (e / 4) + 4 half + e % 4 (e = 0..7),
+        // as the score accumulators hold them; block q = dims 32 q .. + 31.
+        auto a_tr = [&](int ks, int q) -> u32x4 {
+            const u32x2 lo = lds_read_tr4(tb + pv[q] + (16 * ks) * (DV * 2));
+            const u32x2 hi = lds_read_tr4(tb + pv[q] + (16 * ks + 8) * (DV * 2));
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        u32x4 av[4];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            u32x2 R[8];
+        for (int i = 0; i < 4; ++i) av[i] = a_tr(0, i);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int row = 16 * kk + 8 * (e >> 2) + 4 * half + (e & 3);
-                R[e] = *reinterpret_cast<const u32x2 *>(vt + row * kVRow + 8 * l32);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint32_t sel = (v & 1) ? 0x07060302u : 0x05040100u;
-                u32x4 a;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t x = (v < 2) ? R[2 * p][0] : R[2 * p][1];
-                    const uint32_t y = (v < 2) ? R[2 * p + 1][0] : R[2 * p + 1][1];
-                    a[p] = __builtin_amdgcn_perm(y, x, sel);
-                }
-                oacc[v] = mfma32(a, pk[kk], oacc[v]);
-            }
+        for (int i = 0; i < 16; ++i) {  // i = 4 ks + q
+            oacc[i & 3] = mfma32(av[i & 3], pk[i >> 2], oacc[i & 3]);
+            if (i + 4 < 16) av[i & 3] = a_tr((i + 4) >> 2, (i + 4) & 3);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+
+    if (ntiles > 0) issue_tile(0, tiles);
+    if (ntiles > 1) issue_tile(kAT, tiles + kATile);
+    int buf = 0;  // tile it lives in buffer it % 3
+    for (int it = 0; it < ntiles; ++it) {
+        const int nxt = buf == 0 ? 2 : buf - 1;  // (it + 2) % 3
+        tile_step(it, tiles + buf * kATile, tiles + nxt * kATile);
+        buf = buf == 2 ? 0 : buf + 1;
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (t >= T) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t orow = ((static_cast<int64_t>(b) * T + t) * H + h) * DV;
+    // oacc[q][r] is value dim 32 q + 8 (r / 4) + 4 half + r % 4 of query t.
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int i = 8 * (r >> 2) + 4 * half + (r & 3);  // value columns 4 i .. 4 i + 3
-        const float o0 = oacc[0][r] * inv, o1 = oacc[1][r] * inv;
-        const float o2 = oacc[2][r] * inv, o3 = oacc[3][r] * inv;
-        if (out_bf16) {
-            u32x2 v = {pack_bf16(o0, o1), pack_bf16(o2, o3)};
-            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(out) + orow + 4 * i) = v;
-        } else {
-            float *o = reinterpret_cast<float *>(out) + orow + 4 * i;
-            o[0] = o0; o[1] = o1; o[2] = o2; o[3] = o3;
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d = 32 * q + 8 * g + 4 * half;
+            const float o0 = oacc[q][4 * g] * inv, o1 = oacc[q][4 * g + 1] * inv;
+            const float o2 = oacc[q][4 * g + 2] * inv, o3 = oacc[q][4 * g + 3] * inv;
+            if (out_bf16) {
+                const u32x2 v = {pack_bf16(o0, o1), pack_bf16(o2, o3)};
+                *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(out) + orow + d) = v;
+            } else {
+                const f32x4 v = {o0, o1, o2, o3};
+                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + orow + d) = v;
+            }
         }
-    }
 }
 
 }  // namespace
@@ -339,24 +456,21 @@ hipError_t launch_prefill_bf16(const PrefillShape &s, const void *q_nope, const 
                                const void *kpe, const int32_t *seqlens, void *out, void *kbuf,
                                void *vbuf, hipStream_t st)
 {
-    const int n_feat = s.H * DN;
-    dim3 ggrid(n_feat / GT, static_cast<unsigned>((s.n_max + GT - 1) / GT), s.B);
-    decompress_gemm_bf16_kernel<<<ggrid, kGemmThreads, 0, st>>>(
-        s.n_max, n_feat, static_cast<const uint16_t *>(w_uk), static_cast<const uint16_t *>(ckv),
-        s.ckv_sb, s.ckv_sn, seqlens, static_cast<uint16_t *>(kbuf));
+    // K and V are [B][H][n_max][128] bf16 in the workspace.
+    dim3 ggrid(s.H, static_cast<unsigned>((s.n_max + kGN - 1) / kGN), 2 * s.B);
+    decompress_gemm_bf16_kernel<<<ggrid, kGThreads, 0, st>>>(
+        s.H, s.n_max, static_cast<const uint16_t *>(w_uk), static_cast<const uint16_t *>(w_uv),
+        static_cast<const uint16_t *>(ckv), s.ckv_sb, static_cast<int>(s.ckv_sn * 2), seqlens,
+        static_cast<uint16_t *>(kbuf), static_cast<uint16_t *>(vbuf));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    decompress_gemm_bf16_kernel<<<ggrid, kGemmThreads, 0, st>>>(
-        s.n_max, n_feat, static_cast<const uint16_t *>(w_uv), static_cast<const uint16_t *>(ckv),
-        s.ckv_sb, s.ckv_sn, seqlens, static_cast<uint16_t *>(vbuf));
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dim3 agrid((s.T + kQB - 1) / kQB, s.H, s.B);
-    prefill_attn_bf16_kernel<<<agrid, kAttnThreads, 0, st>>>(
-        s.T, s.H, s.n_max, static_cast<const uint16_t *>(q_nope), static_cast<const uint16_t *>(q_rope),
-        static_cast<const uint16_t *>(kpe), s.kpe_sb, s.kpe_sn, seqlens,
-        static_cast<const uint16_t *>(kbuf), static_cast<const uint16_t *>(vbuf), s.scale * kLog2e,
-        out, s.out_bf16);
+    const int nqb = (s.T + kAQ - 1) / kAQ;
+    const unsigned nblk = static_cast<unsigned>(nqb) * static_cast<unsigned>(s.B * s.H);
+    prefill_attn_bf16_kernel<<<nblk, kAThreads, 0, st>>>(
+        s.T, s.H, s.B, nqb, s.n_max, static_cast<const uint16_t *>(q_nope),
+        static_cast<const uint16_t *>(q_rope), static_cast<const uint16_t *>(kpe), s.kpe_sb,
+        static_cast<int>(s.kpe_sn * 2), seqlens, static_cast<const uint16_t *>(kbuf),
+        static_cast<const uint16_t *>(vbuf), s.scale * kLog2e, out, s.out_bf16);
     return hipGetLastError();
 }
 
