@@ -108,12 +108,12 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, const ui
 // LDS tile layout: latent row r (one 1-KiB load each, so its placement is
 // free) sits at r * 1280 + 16 * f(r), f(r) = 4 (r & 3) + ((r >> 2) & 3) < 16:
 // 1280-byte slots keep the staggered rows from overlapping and leave the bank
-// phase to f alone.  The stagger keeps both access patterns nearly free of
-// bank conflicts: the score MFMA's lanes read 16 consecutive rows at one
-// column (f distinct over any 16 consecutive rows), and each 16-lane group of
-// a transposing read takes 32 bytes from 4 consecutive rows r = 4m..4m+3
+// phase to f alone.  The stagger keeps both access patterns free of bank
+// conflicts: the score MFMA's lanes read 16 consecutive rows at one column
+// (f distinct over any 16 consecutive rows), and each 16-lane group of a
+// transposing read takes 32 bytes from 4 consecutive rows r = 4m..4m+3
 // (f = 4k + const, so their windows start 64 bytes apart).  Then come 32
-// RoPE-key rows of 128 bytes, 16-byte chunks XOR-swizzled by (row & 7).
+// RoPE-key rows of 128 bytes, 16-byte chunks XOR-swizzled by (row >> 1) & 7.
 // Every read address is a per-lane base plus an immediate.
 //
 // Score  S^T[token][head] = C . Qa^T  (A = cache rows, B = absorbed query)
@@ -165,6 +165,12 @@ static_assert(kTrHiStagger == lat_slot(9) - lat_slot(1) - 8 * kLatSlot &&
               kTrHiStagger == lat_slot(31) - lat_slot(23) - 8 * kLatSlot,
               "uniform stagger delta between the two halves of a K step");
 constexpr float kRefSlack = 64.0f;              // log2 headroom above the reference maximum
+// LDS operand reads kept in flight ahead of the MFMA that consumes them: with
+// one wave per SIMD, this depth is what covers the LDS latency.
+#ifndef MLA_DECODE_LOOKAHEAD
+#define MLA_DECODE_LOOKAHEAD 8
+#endif
+constexpr int kLook = MLA_DECODE_LOOKAHEAD;
 
 __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     int H, int S, int64_t n_max, const uint16_t *__restrict__ ckv, int64_t ckv_sb, int ckv_rowb,
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     // chunk (lane % 8) ^ (row & 7)).
     const unsigned lat_src = static_cast<unsigned>(8 * w * ckv_rowb + 16 * lane);
     const int rr = 8 * w + (lane >> 3);
-    const unsigned rope_src = static_cast<unsigned>(rr * kpe_rowb + 16 * ((lane & 7) ^ (rr & 7)));
+    const unsigned rope_src = static_cast<unsigned>(rr * kpe_rowb + 16 * ((lane & 7) ^ ((rr >> 1) & 7)));
     auto issue_tile = [&](int n0, unsigned char *dst) {
         const unsigned lat_base = static_cast<unsigned>(n0) * static_cast<unsigned>(ckv_rowb);
 #pragma unroll
@@ -272,20 +278,20 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
         const unsigned char *sr = tb + kRopeBase + l32 * kRopeRow;
         auto a_at = [&](int s) -> u32x4 {
             if (s < DC / 16) return *reinterpret_cast<const u32x4 *>(sa + 32 * s);
-            return *reinterpret_cast<const u32x4 *>(sr + 16 * ((2 * (s - DC / 16) + half) ^ (l32 & 7)));
+            return *reinterpret_cast<const u32x4 *>(sr + 16 * ((2 * (s - DC / 16) + half) ^ ((l32 >> 1) & 7)));
         };
         f32x16 sacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-        u32x4 abuf[4];
+        u32x4 abuf[kLook];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) abuf[s] = a_at(s);
+        for (int s = 0; s < kLook; ++s) abuf[s] = a_at(s);
 #pragma unroll
         for (int s = 0; s < DQK / 16; ++s) {
             const u32x4 bq = s < DC / 16 ? qreg[s]
                                          : *reinterpret_cast<const u32x4 *>(qr + 32 * (s - DC / 16));
-            sacc = mfma32(abuf[s & 3], bq, sacc);
-            if (s + 4 < DQK / 16) abuf[s & 3] = a_at(s + 4);
+            sacc = mfma32(abuf[s % kLook], bq, sacc);
+            if (s + kLook < DQK / 16) abuf[s % kLook] = a_at(s + kLook);
             __builtin_amdgcn_sched_barrier(0);
         }
         // sacc[r] is token 8 (r/4) + 4 half + r%4 of the tile, head l32.
@@ -331,14 +337,14 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
             const u32x2 hi = lds_read_tr4(pv + (16 * ks + 8) * kLatSlot + kTrHiStagger + 64 * q);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
         };
-        u32x4 av[4];
+        u32x4 av[kLook];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) av[i] = a_tr(0, i);
+        for (int i = 0; i < kLook; ++i) av[i] = a_tr(0, i);
 #pragma unroll
         for (int i = 0; i < 32; ++i) {  // i = 16 ks + q
             const int ks = i >> 4, q = i & 15;
-            oacc[q] = mfma32(av[i & 3], pk[ks], oacc[q]);
-            if (i + 4 < 32) av[i & 3] = a_tr((i + 4) >> 4, (i + 4) & 15);
+            oacc[q] = mfma32(av[i % kLook], pk[ks], oacc[q]);
+            if (i + kLook < 32) av[i % kLook] = a_tr((i + kLook) >> 4, (i + kLook) & 15);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -372,14 +378,16 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 3. merge + up-project: grid (H, ceil(B/4)), 256 threads.
-//    For each sequence: M = max_s m_s, w_s = 2^(m_s - M),
-//    o_lat = sum_s w_s O_s / sum_s w_s l_s in ascending s, then
-//    out = W_UV[h] o_lat.  A split marked with a NaN maximum (its weights
-//    could have overflowed) is first recomputed here for this head with the
-//    split's true maximum, in plain fp32.
+// 3. merge + up-project: grid (H, B), 256 threads, one (head, sequence) each.
+//    M = max_s m_s, w_s = 2^(m_s - M), o_lat = sum_s w_s O_s / sum_s w_s l_s,
+//    every sum in a fixed order (bitwise repeatable), then out = W_UV[h] o_lat.
+//    A split marked with a NaN maximum (its weights could have overflowed) is
+//    first recomputed here for this head with the split's true maximum, in
+//    plain fp32.  The workgroups of one head differ in blockIdx by multiples
+//    of H, so with H a multiple of 8 they share an XCD and its L2 copy of
+//    W_UV[h].
 // ---------------------------------------------------------------------------
-constexpr int kMergeBatch = 4;
+constexpr int kMergeLoads = 8;  // partial pieces per thread in flight
 
 struct CacheView {
     int64_t n_max;
@@ -459,116 +467,130 @@ __device__ void recompute_partial(const CacheView &cv, int H, int S, int b, int 
     __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int B, int H, int S,
+__global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
                                                                 float *__restrict__ part_o,
                                                                 float *__restrict__ part_ml,
                                                                 const uint16_t *__restrict__ w_uv,
                                                                 void *__restrict__ out, int out_bf16,
                                                                 CacheView cv)
 {
-    const int h = blockIdx.x, b0 = blockIdx.y * kMergeBatch, tid = threadIdx.x;
-    const int nb = min(kMergeBatch, B - b0);
-    __shared__ float wt[kMergeBatch][kMaxSplits];  // split weights 2^(m_s - M), 0 for empty
-    __shared__ float ls[kMaxSplits];               // split softmax mass
-    __shared__ float inv_l[kMergeBatch];
-    __shared__ float wmax[4];
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wv_id = tid >> 6;
+    __shared__ float wt[kMaxSplits];      // split weights 2^(m_s - M), 0 for empty splits
+    __shared__ float red[4];
     __shared__ int any_nan;
-    __shared__ __attribute__((aligned(16))) float ol[kMergeBatch][DC];
+    __shared__ __attribute__((aligned(16))) f32x4 half_sum[2][DC / 4];
+    __shared__ __attribute__((aligned(16))) float ol[DC];
 
-    for (int bb = 0; bb < nb; ++bb) {
-        const int b = b0 + bb;
-        const int64_t base = static_cast<int64_t>(b) * S * H + h;  // row of split 0
-        // marked (NaN) splits are recomputed first, in ascending order
-        if (tid == 0) any_nan = 0;
-        __syncthreads();
-        float ms = -INFINITY;
+    // Every load is issued up front, in the order the data is needed, so the
+    // whole merge costs one memory round trip: (m, l) of split tid, then this
+    // thread's first 16 partial pieces, then its W_UV pieces.
+    const int64_t base = static_cast<int64_t>(b) * S * H + h;  // row of split 0
+    // Loads are unconditional (indices past the last split are clamped) so
+    // that no branch makes the compiler wait on them early; the surplus values
+    // are discarded by selects.
+    const float2 ml = *reinterpret_cast<const float2 *>(
+        part_ml + (base + static_cast<int64_t>(min(tid, S - 1)) * H) * 2);
+    float ms = tid < S ? ml.x : -INFINITY;
+    float ls = tid < S ? ml.y : 0.f;
+    // partials: thread -> 4 columns (4 (tid % 128)), splits of parity tid / 128,
+    // kMergeLoads splits per batch
+    const int c4 = tid & (DC / 4 - 1), par = tid >> 7;
+    const float *po = part_o + base * DC + 4 * c4;
+    f32x4 pv[kMergeLoads];
+    auto load_batch = [&](int sp0) {
+#pragma unroll
+        for (int k = 0; k < kMergeLoads; ++k) {
+            const int sp = min(sp0 + 2 * k, S - 1);
+            pv[k] = *reinterpret_cast<const f32x4 *>(po + static_cast<int64_t>(sp) * H * DC);
+        }
+    };
+    load_batch(par);
+    // W_UV[h]: wave w takes rows 32 w .. 32 w + 31 in 4 groups of 8; lane
+    // (row 32 w + 8 j + l / 8, 16-byte piece l % 8 + 8 c) -- 8 rows x 128
+    // contiguous bytes per load instruction.
+    const int r8 = lane >> 3, p8 = lane & 7;
+    const u32x4 *wbase = reinterpret_cast<const u32x4 *>(w_uv + (static_cast<int64_t>(h) * DV + 32 * wv_id + r8) * DC) + p8;
+    u32x4 wq[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) wq[j][c] = wbase[j * 8 * (DC / 8) + 8 * c];
+
+    // Marked (NaN) splits are recomputed first, in ascending order, and the
+    // partials reloaded.
+    if (tid == 0) any_nan = 0;
+    __syncthreads();
+    if (__builtin_isnan(ms)) any_nan = 1;
+    __syncthreads();
+    if (any_nan) {
+        for (int sp = 0; sp < S; ++sp)
+            if (__builtin_isnan(part_ml[(base + static_cast<int64_t>(sp) * H) * 2]))
+                recompute_partial(cv, H, S, b, sp, h, part_o, part_ml);
         if (tid < S) {
             ms = part_ml[(base + static_cast<int64_t>(tid) * H) * 2];
-            if (__builtin_isnan(ms)) any_nan = 1;
+            ls = part_ml[(base + static_cast<int64_t>(tid) * H) * 2 + 1];
         }
-        __syncthreads();
-        if (any_nan) {
-            for (int sp = 0; sp < S; ++sp)
-                if (__builtin_isnan(part_ml[(base + static_cast<int64_t>(sp) * H) * 2]))
-                    recompute_partial(cv, H, S, b, sp, h, part_o, part_ml);
-            if (tid < S) ms = part_ml[(base + static_cast<int64_t>(tid) * H) * 2];
-        }
-        // M = max_s m_s (wave tree, then the four wave results in order)
-        float mx = ms;
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        if ((tid & 63) == 0) wmax[tid >> 6] = mx;
-        __syncthreads();
-        mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-        if (tid < S) {
-            wt[bb][tid] = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
-            ls[tid] = part_ml[(base + static_cast<int64_t>(tid) * H) * 2 + 1];
-        }
-        __syncthreads();
-        if (tid == 0) {
-            float l = 0.f;  // ascending split order
-            for (int sp = 0; sp < S; ++sp)
-                if (wt[bb][sp] != 0.f) l = fmaf(wt[bb][sp], ls[sp], l);
-            inv_l[bb] = l > 0.f ? 1.f / l : 0.f;
-        }
-        // o_lat columns 2 tid, 2 tid + 1: splits in groups of 8 loads in flight;
-        // empty splits (weight 0, O never written) are selected away, not multiplied.
-        float a0 = 0.f, a1 = 0.f;
-        const float *po = part_o + base * DC + 2 * tid;
-        for (int sp0 = 0; sp0 < S; sp0 += 8) {
-            float2 v[8];
+        load_batch(par);
+    }
+    const float mx = block_reduce(ms, red, true);           // M = max_s m_s
+    const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
+    if (tid < S) wt[tid] = w;
+    const float l = block_reduce(w != 0.f ? w * ls : 0.f, red, false);  // its barriers publish wt[]
+    const float inv_l = l > 0.f ? 1.f / l : 0.f;
+
+    // Weighted sum; empty splits (weight 0, O never written) are selected
+    // away, not multiplied.
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = par;;) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (sp0 + k < S) v[k] = *reinterpret_cast<const float2 *>(po + static_cast<int64_t>(sp0 + k) * H * DC);
+        for (int k = 0; k < kMergeLoads; ++k) {
+            const int sp = sp0 + 2 * k;
+            const float wk = sp < S ? wt[sp] : 0.f;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                if (sp0 + k < S) {
-                    const float wk = wt[bb][sp0 + k];
-                    a0 = fmaf(wk, wk != 0.f ? v[k].x : 0.f, a0);
-                    a1 = fmaf(wk, wk != 0.f ? v[k].y : 0.f, a1);
-                }
-            }
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(wk, wk != 0.f ? pv[k][e] : 0.f, acc[e]);
         }
-        __syncthreads();
-        ol[bb][2 * tid] = a0 * inv_l[bb];
-        ol[bb][2 * tid + 1] = a1 * inv_l[bb];
+        sp0 += 2 * kMergeLoads;
+        if (sp0 >= S) break;
+        load_batch(sp0);
+    }
+    half_sum[par][c4] = acc;
+    __syncthreads();
+    if (tid < DC / 4) {
+        const f32x4 o = (half_sum[0][tid] + half_sum[1][tid]) * inv_l;
+        *reinterpret_cast<f32x4 *>(ol + 4 * tid) = o;
     }
     __syncthreads();
 
-    // out[b][h][v] = W_UV[h][v] . o_lat[b]: wave w takes rows 32 w .. 32 w + 31;
-    // lane (row 32 w + l % 32, column half l / 32) sums 256 columns, 32 loads
-    // of 16 bytes in flight, then the two halves are added.
-    const int lane = tid & 63, v = 32 * (tid >> 6) + (lane & 31), hc = lane >> 5;
-    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(w_uv + (static_cast<int64_t>(h) * DV + v) * DC + 256 * hc);
-    u32x4 wv[32];
+    // out[b][h][v] = W_UV[h][v] . o_lat: each row's 8 lanes add their 64
+    // columns, then a 3-step butterfly over the 8 lanes.
 #pragma unroll
-    for (int c = 0; c < 32; ++c) wv[c] = wrow[c];
-    float acc[kMergeBatch] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) {
+        float a = 0.f;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
-        float wf[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            wf[2 * e] = bf16lo(wv[c][e]);
-            wf[2 * e + 1] = bf16hi(wv[c][e]);
+        for (int c = 0; c < 8; ++c) {
+            const float *o = ol + 8 * (p8 + 8 * c);
+            const f32x4 o0 = *reinterpret_cast<const f32x4 *>(o);
+            const f32x4 o1 = *reinterpret_cast<const f32x4 *>(o + 4);
+            a = fmaf(bf16lo(wq[j][c][0]), o0[0], a);
+            a = fmaf(bf16hi(wq[j][c][0]), o0[1], a);
+            a = fmaf(bf16lo(wq[j][c][1]), o0[2], a);
+            a = fmaf(bf16hi(wq[j][c][1]), o0[3], a);
+            a = fmaf(bf16lo(wq[j][c][2]), o1[0], a);
+            a = fmaf(bf16hi(wq[j][c][2]), o1[1], a);
+            a = fmaf(bf16lo(wq[j][c][3]), o1[2], a);
+            a = fmaf(bf16hi(wq[j][c][3]), o1[3], a);
         }
-#pragma unroll
-        for (int bb = 0; bb < kMergeBatch; ++bb) {
-            const float *o = &ol[bb][256 * hc + 8 * c];
-            float sacc = acc[bb];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sacc = fmaf(wf[e], o[e], sacc);
-            acc[bb] = sacc;
-        }
-    }
-#pragma unroll
-    for (int bb = 0; bb < kMergeBatch; ++bb) acc[bb] += __shfl_xor(acc[bb], 32);
-    if (hc == 0) {
-        for (int bb = 0; bb < nb; ++bb) {
-            const int64_t oi = (static_cast<int64_t>(b0 + bb) * H + h) * DV + v;
+        a += __shfl_xor(a, 1);
+        a += __shfl_xor(a, 2);
+        a += __shfl_xor(a, 4);
+        if (p8 == 0) {
+            const int v = 32 * wv_id + 8 * j + r8;
+            const int64_t oi = (static_cast<int64_t>(b) * H + h) * DV + v;
             if (out_bf16)
-                reinterpret_cast<__bf16 *>(out)[oi] = static_cast<__bf16>(acc[bb]);
+                reinterpret_cast<__bf16 *>(out)[oi] = static_cast<__bf16>(a);
             else
-                reinterpret_cast<float *>(out)[oi] = acc[bb];
+                reinterpret_cast<float *>(out)[oi] = a;
         }
     }
 }
@@ -603,11 +625,11 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
         if (e != hipSuccess) return e;
     }
     if (events) (void)hipEventRecord(events[2], st);
-    dim3 grid(s.H, (s.B + kMergeBatch - 1) / kMergeBatch);
+    dim3 grid(s.H, s.B);
     CacheView cv{s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb, s.ckv_sn,
                  static_cast<const uint16_t *>(kpe), s.kpe_sb, s.kpe_sn, seqlens, qa,
                  s.scale * kLog2e};
-    merge_upproj_bf16_kernel<<<grid, 256, 0, st>>>(s.B, s.H, s.S, ws.part_o, ws.part_ml,
+    merge_upproj_bf16_kernel<<<grid, 256, 0, st>>>(s.H, s.S, ws.part_o, ws.part_ml,
                                                    static_cast<const uint16_t *>(w_uv), out, s.out_bf16,
                                                    cv);
     hipError_t e = hipGetLastError();
