@@ -165,31 +165,12 @@ static_assert(kTrHiStagger == lat_slot(9) - lat_slot(1) - 8 * kLatSlot &&
               kTrHiStagger == lat_slot(31) - lat_slot(23) - 8 * kLatSlot,
               "uniform stagger delta between the two halves of a K step");
 constexpr float kRefSlack = 64.0f;              // log2 headroom above the reference maximum
-
-// Score accumulation pinned to VGPRs (the 256 AGPRs hold the wave's output
-// accumulators): v_mfma_f32_32x32x16_bf16 issued as inline assembly.
-// Back-to-back accumulation into the same registers is interlocked by the
-// hardware; a VALU read of the result needs wait states, which the last
-// link of a chain carries itself.
-__device__ __forceinline__ void mfma_v_init(f32x16 &c, u32x4 a, u32x4 b)
-{
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v_acc(f32x16 &c, u32x4 a, u32x4 b)
-{
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_v_last(f32x16 &c, u32x4 a, u32x4 b)
-{
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 3"
-                 : "+v"(c) : "v"(a), "v"(b));
-}
-
-// One tile step of the software pipeline issues 68 MFMAs: the 36 score steps
-// of the next tile (two accumulation chains, even and odd K steps) and the
-// 32 P.C MFMAs of the current tile, in groups [S, S, S, S, PV] x 9 followed
-// by the remaining 23 P.C MFMAs, under which the next tile's softmax runs.
-constexpr int kRing = 4;                        // operand reads in flight ahead of their MFMA
+// LDS operand reads kept in flight ahead of the MFMA that consumes them: with
+// one wave per SIMD, this depth is what covers the LDS latency.
+#ifndef MLA_DECODE_LOOKAHEAD
+#define MLA_DECODE_LOOKAHEAD 8
+#endif
+constexpr int kLook = MLA_DECODE_LOOKAHEAD;
 
 __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     int H, int S, int64_t n_max, const uint16_t *__restrict__ ckv, int64_t ckv_sb, int ckv_rowb,
@@ -248,7 +229,7 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     // This wave's nine loads of the tile starting at token n0: latent rows
     // 8 w .. 8 w + 7 (one 1-KiB load each), and RoPE rows 8 w .. 8 w + 7 in
     // one load (lane -> row 8 w + lane / 8, LDS chunk lane % 8 holding source
-    // chunk (lane % 8) ^ ((row >> 1) & 7)).
+    // chunk (lane % 8) ^ (row & 7)).
     const unsigned lat_src = static_cast<unsigned>(8 * w * ckv_rowb + 16 * lane);
     const int rr = 8 * w + (lane >> 3);
     const unsigned rope_src = static_cast<unsigned>(rr * kpe_rowb + 16 * ((lane & 7) ^ ((rr >> 1) & 7)));
@@ -280,159 +261,102 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
         for (int r = 0; r < 16; ++r) oacc[q][r] = 0.f;
     float m_ref = -INFINITY;  // per head (lane column): the first tile's maximum
     float l_run = 0.f;
-    float s_hi = -INFINITY;   // per lane: the largest score of the split (log2 units)
+    bool over = false;        // a later score exceeded m_ref + 64 for this head
 
-    // Operands.  Score step s of tile tb: A = cache row l32, K elements
-    // 16 s + 8 half + 0..7; B = the absorbed query (registers, or the RoPE
-    // part in LDS).  P.C MFMA i = 16 ks + q of tile tb: A via two transposing
-    // reads (tokens 16 ks + 8 r + 4 half + 0..3, latent columns 32 q + l32).
-    auto s_opnd = [&](const unsigned char *tb, int st) -> u32x4 {
-        if (st < DC / 16) return *reinterpret_cast<const u32x4 *>(tb + s_lat + 32 * st);
-        return *reinterpret_cast<const u32x4 *>(tb + kRopeBase + l32 * kRopeRow +
-                                                16 * ((2 * (st - DC / 16) + half) ^ ((l32 >> 1) & 7)));
-    };
-    auto qr_opnd = [&](int st) -> u32x4 {
-        return *reinterpret_cast<const u32x4 *>(qr + 32 * (st - DC / 16));
-    };
-    auto pv_opnd = [&](const unsigned char *tb, int i) -> u32x4 {
-        const int ks = i >> 4, q = i & 15;
-        const unsigned char *pv = tb + pv_base;
-        const u32x2 lo = lds_read_tr4(pv + (16 * ks) * kLatSlot + 64 * q);
-        const u32x2 hi = lds_read_tr4(pv + (16 * ks + 8) * kLatSlot + kTrHiStagger + 64 * q);
-        return u32x4{lo[0], lo[1], hi[0], hi[1]};
-    };
-    // Score MFMA of step st into the even (sa) or odd (sb) chain.
-    auto score_mfma = [&](f32x16 &sa, f32x16 &sb, int st, u32x4 a, u32x4 bq) {
-        if (st == 0) mfma_v_init(sa, a, bq);
-        else if (st == 1) mfma_v_init(sb, a, bq);
-        else if (st == DQK / 16 - 2) mfma_v_last(sa, a, bq);
-        else if (st == DQK / 16 - 1) mfma_v_last(sb, a, bq);
-        else if (st & 1) mfma_v_acc(sb, a, bq);
-        else mfma_v_acc(sa, a, bq);
-    };
-    // Softmax weights of value pair pr (accumulator elements 2 pr, 2 pr + 1 =
-    // tokens n0 + 8 (pr / 2) + 4 half + 2 (pr % 2) + 0..1) of a tile's scores.
-    auto weights = [&](const f32x16 &sc, int n0, bool partial, int pr, float &psum) -> uint32_t {
-        float x0 = sc[2 * pr] * c2, x1 = sc[2 * pr + 1] * c2;
-        if (partial) {
-            const int tok = n0 + 8 * (pr >> 1) + 4 * half + 2 * (pr & 1);
-            x0 = tok < end ? x0 : -INFINITY;
-            x1 = tok + 1 < end ? x1 : -INFINITY;
+    // One tile: wait for it, hand the next-but-one tile's loads to the
+    // hardware, then scores, softmax weights and the latent accumulation.
+    auto tile_step = [&](int t, const unsigned char *tb, unsigned char *next_dst) {
+        const int n0 = start + t * kTile;
+        if (t + 1 < ntiles)
+            wait_then_barrier<kLoadsPerWave>();
+        else
+            wait_then_barrier<0>();
+        if (t + 2 < ntiles) issue_tile(n0 + 2 * kTile, next_dst);
+
+        // ---- scores: S^T[token i][head j] = sum_k C[i][k] Qa[j][k] ----
+        const unsigned char *sa = tb + s_lat;
+        const unsigned char *sr = tb + kRopeBase + l32 * kRopeRow;
+        auto a_at = [&](int s) -> u32x4 {
+            if (s < DC / 16) return *reinterpret_cast<const u32x4 *>(sa + 32 * s);
+            return *reinterpret_cast<const u32x4 *>(sr + 16 * ((2 * (s - DC / 16) + half) ^ ((l32 >> 1) & 7)));
+        };
+        f32x16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        u32x4 abuf[kLook];
+#pragma unroll
+        for (int s = 0; s < kLook; ++s) abuf[s] = a_at(s);
+#pragma unroll
+        for (int s = 0; s < DQK / 16; ++s) {
+            const u32x4 bq = s < DC / 16 ? qreg[s]
+                                         : *reinterpret_cast<const u32x4 *>(qr + 32 * (s - DC / 16));
+            sacc = mfma32(abuf[s % kLook], bq, sacc);
+            if (s + kLook < DQK / 16) abuf[s % kLook] = a_at(s + kLook);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        s_hi = fmaxf(s_hi, fmaxf(x0, x1));
-        const float p0 = __builtin_amdgcn_exp2f(x0 - m_ref);
-        const float p1 = __builtin_amdgcn_exp2f(x1 - m_ref);
-        psum += p0 + p1;
-        return pack_bf16(p0, p1);
-    };
-    auto is_partial = [&](int t) { return start + (t + 1) * kTile > end; };
+        // sacc[r] is token 8 (r/4) + 4 half + r%4 of the tile, head l32.
+        float tmax = -INFINITY;
+        if (n0 + kTile <= end) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sacc[r] *= c2;
+                tmax = fmaxf(tmax, sacc[r]);
+            }
+        } else {  // the split's last, partial tile
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int tok = n0 + 8 * (r >> 2) + 4 * half + (r & 3);
+                sacc[r] = tok < end ? sacc[r] * c2 : -INFINITY;
+                tmax = fmaxf(tmax, sacc[r]);
+            }
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        if (t == 0) m_ref = tmax;
+        over |= tmax > m_ref + kRefSlack;
 
-    // ---- prologue: tile 0's scores, reference maximum and weights ----
+        u32x4 pk[2];
+        float psum = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float p0 = __builtin_amdgcn_exp2f(sacc[8 * ks + 2 * p] - m_ref);
+                const float p1 = __builtin_amdgcn_exp2f(sacc[8 * ks + 2 * p + 1] - m_ref);
+                psum += p0 + p1;
+                pk[ks][p] = pack_bf16(p0, p1);
+            }
+        l_run += psum;
+
+        // ---- O^T[col][head] += C^T[col][token] P^T[token][head] ----
+        // K step ks covers tokens 16 ks + 8 (e / 4) + 4 half + e % 4 (e = 0..7
+        // across the two transposing reads), where the score accumulator left
+        // them; j-block q holds latent columns 32 q .. 32 q + 31.
+        const unsigned char *pv = tb + pv_base;
+        auto a_tr = [&](int ks, int q) -> u32x4 {
+            const u32x2 lo = lds_read_tr4(pv + (16 * ks) * kLatSlot + 64 * q);
+            const u32x2 hi = lds_read_tr4(pv + (16 * ks + 8) * kLatSlot + kTrHiStagger + 64 * q);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        u32x4 av[kLook];
+#pragma unroll
+        for (int i = 0; i < kLook; ++i) av[i] = a_tr(0, i);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {  // i = 16 ks + q
+            const int ks = i >> 4, q = i & 15;
+            oacc[q] = mfma32(av[i % kLook], pk[ks], oacc[q]);
+            if (i + kLook < 32) av[i % kLook] = a_tr((i + kLook) >> 4, (i + kLook) & 15);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     issue_tile(start, tiles);
     if (ntiles > 1) issue_tile(start + kTile, tiles + kTileBytes);
-    if (ntiles > 1)
-        wait_then_barrier<kLoadsPerWave>();
-    else
-        wait_then_barrier<0>();
-    u32x4 pk[2];  // weights of the tile whose P.C is next, as the P^T operand
-    {
-        f32x16 sa, sb;
-        u32x4 ring[kRing];
-#pragma unroll
-        for (int i = 0; i < kRing; ++i) ring[i] = s_opnd(tiles, i);
-#pragma unroll
-        for (int st = 0; st < DQK / 16; ++st) {
-            const u32x4 bq = st < DC / 16 ? qreg[st] : qr_opnd(st);
-            score_mfma(sa, sb, st, ring[st % kRing], bq);
-            if (st + kRing < DQK / 16) ring[st % kRing] = s_opnd(tiles, st + kRing);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const f32x16 sc = sa + sb;
-        const bool partial = is_partial(0);
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int tok = start + 8 * (r >> 2) + 4 * half + (r & 3);
-            tmax = fmaxf(tmax, (!partial || tok < end) ? sc[r] * c2 : -INFINITY);
-        }
-        m_ref = fmaxf(tmax, __shfl_xor(tmax, 32));
-        float psum = 0.f;
-#pragma unroll
-        for (int pr = 0; pr < 8; ++pr) pk[pr >> 2][pr & 3] = weights(sc, start, partial, pr, psum);
-        l_run += psum;
-    }
-
-    // ---- steady state: tile t's P.C interleaved with tile t + 1's scores ----
     int buf = 0;  // tile t lives in buffer t % 3
-    for (int t = 0; t + 1 < ntiles; ++t) {
-        const int nb = buf == 2 ? 0 : buf + 1;    // (t + 1) % 3
-        const int fb = nb == 2 ? 0 : nb + 1;      // (t + 2) % 3: tile t - 1's, free
-        const unsigned char *tb = tiles + buf * kTileBytes;
-        const unsigned char *tn = tiles + nb * kTileBytes;
-        wait_then_barrier<0>();                   // tile t + 1 has landed everywhere
-        if (t + 2 < ntiles) issue_tile(start + (t + 2) * kTile, tiles + fb * kTileBytes);
-        const int n1 = start + (t + 1) * kTile;
-        const bool partial = is_partial(t + 1);
-
-        f32x16 sa, sb, sc;
-        u32x4 sop[4], pvop, qb[DR / 16], pvr[kRing];
-        u32x4 pkn[2];
-        float psum = 0.f;
-        // phase A: groups g = 0..8 of [S(4g) .. S(4g + 3), PV(g)]; the operands
-        // of group g + 1 are read while group g's MFMAs run.
-#pragma unroll
-        for (int p4 = 0; p4 < 4; ++p4) sop[p4] = s_opnd(tn, p4);
-        pvop = pv_opnd(tb, 0);
-#pragma unroll
-        for (int g = 0; g < 9; ++g) {
-#pragma unroll
-            for (int p4 = 0; p4 < 4; ++p4) {
-                const int st = 4 * g + p4;
-                const u32x4 bq = st < DC / 16 ? qreg[st] : qb[st - DC / 16];
-                score_mfma(sa, sb, st, sop[p4], bq);
-                if (g + 1 < 9) {
-                    const int sn = st + 4;
-                    sop[p4] = s_opnd(tn, sn);
-                    if (sn >= DC / 16) qb[sn - DC / 16] = qr_opnd(sn);
-                } else {
-                    pvr[p4] = pv_opnd(tb, 9 + p4);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            oacc[g] = mfma32(pvop, pk[0], oacc[g]);
-            if (g + 1 < 9) pvop = pv_opnd(tb, g + 1);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // phase B: PV(9) .. PV(31), with the next tile's softmax under them
-#pragma unroll
-        for (int j = 9; j < 32; ++j) {
-            oacc[j & 15] = mfma32(pvr[(j - 9) % kRing], pk[j >> 4], oacc[j & 15]);
-            if (j + kRing < 32) pvr[(j - 9) % kRing] = pv_opnd(tb, j + kRing);
-            if (j == 10) sc = sa + sb;
-            if (j >= 11 && j < 19) pkn[(j - 11) >> 2][(j - 11) & 3] = weights(sc, n1, partial, j - 11, psum);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        l_run += psum;
-        pk[0] = pkn[0];
-        pk[1] = pkn[1];
-        buf = nb;
+    for (int t = 0; t < ntiles; ++t) {
+        const int nxt = buf == 0 ? 2 : buf - 1;  // (t + 2) % 3
+        tile_step(t, tiles + buf * kTileBytes, tiles + nxt * kTileBytes);
+        buf = buf == 2 ? 0 : buf + 1;
     }
-
-    // ---- epilogue: the last tile's P.C ----
-    {
-        const unsigned char *tb = tiles + buf * kTileBytes;
-        u32x4 ring[kRing];
-#pragma unroll
-        for (int i = 0; i < kRing; ++i) ring[i] = pv_opnd(tb, i);
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            oacc[i & 15] = mfma32(ring[i % kRing], pk[i >> 4], oacc[i & 15]);
-            if (i + kRing < 32) ring[i % kRing] = pv_opnd(tb, i + kRing);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    const float hi_all = fmaxf(s_hi, __shfl_xor(s_hi, 32));
-    const bool over = hi_all > m_ref + kRefSlack;  // a later score exceeded m_ref + 64
 
     // ---- write the split partial: un-normalised O, reference max, mass ----
     // Accumulator q, element r is latent column 32 q + 8 (r/4) + 4 half + r%4.
