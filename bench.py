@@ -122,7 +122,7 @@ def bench_prefill(args, mla, datagen):
 
     from mla_latent_kv_12_amd.tensors import to_device
 
-    case = datagen.make_config(4)
+    case = datagen.make_workload("v3-prefill-4k")
     dt = case.dtype
     cache = to_device(case.cache, dt)
     q_nope, q_rope = to_device(case.q_nope, dt), to_device(case.q_rope, dt)
@@ -177,8 +177,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3],
-                    help="decode workload index (3 = V3 shape, batch 8, 128k context)")
+    ap.add_argument("--workload", default="v3-128k", choices=["v3-4k", "v3-ragged", "v3-128k"],
+                    help="decode workload (v3-128k: V3 shape, batch 8, 131072 cached tokens)")
     ap.add_argument("--splits", type=int, default=0, help="context splits (0 = library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -193,8 +193,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are "
-                                   "not part of this build (see the sharding design)",
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path across "
+                                   "several GPUs (context or batch sharding) is a design only",
                           "n_gpus": args.gpus}), flush=True)
         return 2
 
@@ -228,7 +228,7 @@ def main(argv=None):
         return bench_prefill(args, mla, datagen)
 
     t_gen = time.perf_counter()
-    case = datagen.make_config(args.config)
+    case = datagen.make_workload(args.workload)
     print(f"# generated {case.name} in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
           flush=True)
     copies = [decode_tensors(case) for _ in range(max(1, args.rotate))]
@@ -308,7 +308,7 @@ def main(argv=None):
                                           1e3 * float(np.percentile(attn, 90))]},
         "roofline": {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": attn_gbps / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(args.config == 3 and args.splits in (0, 32)),
+                     "traffic": measured_traffic(args.workload == "v3-128k" and args.splits in (0, 32)),
                      "kernel": "decode_splitkv_bf16_kernel",
                      "algorithmic_bytes_per_launch": cache_bytes},
     }

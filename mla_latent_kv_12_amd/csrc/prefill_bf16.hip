@@ -35,31 +35,40 @@ __device__ __forceinline__ int clamp_len(int32_t v, int64_t n_max)
 // ---------------------------------------------------------------------------
 // 1. decompress GEMM: D[token][feature] = c[token][:] . W[feature][:] for the
 //    128 features of one head and 256 tokens.  8 waves as 2 (features) x 4
-//    (tokens) of 64 x 64.  K (the 512 latent channels) in chunks of 64: each
-//    chunk is 128 W rows + 256 c rows of 128 bytes, loaded direct-to-LDS,
-//    three chunks deep.  Row r's 16-byte pieces are XOR-swizzled by
-//    (r >> 1) & 7, so the MFMA operand reads (16 consecutive rows at one
-//    piece) touch 16 distinct bank groups.  The bf16 result is staged in LDS
-//    and written as whole 256-byte rows of the head-major output.
+//    (tokens) of 64 x 64.  K (the 512 latent channels) in chunks of 32: each
+//    chunk is 128 W rows + 256 c rows of 64 bytes, loaded direct-to-LDS,
+//    three chunks deep, 72 KiB per workgroup so that two workgroups share a
+//    CU and one's start-up overlaps the other's MFMAs.  Row r's 16-byte
+//    pieces are XOR-swizzled by (r / 4) & 3, so the MFMA operand reads (16
+//    consecutive rows at one piece) touch 16 distinct bank groups.  The bf16
+//    result is staged in LDS and written as whole 256-byte rows of the
+//    head-major output.
 // ---------------------------------------------------------------------------
 constexpr int kGF = 128;                                // features per workgroup (one head)
 constexpr int kGN = 256;                                // tokens per workgroup
-constexpr int kGK = 64;                                 // K chunk
+constexpr int kGK = 32;                                 // K chunk
 constexpr int kGWaves = 8;
 constexpr int kGThreads = 64 * kGWaves;
-constexpr int kGRowB = kGK * 2;                         // 128 B per LDS row of a chunk
-constexpr int kGWBytes = kGF * kGRowB;                  // 16 KiB
-constexpr int kGStage = kGWBytes + kGN * kGRowB;        // 48 KiB
-constexpr int kGDmaPerWave = kGStage / 1024 / kGWaves;  // 6
-constexpr int kGChunks = DC / kGK;                      // 8
+constexpr int kGRowB = kGK * 2;                         // 64 B per LDS row of a chunk
+constexpr int kGPieces = kGRowB / 16;                   // 16-byte pieces per row
+constexpr int kGRowsPerLoad = 1024 / kGRowB;            // rows per 1-KiB load
+constexpr int kGWLoads = kGF / kGRowsPerLoad;           // W loads per chunk
+constexpr int kGWBytes = kGF * kGRowB;                  // 8 KiB
+constexpr int kGStage = kGWBytes + kGN * kGRowB;        // 24 KiB
+constexpr int kGDmaPerWave = kGStage / 1024 / kGWaves;  // 3
+constexpr int kGChunks = DC / kGK;                      // 16
 constexpr int kGOutRow = DN * 2 + 16;                   // 272 B epilogue staging row
 static_assert(kGF == DN && kGF == DV, "one workgroup covers one head's features");
 static_assert(kGDmaPerWave * 1024 * kGWaves == kGStage, "whole loads per wave");
-static_assert(kGWBytes / 1024 == 2 * kGWaves, "the first two loads of each wave are W rows");
-static_assert(3 * kGStage <= 160 * 1024, "LDS budget");
+static_assert(kGWLoads % kGWaves == 0, "load e of every wave is a W load or a c load");
+static_assert(2 * (3 * kGStage) <= 160 * 1024, "two workgroups per CU");
 static_assert(kGN * kGOutRow <= 3 * kGStage, "epilogue staging fits in the chunk buffers");
 
-__global__ __launch_bounds__(kGThreads, 1) void decompress_gemm_bf16_kernel(
+// Piece swizzle of chunk row r: the rows of one 16-row group take the 16
+// (row phase, piece) combinations of the 16 bank groups.
+__host__ __device__ constexpr int gemm_swz(int r) { return (r / (16 / kGPieces)) % kGPieces; }
+
+__global__ __launch_bounds__(kGThreads, 2) void decompress_gemm_bf16_kernel(
     int H, int64_t n_max, const uint16_t *__restrict__ w_uk, const uint16_t *__restrict__ w_uv,
     const uint16_t *__restrict__ ckv, int64_t ckv_sb, int ckv_rowb,
     const int32_t *__restrict__ seqlens, uint16_t *__restrict__ kbuf, uint16_t *__restrict__ vbuf)
@@ -82,37 +91,37 @@ __global__ __launch_bounds__(kGThreads, 1) void decompress_gemm_bf16_kernel(
     const i32x4 rs_c = make_rsrc(ckv + static_cast<int64_t>(b) * ckv_sb,
                                  static_cast<uint32_t>(L) * static_cast<uint32_t>(ckv_rowb));
 
-    // Load d = wv + 8 e of a chunk (e = 0..5): d < 16 are W rows 8 d .. 8 d + 7,
-    // the rest c rows 8 (d - 16) .. + 7.  Lane -> row 8 i + lane / 8, LDS piece
-    // lane % 8 holding source piece (lane % 8) ^ ((row >> 1) & 7).
+    // Load d = wv + 8 e of a chunk: d < kGWLoads are W rows, the rest c rows,
+    // kGRowsPerLoad rows each.  Lane -> row (first row) + lane / pieces, LDS
+    // piece lane % pieces holding source piece (lane % pieces) ^ gemm_swz(row).
     unsigned voff[kGDmaPerWave];
 #pragma unroll
     for (int e = 0; e < kGDmaPerWave; ++e) {
         const int d = wv + kGWaves * e;
-        const int i = d < 16 ? d : d - 16;
-        const int row = 8 * i + (lane >> 3);
-        const int piece = (lane & 7) ^ ((row >> 1) & 7);
-        voff[e] = d < 16 ? static_cast<unsigned>(row * DC * 2 + 16 * piece)
-                         : static_cast<unsigned>((n0 + row) * ckv_rowb + 16 * piece);
+        const int i = d < kGWLoads ? d : d - kGWLoads;
+        const int row = kGRowsPerLoad * i + lane / kGPieces;
+        const int piece = (lane % kGPieces) ^ gemm_swz(row);
+        voff[e] = d < kGWLoads ? static_cast<unsigned>(row * DC * 2 + 16 * piece)
+                               : static_cast<unsigned>((n0 + row) * ckv_rowb + 16 * piece);
     }
     auto issue_chunk = [&](int kc, unsigned char *stage) {
         const unsigned k_byte = static_cast<unsigned>(kc * kGK * 2);
 #pragma unroll
         for (int e = 0; e < kGDmaPerWave; ++e) {
             const int d = wv + kGWaves * e;
-            if (e < 2)
+            if (kGWaves * e < kGWLoads)
                 lds_dma16(rs_w, stage + 1024 * d, voff[e] + k_byte);
             else
-                lds_dma16(rs_c, stage + kGWBytes + 1024 * (d - 16), voff[e] + k_byte);
+                lds_dma16(rs_c, stage + kGWBytes + 1024 * (d - kGWLoads), voff[e] + k_byte);
         }
     };
 
-    // Operand reads: row base + 32 rows * 128 B per block (immediate), piece
-    // (2 ks + half) ^ ((l32 >> 1) & 7).
+    // Operand reads: row base + 32 rows per block (immediate), piece
+    // (2 ks + half) ^ gemm_swz(l32) (block bases are multiples of 32 rows).
     int aoff[kGK / 16];
 #pragma unroll
     for (int ks = 0; ks < kGK / 16; ++ks)
-        aoff[ks] = l32 * kGRowB + 16 * ((2 * ks + half) ^ ((l32 >> 1) & 7));
+        aoff[ks] = l32 * kGRowB + 16 * ((2 * ks + half) ^ gemm_swz(l32));
 
     f32x16 acc[2][2];
 #pragma unroll

@@ -158,24 +158,27 @@ def make_prefill_case(*, B, T, H, dc, dr, dn, dv, d_model, dtype="bf16", seed=SE
                        w_uk, w_uv, cache, np.full(B, T, dtype=np.int32))
 
 
-# The five workloads: index -> (kind, keyword arguments).
-CONFIGS = {
-    0: ("decode", dict(name="tiny-f32 B1 H4 dc64 dr16 L128", dtype="f32", B=1, H=4, dc=64,
-                       dr=16, dn=32, dv=32, n_max=128)),
-    1: ("decode", dict(name="V3 bf16 B1 L4096", dtype="bf16", B=1, H=128, dc=512, dr=64,
-                       dn=128, dv=128, n_max=4096)),
-    2: ("decode", dict(name="V3 bf16 B32 ragged L~U[1,8192]", dtype="bf16", B=32, H=128,
-                       dc=512, dr=64, dn=128, dv=128, n_max=8192, ragged=True)),
-    3: ("decode", dict(name="V3 bf16 B8 L131072", dtype="bf16", B=8, H=128, dc=512, dr=64,
-                       dn=128, dv=128, n_max=131072)),
-    4: ("prefill", dict(name="V3 bf16 causal prefill B1 T4096", dtype="bf16", B=1, T=4096,
-                        H=128, dc=512, dr=64, dn=128, dv=128, d_model=7168)),
+# The named workloads: name -> (kind, seed offset, keyword arguments).  The
+# seed of a workload is SEED_BASE + its offset.
+WORKLOADS = {
+    "tiny-f32": ("decode", 0, dict(name="tiny-f32 B1 H4 dc64 dr16 L128", dtype="f32", B=1, H=4,
+                                   dc=64, dr=16, dn=32, dv=32, n_max=128)),
+    "v3-4k": ("decode", 1, dict(name="V3 bf16 B1 L4096", dtype="bf16", B=1, H=128, dc=512, dr=64,
+                                dn=128, dv=128, n_max=4096)),
+    "v3-ragged": ("decode", 2, dict(name="V3 bf16 B32 ragged L~U[1,8192]", dtype="bf16", B=32,
+                                    H=128, dc=512, dr=64, dn=128, dv=128, n_max=8192,
+                                    ragged=True)),
+    "v3-128k": ("decode", 3, dict(name="V3 bf16 B8 L131072", dtype="bf16", B=8, H=128, dc=512,
+                                  dr=64, dn=128, dv=128, n_max=131072)),
+    "v3-prefill-4k": ("prefill", 4, dict(name="V3 bf16 causal prefill B1 T4096", dtype="bf16",
+                                         B=1, T=4096, H=128, dc=512, dr=64, dn=128, dv=128,
+                                         d_model=7168)),
 }
 
 
-def make_config(index: int, seed: int | None = None):
-    kind, kw = CONFIGS[index]
-    seed = SEED_BASE + index if seed is None else seed
+def make_workload(name: str, seed: int | None = None):
+    kind, offset, kw = WORKLOADS[name]
+    seed = SEED_BASE + offset if seed is None else seed
     if kind == "decode":
         return make_decode_case(seed=seed, **kw)
     return make_prefill_case(seed=seed, **kw)

@@ -190,8 +190,8 @@ def test_bf16_rounding_is_nearest_even():
 
 
 def test_datagen_is_seeded_and_shaped():
-    a = datagen.make_config(0)
-    b = datagen.make_config(0)
+    a = datagen.make_workload("tiny-f32")
+    b = datagen.make_workload("tiny-f32")
     assert np.array_equal(a.cache, b.cache) and np.array_equal(a.w_uk, b.w_uk)
     assert a.cache.shape == (1, 128, 80) and a.dtype == "f32"
     assert a.scale == pytest.approx(1 / np.sqrt(48))

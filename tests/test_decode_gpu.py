@@ -31,9 +31,9 @@ def v3_case(B, n_max, seed, seqlens=None, ragged=False, **kw):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("splits", [0, 1, 2, 3, 4, 7])
-def test_tiny_f32_config0(splits):
-    case = datagen.make_config(0)
-    say(f"config0 tiny f32 seed={datagen.SEED_BASE} splits={splits}")
+def test_tiny_f32_workload(splits):
+    case = datagen.make_workload("tiny-f32")
+    say(f"tiny f32 workload seed={datagen.SEED_BASE} splits={splits}")
     out = to_host_f64(run_decode(case, num_splits=splits))
     assert_close(out, oracle_decode(case), "f32", "vs absorbed oracle")
     assert_close(out, oracle_decode(case, naive=True), "f32", "vs naive oracle")
@@ -70,9 +70,9 @@ def test_absorb_q(dtype):
 # bf16 workloads at their full sizes
 # ---------------------------------------------------------------------------
 
-def test_bf16_config1_full():
-    case = datagen.make_config(1)
-    say(f"config1 V3 B=1 L=4096 seed={datagen.SEED_BASE + 1}")
+def test_bf16_v3_4k_full():
+    case = datagen.make_workload("v3-4k")
+    say(f"V3 B=1 L=4096 seed={datagen.SEED_BASE + 1}")
     out = to_host_f64(run_decode(case))
     assert_close(out, oracle_decode(case), "bf16", "all heads vs absorbed oracle")
     pairs = [(0, h) for h in (0, 37, 101, 127)]
@@ -83,9 +83,9 @@ def test_bf16_config1_full():
     assert_close(out32, oracle_decode(case), "bf16", "fp32 output")
 
 
-def test_bf16_config2_ragged_full():
-    case = datagen.make_config(2)
-    say(f"config2 V3 B=32 ragged seed={datagen.SEED_BASE + 2} seqlens={case.seqlens.tolist()}")
+def test_bf16_v3_ragged_full():
+    case = datagen.make_workload("v3-ragged")
+    say(f"V3 B=32 ragged seed={datagen.SEED_BASE + 2} seqlens={case.seqlens.tolist()}")
     out = run_decode(case)
     order = np.argsort(case.seqlens)
     rng = np.random.default_rng(1)
@@ -96,9 +96,9 @@ def test_bf16_config2_ragged_full():
     assert_close(gather_pairs(out, pairs), ref, "bf16", f"{len(pairs)} sampled pairs")
 
 
-def test_bf16_config3_128k_full():
-    case = datagen.make_config(3)
-    say(f"config3 V3 B=8 L=131072 seed={datagen.SEED_BASE + 3}")
+def test_bf16_v3_128k_full():
+    case = datagen.make_workload("v3-128k")
+    say(f"V3 B=8 L=131072 seed={datagen.SEED_BASE + 3}")
     out = run_decode(case)  # automatic split count, as the benchmark launches it
     rng = np.random.default_rng(3)
     pairs = [(b, int(rng.integers(128))) for b in range(8)] + [(3, 0), (5, 127)]
@@ -244,3 +244,15 @@ def test_bf16_separate_rope_buffer_and_padded_rows():
     t2 = dict(t, ckv_cache=big[:, :, :512], kpe_cache=kpe)
     sep = run_decode(case, tensors=t2)
     assert torch.equal(fused, sep)
+
+
+@pytest.mark.parametrize("H,seqlens,splits", [(256, [777, 64], 0), (384, [31, 200, 1], 5)])
+def test_bf16_several_head_groups(H, seqlens, splits):
+    """More than one group of 128 heads: every group must read its own absorbed
+    queries and write its own partials and outputs."""
+    seed = 1700 + H + len(seqlens)
+    say(f"bf16 H={H} seqlens={seqlens} splits={splits} seed={seed}")
+    case = datagen.make_decode_case(B=len(seqlens), n_max=max(seqlens), seed=seed, seqlens=seqlens,
+                                    dtype="bf16", H=H, dc=512, dr=64, dn=128, dv=128)
+    out = to_host_f64(run_decode(case, num_splits=splits, out_dtype="f32"))
+    assert_close(out, oracle_decode(case), "bf16", f"H={H} vs absorbed oracle")

@@ -87,6 +87,22 @@ def test_prefill_bf16_against_naive(T, L):
     assert_close(got, absorbed_rows(case, rows_all), "bf16", "all rows vs absorbed identity")
 
 
+@pytest.mark.parametrize("B,T,L,H", [
+    (1, 40, [50], 3),               # 3 (sequence, head) pairs: plain block order
+    (3, 300, [300, 310, 555], 8),   # two query blocks, a ragged tail, keys beyond T
+    (2, 257, [257, 700], 4),        # one query past a 256-query block
+])
+def test_prefill_bf16_block_mapping_and_ragged(B, T, L, H):
+    say(f"prefill bf16 B={B} T={T} L={L} H={H}")
+    case = make_case(B, T, L, H, "bf16", 1500 + T + H)
+    out = run_prefill(case, out_dtype="f32")
+    rows = [(b, t) for b in range(B) for t in sorted({0, 1, T // 3, T - 2, T - 1, min(T - 1, 255), min(T - 1, 256)})]
+    got = np.stack([out[b, t] for b, t in rows])
+    assert_close(got, absorbed_rows(case, rows), "bf16", "sampled rows vs absorbed identity")
+    ref = oracle_rows(case, rows[:4])
+    assert_close(np.stack([out[b, t] for b, t in rows[:4]]), ref, "bf16", "4 rows vs naive oracle")
+
+
 def test_prefill_single_token_equals_decode():
     say("prefill T=1 vs decode (bf16, 128 heads)")
     case = make_case(3, 1, [200, 33, 1], 128, "bf16", 1401)
@@ -99,9 +115,9 @@ def test_prefill_single_token_equals_decode():
     assert_close(pre, dec, "bf16", "prefill(T=1) vs decode")
 
 
-def test_prefill_config4_full():
-    case = datagen.make_config(4)
-    say(f"config4 prefill T=4096 H=128 seed={datagen.SEED_BASE + 4}")
+def test_prefill_v3_4k_full():
+    case = datagen.make_workload("v3-prefill-4k")
+    say(f"V3 prefill T=4096 H=128 seed={datagen.SEED_BASE + 4}")
     t = prefill_tensors(case)
     out16 = run_prefill(case, t)              # the benchmark's launch: bf16 output
     out = run_prefill(case, t, out_dtype="f32")
