@@ -44,9 +44,10 @@ def test_traffic_record_is_tied_to_the_kernel_source(tmp_path, monkeypatch):
 
 def test_traffic_record_is_consistent():
     kv = _record(bench.TRAFFIC_FILE)
-    fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"]) * 1024
-    write = float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"]) * 1024
-    assert abs(fetch + write - float(kv["traffic_bytes_per_launch"])) <= 1.0
     copy_kib = int(kv["copy_bytes"]) / 1024
-    assert abs(float(kv["fetch_scale"]) - copy_kib / float(kv["copy_fetch_kib"])) < 1e-3
-    assert abs(float(kv["write_scale"]) - copy_kib / float(kv["copy_write_kib"])) < 1e-3
+    fs = copy_kib / float(kv["copy_fetch_kib"])     # the scales, from the copy's counts
+    ws = copy_kib / float(kv["copy_write_kib"])
+    assert abs(float(kv["fetch_scale"]) - fs) < 1e-3 and abs(float(kv["write_scale"]) - ws) < 1e-3
+    fetch = float(kv["fetch_kib_per_dispatch"]) * fs * 1024
+    write = float(kv["write_kib_per_dispatch"]) * ws * 1024
+    assert abs(fetch + write - float(kv["traffic_bytes_per_launch"])) <= 1e-6 * (fetch + write)
