@@ -8,10 +8,12 @@ from .oracle import (  # noqa: F401
     OracleError,
     absorb_q,
     build,
+    cache_rows,
     decode_absorbed,
     decode_naive,
     kv_cache_bytes,
     max_threads,
     prefill_naive,
+    rope,
     set_threads,
 )

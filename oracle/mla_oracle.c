@@ -293,6 +293,62 @@ int oracle_prefill_naive(const oracle_dims *d, int64_t T, const void *q_nope, co
 }
 
 /*
+ * Rotary position embedding of one d_r-vector at position pos (RoFormer, the
+ * rotary embedding the "mla-from-scratch" README cites for its relative
+ * position property): consecutive pairs (x_{2i}, x_{2i+1}) are rotated by the
+ * angle pos * theta_i, theta_i = base^(-2 i / d_r).  d_r must be even.
+ */
+void oracle_rope(int64_t dr, const double *x, double pos, double base, double *out)
+{
+    for (int64_t i = 0; i < dr / 2; ++i) {
+        const double theta = pow(base, -2.0 * (double)i / (double)dr);
+        const double a = pos * theta;
+        const double c = cos(a), s = sin(a);
+        const double x0 = x[2 * i], x1 = x[2 * i + 1];
+        out[2 * i] = x0 * c - x1 * s;
+        out[2 * i + 1] = x0 * s + x1 * c;
+    }
+}
+
+/*
+ * The cache producer for one new token per sequence: the compressed latent
+ * c_t = W_DKV h_t ("Deep-Dive ...", section 2: the down-projection of the
+ * hidden state) and the decoupled RoPE key k^R_t = RoPE_t(W_KR h_t) (the
+ * extra, uncompressed positional channels of the eyestech-mla description,
+ * "Key Architectural Highlights", and the "mla-from-scratch" README).  These
+ * are the rows the decode step appends to the cache before attending
+ * (songhuiming walk-through, MLA step 2).  h is [B][d_model]; W_DKV is
+ * [d_c][d_model]; W_KR is [d_r][d_model]; pos[b] is the row's position.
+ * Outputs: c [B][d_c] and kr [B][d_r], both fp64.
+ */
+int oracle_cache_rows(int64_t B, int64_t d_model, int64_t dc, int64_t dr, int32_t dtype,
+                      const void *h, const void *w_dkv, const void *w_kr, const int64_t *pos,
+                      double base, double *c, double *kr)
+{
+    if (B < 0 || d_model <= 0 || dc <= 0 || dr < 0 || (dr & 1) || !c || (dr > 0 && !kr)) return 1;
+    if (dtype != OR_F64 && dtype != OR_F32 && dtype != OR_BF16) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+        double *hb = malloc(sizeof(double) * (size_t)d_model);
+        double *raw = malloc(sizeof(double) * (size_t)(dr > 0 ? dr : 1));
+        widen_row(h, dtype, b * d_model, d_model, hb);
+        for (int64_t j = 0; j < dc; ++j) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < d_model; ++k) acc += widen(w_dkv, dtype, j * d_model + k) * hb[k];
+            c[b * dc + j] = acc;
+        }
+        for (int64_t j = 0; j < dr; ++j) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < d_model; ++k) acc += widen(w_kr, dtype, j * d_model + k) * hb[k];
+            raw[j] = acc;
+        }
+        if (dr > 0) oracle_rope(dr, raw, (double)pos[b], base, kr + b * dr);
+        free(hb); free(raw);
+    }
+    return 0;
+}
+
+/*
  * O4 -- latent-cache size in bytes: one row of d_c + d_r scalars per token
  * per layer per sequence ("mla-from-scratch" README, cache table: MLA is
  * d_c + d_rope = 512 + 64; eyestech-mla description, memory benchmark API).

@@ -14,6 +14,11 @@ Parity status of each function (the pins live in ``tests/test_oracle_pins.py``):
   prefill_naive    pinned: torch fp64 attention with an explicit bottom-right
                    causal mask; T=1 reduces to decode.
   kv_cache_bytes   pinned: the cache tables printed on the pages.
+  rope             pinned: the relative-position property (scores depend only on
+                   the position difference), norm preservation, position 0 is
+                   the identity, closed forms for one and two rotation pairs.
+  cache_rows       pinned: position 0 equals a plain fp64 matrix product
+                   (numpy); the RoPE part is rope() of that product.
 """
 from __future__ import annotations
 
@@ -72,6 +77,11 @@ def _open(path: str) -> ctypes.CDLL:
                                          vp, vp, i64, dp]
     lib.oracle_prefill_naive.restype = ctypes.c_int
     lib.oracle_kv_cache_bytes.argtypes = [i64] * 6
+    lib.oracle_rope.argtypes = [i64, dp, ctypes.c_double, ctypes.c_double, dp]
+    lib.oracle_rope.restype = None
+    lib.oracle_cache_rows.argtypes = [i64, i64, i64, i64, ctypes.c_int32, vp, vp, vp, vp,
+                                      ctypes.c_double, dp, dp]
+    lib.oracle_cache_rows.restype = ctypes.c_int
     lib.oracle_kv_cache_bytes.restype = ctypes.c_uint64
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -214,6 +224,38 @@ def prefill_naive(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, rows):
     if rc != 0:
         raise OracleError("oracle_prefill_naive rejected its arguments")
     return out
+
+
+def rope(x, pos, base=10000.0):
+    """Rotary embedding of the d_r-vector x at position pos (fp64)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    if x.shape[-1] % 2:
+        raise OracleError("rotary width must be even")
+    _load().oracle_rope(x.shape[-1], _ptr(x), float(pos), float(base), _ptr(out))
+    return out
+
+
+def cache_rows(h, w_dkv, w_kr, positions, base=10000.0):
+    """New cache rows for one token per sequence: c = W_DKV h and the rotated
+    decoupled key k^R = RoPE_pos(W_KR h).  h [B, d_model], W_DKV [d_c, d_model],
+    W_KR [d_r, d_model]; returns (c [B, d_c], k^R [B, d_r]) in fp64."""
+    h = np.ascontiguousarray(h)
+    w_dkv = np.ascontiguousarray(w_dkv)
+    w_kr = np.ascontiguousarray(w_kr)
+    dt = _code(h)
+    if _code(w_dkv) != dt or _code(w_kr) != dt:
+        raise OracleError("all inputs must share one storage dtype")
+    B, d_model = h.shape
+    dc, dr = w_dkv.shape[0], w_kr.shape[0]
+    pos = np.ascontiguousarray(positions, dtype=np.int64)
+    c = np.zeros((B, dc), dtype=np.float64)
+    kr = np.zeros((B, dr), dtype=np.float64)
+    rc = _load().oracle_cache_rows(B, d_model, dc, dr, dt, _ptr(h), _ptr(w_dkv), _ptr(w_kr),
+                                   _ptr(pos), float(base), _ptr(c), _ptr(kr))
+    if rc != 0:
+        raise OracleError("oracle_cache_rows rejected its arguments")
+    return c, kr
 
 
 def kv_cache_bytes(n_layers, batch, seq_len, d_c=512, d_r=64, bytes_per_elem=2) -> int:

@@ -67,6 +67,18 @@ MUTATIONS = [
     ("cache bytes: RoPE part left out",
      "(uint64_t)(d_c + d_r) * (uint64_t)bytes_per_elem;",
      "(uint64_t)d_c * (uint64_t)bytes_per_elem; (void)d_r;"),
+    ("rope: sine of the first component flipped",
+     "out[2 * i] = x0 * c - x1 * s;", "out[2 * i] = x0 * c + x1 * s;"),
+    ("rope: theta exponent without its factor 2",
+     "pow(base, -2.0 * (double)i / (double)dr)", "pow(base, -1.0 * (double)i / (double)dr)"),
+    ("rope: rotation angle without the position",
+     "const double a = pos * theta;", "const double a = theta; (void)pos;"),
+    ("cache rows: RoPE key projected with W_DKV",
+     "acc += widen(w_kr, dtype, j * d_model + k) * hb[k];",
+     "acc += widen(w_dkv, dtype, j * d_model + k) * hb[k];"),
+    ("cache rows: the key left unrotated",
+     "if (dr > 0) oracle_rope(dr, raw, (double)pos[b], base, kr + b * dr);",
+     "if (dr > 0) oracle_rope(dr, raw, 0.0, base, kr + b * dr);"),
     ("bf16 widening shifted",
      "uint32_t u = ((uint32_t)((const uint16_t *)base)[i]) << 16;",
      "uint32_t u = ((uint32_t)((const uint16_t *)base)[i]) << 15;"),
@@ -98,6 +110,10 @@ PINS = {
     "eyestech telemetry table": pins.test_cache_bytes_eyestech_telemetry,
     "mla-from-scratch table": pins.test_cache_bytes_mla_from_scratch_table,
     "songhuiming 99 tokens": pins.test_cache_elems_songhuiming_99_tokens,
+    "rope relative position": pins.test_rope_relative_position_property,
+    "rope norm and identity": pins.test_rope_norm_and_identity,
+    "rope closed forms": lambda: pins.test_rope_closed_forms(10000.0),
+    "cache rows": pins.test_cache_rows_are_projections_then_rotation,
 }
 
 

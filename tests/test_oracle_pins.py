@@ -405,3 +405,60 @@ def test_absorb_content_score_identity():
             assert abs(qa[b, h] @ c - q[b, h] @ k) <= 1e-12 * max(1.0, abs(q[b, h] @ k))
     # a transposed weight would not even have the right length
     assert qa.shape == (B, H, dc)
+
+
+# --------------------------------------------------------------------------
+# Rotary embedding of the decoupled key (RoFormer, cited by the
+# "mla-from-scratch" README for the relative position property) and the
+# cache-row producer c = W_DKV h, k^R = RoPE(W_KR h)
+# --------------------------------------------------------------------------
+
+def test_rope_relative_position_property():
+    """<R_m q, R_n k> depends on n - m only."""
+    rng = np.random.default_rng(61)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    for m, n in [(0, 5), (3, 8), (1000, 1005), (131066, 131071)]:
+        ref = oracle.rope(q, 0) @ oracle.rope(k, n - m)
+        got = oracle.rope(q, m) @ oracle.rope(k, n)
+        assert abs(got - ref) <= 1e-10 * max(1.0, abs(ref)), (m, n)
+    a = oracle.rope(q, 0) @ oracle.rope(k, 5)
+    b = oracle.rope(q, 0) @ oracle.rope(k, 6)
+    assert abs(a - b) > 1e-3
+
+
+def test_rope_norm_and_identity():
+    rng = np.random.default_rng(62)
+    x = rng.standard_normal(64)
+    assert np.array_equal(oracle.rope(x, 0), x)
+    for p in (1, 77, 4096, 131071):
+        assert abs(np.linalg.norm(oracle.rope(x, p)) - np.linalg.norm(x)) <= 1e-12 * np.linalg.norm(x)
+
+
+@pytest.mark.parametrize("base", [10000.0, 500.0])
+def test_rope_closed_forms(base):
+    """One pair: rotation by pos radians (theta_0 = 1).  Two pairs: the second
+    turns by pos * base^(-1/2)."""
+    x = np.array([0.3, -1.7, 2.2, 0.9])
+    for p in (1, 2, 13, 1000):
+        one = oracle.rope(x[:2], p, base)
+        assert np.allclose(one, [x[0] * math.cos(p) - x[1] * math.sin(p),
+                                 x[0] * math.sin(p) + x[1] * math.cos(p)], rtol=0, atol=1e-12)
+        two = oracle.rope(x, p, base)
+        a = p * base ** -0.5
+        assert np.allclose(two[:2], one, rtol=0, atol=1e-12)
+        assert np.allclose(two[2:], [x[2] * math.cos(a) - x[3] * math.sin(a),
+                                     x[2] * math.sin(a) + x[3] * math.cos(a)], rtol=0, atol=1e-12)
+
+
+def test_cache_rows_are_projections_then_rotation():
+    rng = np.random.default_rng(63)
+    B, d_model, dc, dr = 3, 96, 32, 8
+    h = rng.standard_normal((B, d_model))
+    w_dkv = rng.standard_normal((dc, d_model)) / math.sqrt(d_model)
+    w_kr = rng.standard_normal((dr, d_model)) / math.sqrt(d_model)
+    pos = [0, 7, 131071]
+    c, kr = oracle.cache_rows(h, w_dkv, w_kr, pos)
+    assert np.allclose(c, h @ w_dkv.T, rtol=0, atol=1e-12)            # library matmul
+    assert np.allclose(kr[0], h[0] @ w_kr.T, rtol=0, atol=1e-12)      # position 0: no rotation
+    for b in (1, 2):
+        assert np.allclose(kr[b], oracle.rope(h[b] @ w_kr.T, pos[b]), rtol=0, atol=1e-12)
