@@ -180,6 +180,54 @@ def bench_prefill(args, mla, datagen):
     return 0
 
 
+def bench_append(args, mla, datagen):
+    """The cache-row producer for one decode step: c = W_DKV h and the rotated
+    k^R = RoPE(W_KR h) for 8 sequences (d_model 7168), written into a 128k-row
+    cache; one JSON line with the algorithmic HBM rate against 8 TB/s."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_12_amd.tensors import to_device
+
+    case = datagen.make_workload("v3-append")
+    dt = case.dtype
+    h, w_dkv, w_kr = to_device(case.h, dt), to_device(case.w_dkv, dt), to_device(case.w_kr, dt)
+    n_max = 131072
+    cache = torch.zeros((case.B, n_max, case.dc + case.dr), dtype=torch.bfloat16, device="cuda")
+    pos = torch.tensor([(131071 - 977 * b) % n_max for b in range(case.B)], dtype=torch.int32,
+                       device="cuda")
+
+    def step():
+        mla.cache_append(h, w_dkv, w_kr, pos, cache[:, :, :case.dc], cache[:, :, case.dc:])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    us = 1e3 * float(np.mean(per))
+    nbytes = ((case.dc + case.dr) * case.d_model + case.B * case.d_model
+              + case.B * (case.dc + case.dr)) * 2
+    gbps = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "mode": "append", "metric": "cache-row producer HBM GB/s (% of peak)", "value": gbps,
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "us_per_step": us, "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic (seeded normals)",
+        "config": {"workload": case.name, "batch": case.B, "d_model": case.d_model,
+                   "d_c": case.dc, "d_r": case.dr},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_call": nbytes},
+        "us_p10_p90": [1e3 * float(np.percentile(per, 10)), 1e3 * float(np.percentile(per, 90))]}),
+        flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,9 +238,10 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0, help="context splits (0 = library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["decode", "prefill", "copy"], default="decode",
+    ap.add_argument("--mode", choices=["decode", "prefill", "append", "copy"], default="decode",
                     help="prefill: the naive causal prefill (V3 shape, T=4096) against the bf16 "
-                         "MFMA peak; copy: a plain device-to-device copy of --copy-bytes, the "
+                         "MFMA peak; append: the cache-row producer (batch 8, d_model 7168) "
+                         "against HBM; copy: a plain device-to-device copy of --copy-bytes, the "
                          "reference that scales the profiler's byte counters")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--rotate", type=int, default=1,
@@ -234,6 +283,8 @@ def main(argv=None):
 
     if args.mode == "prefill":
         return bench_prefill(args, mla, datagen)
+    if args.mode == "append":
+        return bench_append(args, mla, datagen)
 
     t_gen = time.perf_counter()
     case = datagen.make_workload(args.workload)

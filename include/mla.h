@@ -205,6 +205,49 @@ mla_status mla_prefill_naive(const mla_prefill_params *p, const void *q_nope,
                              size_t workspace_bytes, void *stream);
 
 /*
+ * Shape of a cache-append call: one new token per sequence.
+ * Supported: dtype MLA_BF16 or MLA_F32 (every tensor the same), d_c >= 2 and
+ * even, d_r >= 0 and even, d_model a multiple of 8 (bf16) or 4 (fp32).
+ */
+typedef struct mla_append_params {
+    int64_t batch;
+    int64_t d_model;      /* width of the hidden state h                        */
+    int64_t d_c, d_r;
+    int64_t n_max;        /* cache capacity (rows) per sequence                 */
+    int64_t ckv_stride_b, ckv_stride_n, kpe_stride_b, kpe_stride_n;  /* elements */
+    double rope_base;     /* rotary base; 0 -> 10000                            */
+    int32_t dtype;        /* MLA_BF16 or MLA_F32                                */
+    int32_t reserved;     /* must be 0                                          */
+} mla_append_params;
+
+/*
+ * The cache producer, the step before decode: for every sequence b whose
+ * positions[b] lies in [0, n_max), write the new token's cache row
+ *   ckv_cache[b][positions[b]] = W_DKV h_b            (d_c values)
+ *   kpe_cache[b][positions[b]] = RoPE_pos(W_KR h_b)   (d_r values)
+ * ("Deep-Dive: Multi-Head Latent Attention (MLA) and Low-Rank KV Cache
+ * Compression in DeepSeek-V3", section 2: c_t = W_DKV h_t; eyestech-mla
+ * description, "Key Architectural Highlights": the decoupled RoPE key stored
+ * beside the latent; songhuiming walk-through, MLA step 2: the new latent is
+ * appended before attending).  RoPE rotates consecutive pairs (2i, 2i+1) by
+ * the angle pos * theta_i, theta_i = rope_base^(-2i/d_r) (RoFormer, the
+ * rotary embedding the "mla-from-scratch" README cites).
+ *   h         [B][d_model]     dtype
+ *   w_dkv     [d_c][d_model]   dtype (row-major)
+ *   w_kr      [d_r][d_model]   dtype (row-major; may be NULL when d_r == 0)
+ *   positions [B] int32, device memory
+ *   ckv_cache, kpe_cache: strided as for mla_decode, one row written per
+ *             sequence (they may be the two views of one [B][n_max][d_c+d_r]
+ *             buffer)
+ * No other row is touched; a position outside [0, n_max) writes nothing for
+ * its sequence.  Dot products accumulate in fp32, rotation angles are
+ * formed in fp64; bf16 results are rounded to nearest even.
+ */
+mla_status mla_cache_append(const mla_append_params *p, const void *h, const void *w_dkv,
+                            const void *w_kr, const int32_t *positions, void *ckv_cache,
+                            void *kpe_cache, void *stream);
+
+/*
  * Latent-cache size (host): n_layers * batch * seq_len * (d_c + d_r) *
  * bytes_per_elem; 576 scalars per token per layer at the V3 shape
  * (eyestech-mla description, programmatic memory benchmark API).  Returns 0

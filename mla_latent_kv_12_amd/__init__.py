@@ -1,5 +1,6 @@
 """MI355X (gfx950) Multi-Head Latent Attention: absorbed decode over a latent
-KV cache and naive causal prefill, as hand-written HIP kernels behind a C ABI
+KV cache, the cache-row producer (latent and rotated RoPE key) and naive
+causal prefill, as hand-written HIP kernels behind a C ABI
 (include/mla.h).  This package is the thin Python binding over that library.
 """
 from .binding import (  # noqa: F401
@@ -11,10 +12,12 @@ from .binding import (  # noqa: F401
     MLA_ERR_WORKSPACE,
     MLA_F32,
     MLA_OK,
+    AppendParams,
     DecodeParams,
     MLAError,
     PrefillParams,
     absorb_q,
+    cache_append,
     decode,
     decode_num_splits,
     decode_params,

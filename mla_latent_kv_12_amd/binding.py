@@ -26,6 +26,7 @@ EXPORTS = (
     "mla_decode_profiled",
     "mla_prefill_workspace_bytes",
     "mla_prefill_naive",
+    "mla_cache_append",
     "mla_kv_cache_bytes",
     "mla_status_string",
     "mla_last_error",
@@ -63,6 +64,16 @@ class PrefillParams(ctypes.Structure):
     ]
 
 
+class AppendParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("d_model", ctypes.c_int64), ("d_c", ctypes.c_int64),
+        ("d_r", ctypes.c_int64), ("n_max", ctypes.c_int64),
+        ("ckv_stride_b", ctypes.c_int64), ("ckv_stride_n", ctypes.c_int64),
+        ("kpe_stride_b", ctypes.c_int64), ("kpe_stride_n", ctypes.c_int64),
+        ("rope_base", ctypes.c_double), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -92,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.mla_prefill_naive.argtypes = [ctypes.POINTER(PrefillParams), vp, vp, vp, vp, vp, vp, vp,
                                         vp, vp, sz, vp]
         L.mla_prefill_naive.restype = ctypes.c_int
+        L.mla_cache_append.argtypes = [ctypes.POINTER(AppendParams), vp, vp, vp, vp, vp, vp, vp]
+        L.mla_cache_append.restype = ctypes.c_int
         L.mla_kv_cache_bytes.argtypes = [ctypes.c_int64] * 6
         L.mla_kv_cache_bytes.restype = ctypes.c_uint64
         L.mla_status_string.argtypes = [ctypes.c_int]
@@ -248,6 +261,26 @@ def prefill_naive(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, 
                                    _ptr(out), _ptr(workspace), workspace.numel(),
                                    _stream(stream)))
     return out
+
+
+def cache_append(h, w_dkv, w_kr, positions, ckv_cache, kpe_cache, *, rope_base=None,
+                 stream=None):
+    """Write the new token's cache rows (``mla_cache_append``): for each sequence b
+    with 0 <= positions[b] < n_max, ckv_cache[b, pos] = W_DKV h[b] and
+    kpe_cache[b, pos] = RoPE_pos(W_KR h[b]).  h [B, d_model], W_DKV [d_c, d_model],
+    W_KR [d_r, d_model]; the caches are [B, n_max, width] views (updated in place)."""
+    B, d_model = h.shape
+    dc = w_dkv.shape[0]
+    dr = w_kr.shape[0] if w_kr is not None else 0
+    csb, csn = _cache_strides(ckv_cache, dc, "ckv_cache")
+    ksb, ksn = _cache_strides(kpe_cache, dr, "kpe_cache") if dr > 0 else (0, 0)
+    p = AppendParams(batch=B, d_model=d_model, d_c=dc, d_r=dr, n_max=ckv_cache.shape[1],
+                     ckv_stride_b=csb, ckv_stride_n=csn, kpe_stride_b=ksb, kpe_stride_n=ksn,
+                     rope_base=0.0 if rope_base is None else float(rope_base),
+                     dtype=_dtype_code(h.dtype), reserved=0)
+    _check(lib().mla_cache_append(ctypes.byref(p), _ptr(h), _ptr(w_dkv), _ptr(w_kr),
+                                  _ptr(positions), _ptr(ckv_cache),
+                                  _ptr(kpe_cache) if dr > 0 else None, _stream(stream)))
 
 
 def kv_cache_bytes(n_layers, batch, seq_len, d_c=512, d_r=64, bytes_per_elem=2) -> int:

@@ -1,0 +1,162 @@
+// append.hip -- the cache producer, the step before decode: for one new
+// token per sequence, c = W_DKV h and k^R = RoPE_pos(W_KR h), written into
+// row `pos` of that sequence's latent and RoPE-key caches ("Deep-Dive: MLA
+// and Low-Rank KV Cache Compression in DeepSeek-V3", section 2; eyestech-mla
+// description, "Key Architectural Highlights"; songhuiming walk-through, MLA
+// step 2).  The rotation turns consecutive pairs (2i, 2i+1) by pos * theta_i,
+// theta_i = base^(-2i/d_r) (RoFormer).
+//
+// A matrix-vector product per sequence: HBM-bound on the weights (d_c + d_r
+// rows of d_model values, 8.3 MB at the V3 shape), which every workgroup
+// reads once for a group of 8 sequences.  Workgroup = 4 waves = 4 output rows;
+// a wave streams its row in 16-byte pieces, lane-strided, dotting it with up to
+// 8 hidden states at once, then reduces across the wave.  Rows d_c + 2i and
+// d_c + 2i + 1 (one rotation pair) always fall in the same workgroup (row
+// groups start at multiples of 4 and d_c is even), which rotates the pair and
+// writes both.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "cdna4.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+using namespace cdna4;
+
+constexpr int kAppendRows = 4;     // output rows (waves) per workgroup
+constexpr int kAppendGroup = 8;    // sequences per pass over a weight row
+constexpr int kAppendUnroll = 4;   // 16-byte pieces per lane in flight per pass
+
+template <bool BF16>
+__device__ __forceinline__ void piece_to_f32(const u32x4 &v, float *f)
+{
+    if constexpr (BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[2 * e] = bf16lo(v[e]);
+            f[2 * e + 1] = bf16hi(v[e]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[e]);
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(64 * kAppendRows) void cache_append_kernel(
+    int B, int d_model, int dc, int dr, int64_t n_max, const u32x4 *__restrict__ h,
+    const u32x4 *__restrict__ w_dkv, const u32x4 *__restrict__ w_kr,
+    const int32_t *__restrict__ positions, double base, void *__restrict__ ckv, int64_t ckv_sb,
+    int64_t ckv_sn, void *__restrict__ kpe, int64_t kpe_sb, int64_t kpe_sn)
+{
+    constexpr int kVec = BF16 ? 8 : 4;  // elements per 16-byte piece
+    __shared__ float res[kAppendRows][kAppendGroup];
+
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int row0 = blockIdx.x * kAppendRows;
+    const int row = row0 + wv;                  // this wave's output row
+    const bool live = row < dc + dr;
+    const int pieces = d_model / kVec;          // 16-byte pieces per row
+    const u32x4 *wrow = !live ? w_dkv : row < dc ? w_dkv + static_cast<int64_t>(row) * pieces
+                                                 : w_kr + static_cast<int64_t>(row - dc) * pieces;
+
+    for (int b0 = 0; b0 < B; b0 += kAppendGroup) {
+        const int nb = min(kAppendGroup, B - b0);
+        float acc[kAppendGroup];
+#pragma unroll
+        for (int g = 0; g < kAppendGroup; ++g) acc[g] = 0.f;
+        if (live) {
+            // kAppendUnroll pieces per lane per pass, every load of a pass issued
+            // before any is used (indices past the row or the group are clamped to
+            // valid ones and their products dropped)
+            for (int p0 = lane; p0 < pieces; p0 += 64 * kAppendUnroll) {
+                u32x4 wq[kAppendUnroll], hq[kAppendUnroll][kAppendGroup];
+#pragma unroll
+                for (int u = 0; u < kAppendUnroll; ++u) {
+                    const int p = min(p0 + 64 * u, pieces - 1);
+                    wq[u] = wrow[p];
+#pragma unroll
+                    for (int g = 0; g < kAppendGroup; ++g)
+                        hq[u][g] = h[static_cast<int64_t>(b0 + min(g, nb - 1)) * pieces + p];
+                }
+#pragma unroll
+                for (int u = 0; u < kAppendUnroll; ++u) {
+                    if (p0 + 64 * u >= pieces) break;
+                    float wf[kVec];
+                    piece_to_f32<BF16>(wq[u], wf);
+#pragma unroll
+                    for (int g = 0; g < kAppendGroup; ++g) {
+                        float hf[kVec];
+                        piece_to_f32<BF16>(hq[u][g], hf);
+#pragma unroll
+                        for (int e = 0; e < kVec; ++e) acc[g] = fmaf(wf[e], hf[e], acc[g]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < kAppendGroup; ++g)
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) acc[g] += __shfl_xor(acc[g], o);
+        if (lane == 0) {
+#pragma unroll
+            for (int g = 0; g < kAppendGroup; ++g) res[wv][g] = acc[g];
+        }
+        __syncthreads();
+        // one thread per (row, sequence): rotate RoPE pairs, round, store
+        if (tid < kAppendRows * kAppendGroup) {
+            const int r = tid / kAppendGroup, g = tid % kAppendGroup;
+            const int j = row0 + r, b = b0 + g;
+            if (g < nb && j < dc + dr) {
+                const int pos = positions[b];
+                if (pos >= 0 && pos < n_max) {
+                    float v = res[r][g];
+                    if (j >= dc) {                 // rotation pair (2i, 2i + 1)
+                        const int i = (j - dc) >> 1;
+                        const double theta = pow(base, -2.0 * i / dr);
+                        double sn, cs;
+                        sincos(static_cast<double>(pos) * theta, &sn, &cs);
+                        const double x0 = res[r & ~1][g], x1 = res[r | 1][g];
+                        v = static_cast<float>(((j - dc) & 1) == 0 ? x0 * cs - x1 * sn
+                                                                   : x0 * sn + x1 * cs);
+                    }
+                    if (j < dc) {
+                        const int64_t o = static_cast<int64_t>(b) * ckv_sb + static_cast<int64_t>(pos) * ckv_sn + j;
+                        if constexpr (BF16) reinterpret_cast<__bf16 *>(ckv)[o] = static_cast<__bf16>(v);
+                        else reinterpret_cast<float *>(ckv)[o] = v;
+                    } else {
+                        const int64_t o = static_cast<int64_t>(b) * kpe_sb + static_cast<int64_t>(pos) * kpe_sn + (j - dc);
+                        if constexpr (BF16) reinterpret_cast<__bf16 *>(kpe)[o] = static_cast<__bf16>(v);
+                        else reinterpret_cast<float *>(kpe)[o] = v;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_cache_append(const AppendShape &s, const void *h, const void *w_dkv,
+                               const void *w_kr, const int32_t *positions, void *ckv, void *kpe,
+                               hipStream_t st)
+{
+    const int rows = s.dc + s.dr;
+    const unsigned grid = static_cast<unsigned>((rows + kAppendRows - 1) / kAppendRows);
+    if (s.bf16)
+        cache_append_kernel<true><<<grid, 64 * kAppendRows, 0, st>>>(
+            s.B, s.d_model, s.dc, s.dr, s.n_max, static_cast<const u32x4 *>(h),
+            static_cast<const u32x4 *>(w_dkv), static_cast<const u32x4 *>(w_kr), positions,
+            s.rope_base, ckv, s.ckv_sb, s.ckv_sn, kpe, s.kpe_sb, s.kpe_sn);
+    else
+        cache_append_kernel<false><<<grid, 64 * kAppendRows, 0, st>>>(
+            s.B, s.d_model, s.dc, s.dr, s.n_max, static_cast<const u32x4 *>(h),
+            static_cast<const u32x4 *>(w_dkv), static_cast<const u32x4 *>(w_kr), positions,
+            s.rope_base, ckv, s.ckv_sb, s.ckv_sn, kpe, s.kpe_sb, s.kpe_sn);
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -407,6 +407,56 @@ mla_status mla_prefill_naive(const mla_prefill_params *p, const void *q_nope, co
     return ok();
 }
 
+mla_status mla_cache_append(const mla_append_params *p, const void *h, const void *w_dkv,
+                            const void *w_kr, const int32_t *positions, void *ckv_cache,
+                            void *kpe_cache, void *stream)
+{
+    if (!p) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+    if (p->batch < 0 || p->d_model < 1 || p->d_c < 1 || p->d_r < 0 || p->n_max < 1)
+        return fail(MLA_ERR_INVALID_ARG, "invalid size");
+    if (p->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "reserved field must be 0");
+    if (p->dtype != MLA_BF16 && p->dtype != MLA_F32) return fail(MLA_ERR_UNSUPPORTED, "unknown dtype");
+    const bool bf16 = p->dtype == MLA_BF16;
+    const int64_t vec = bf16 ? 8 : 4;  // elements per 16-byte piece
+    if ((p->d_c & 1) || (p->d_r & 1))
+        return fail(MLA_ERR_UNSUPPORTED, "d_c and d_r must be even (rotation pairs)");
+    if (p->d_model % vec)
+        return fail(MLA_ERR_UNSUPPORTED, "d_model must be a multiple of %lld", (long long)vec);
+    if (p->batch > (1 << 24) || p->d_model > (1 << 24) || p->d_c + p->d_r > (1 << 20) ||
+        p->n_max > (1 << 30))
+        return fail(MLA_ERR_UNSUPPORTED, "sizes beyond the supported range");
+    if (p->ckv_stride_n < p->d_c || (p->d_r > 0 && p->kpe_stride_n < p->d_r) ||
+        p->ckv_stride_b < 0 || p->kpe_stride_b < 0)
+        return fail(MLA_ERR_INVALID_ARG, "cache strides smaller than the row width");
+    if (p->batch > 1 && (p->ckv_stride_b < p->n_max * p->ckv_stride_n ||
+                         (p->d_r > 0 && p->kpe_stride_b < p->n_max * p->kpe_stride_n)))
+        return fail(MLA_ERR_INVALID_ARG, "cache sequence stride smaller than n_max rows");
+    if (!(p->rope_base >= 0.0) || isinf(p->rope_base) || (p->rope_base > 0.0 && p->rope_base <= 1.0))
+        return fail(MLA_ERR_INVALID_ARG, "rope_base must be 0 (default) or a finite value > 1");
+    if (p->batch == 0) return ok();
+    if (!h || !w_dkv || !positions || !ckv_cache || (p->d_r > 0 && (!w_kr || !kpe_cache)))
+        return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (!aligned(h, 16) || !aligned(w_dkv, 16) || (w_kr && !aligned(w_kr, 16)) ||
+        !aligned(ckv_cache, bf16 ? 2 : 4) || (kpe_cache && !aligned(kpe_cache, bf16 ? 2 : 4)))
+        return fail(MLA_ERR_INVALID_ARG, "h and the weights must be 16-byte aligned");
+    mla::AppendShape s;
+    s.B = (int)p->batch;
+    s.d_model = (int)p->d_model;
+    s.dc = (int)p->d_c;
+    s.dr = (int)p->d_r;
+    s.n_max = p->n_max;
+    s.ckv_sb = p->ckv_stride_b;
+    s.ckv_sn = p->ckv_stride_n;
+    s.kpe_sb = p->kpe_stride_b;
+    s.kpe_sn = p->kpe_stride_n;
+    s.rope_base = p->rope_base > 0.0 ? p->rope_base : 10000.0;
+    s.bf16 = bf16;
+    hipError_t e = mla::launch_cache_append(s, h, w_dkv, w_kr, positions, ckv_cache, kpe_cache,
+                                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 uint64_t mla_kv_cache_bytes(int64_t n_layers, int64_t batch, int64_t seq_len, int64_t d_c,
                             int64_t d_r, int64_t bytes_per_elem)
 {

@@ -74,4 +74,15 @@ hipError_t launch_prefill_bf16(const PrefillShape &s, const void *q_nope, const 
                                const void *kpe, const int32_t *seqlens, void *out, void *kbuf,
                                void *vbuf, hipStream_t st);
 
+struct AppendShape {
+    int B, d_model, dc, dr;
+    int64_t n_max;
+    int64_t ckv_sb, ckv_sn, kpe_sb, kpe_sn;
+    double rope_base;
+    bool bf16;
+};
+hipError_t launch_cache_append(const AppendShape &s, const void *h, const void *w_dkv,
+                               const void *w_kr, const int32_t *positions, void *ckv,
+                               void *kpe, hipStream_t st);
+
 }  // namespace mla

@@ -158,6 +158,31 @@ def make_prefill_case(*, B, T, H, dc, dr, dn, dv, d_model, dtype="bf16", seed=SE
                        w_uk, w_uv, cache, np.full(B, T, dtype=np.int32))
 
 
+@dataclasses.dataclass
+class AppendCase:
+    """One new token per sequence: hidden states and the two producer weights."""
+    name: str
+    dtype: str
+    B: int
+    d_model: int
+    dc: int
+    dr: int
+    h: np.ndarray       # [B, d_model]
+    w_dkv: np.ndarray   # [dc, d_model]
+    w_kr: np.ndarray    # [dr, d_model]
+
+
+def make_append_case(*, B, d_model, dc, dr, dtype="bf16", seed=SEED_BASE, name="custom"):
+    """h ~ N(0, 1); W_DKV, W_KR ~ N(0, std 1/sqrt(d_model)), so the new latent
+    and key entries are of unit scale.  Draw order: h, W_DKV, W_KR."""
+    rng = np.random.default_rng(seed)
+    w_std = 1.0 / math.sqrt(d_model)
+    h = _store(_normal(rng, (B, d_model)), dtype)
+    w_dkv = _store(_normal(rng, (dc, d_model), w_std), dtype)
+    w_kr = _store(_normal(rng, (dr, d_model), w_std), dtype)
+    return AppendCase(name, dtype, B, d_model, dc, dr, h, w_dkv, w_kr)
+
+
 # The named workloads: name -> (kind, seed offset, keyword arguments).  The
 # seed of a workload is SEED_BASE + its offset.
 WORKLOADS = {
@@ -170,6 +195,8 @@ WORKLOADS = {
                                     ragged=True)),
     "v3-128k": ("decode", 3, dict(name="V3 bf16 B8 L131072", dtype="bf16", B=8, H=128, dc=512,
                                   dr=64, dn=128, dv=128, n_max=131072)),
+    "v3-append": ("append", 5, dict(name="V3 bf16 cache append B8 d_model 7168", dtype="bf16",
+                                    B=8, d_model=7168, dc=512, dr=64)),
     "v3-prefill-4k": ("prefill", 4, dict(name="V3 bf16 causal prefill B1 T4096", dtype="bf16",
                                          B=1, T=4096, H=128, dc=512, dr=64, dn=128, dv=128,
                                          d_model=7168)),
@@ -181,4 +208,6 @@ def make_workload(name: str, seed: int | None = None):
     seed = SEED_BASE + offset if seed is None else seed
     if kind == "decode":
         return make_decode_case(seed=seed, **kw)
+    if kind == "append":
+        return make_append_case(seed=seed, **kw)
     return make_prefill_case(seed=seed, **kw)

@@ -37,6 +37,7 @@ def test_struct_layouts_match_header():
     # field order and C sizes (int64 x 11, float, int32 x 3 -> 104 bytes)
     assert ctypes.sizeof(binding.DecodeParams) == 104
     assert ctypes.sizeof(binding.PrefillParams) == 12 * 8 + 4 * 4
+    assert ctypes.sizeof(binding.AppendParams) == 9 * 8 + 8 + 2 * 4   # + double rope_base
 
 
 def test_kv_cache_bytes_reproduces_the_pages():
@@ -171,6 +172,50 @@ def test_prefill_workspace_and_validation():
     assert call(_prefill_params(tokens=0)) == mla.MLA_ERR_INVALID_ARG
     assert call(p, nbytes=10) == mla.MLA_ERR_WORKSPACE
     assert call(p, ptrs=[vp(0)] + args[1:]) == mla.MLA_ERR_INVALID_ARG
+
+
+def _append_params(**kw):
+    base = dict(batch=8, d_model=7168, d_c=512, d_r=64, n_max=4096, ckv_stride_b=4096 * 576,
+                ckv_stride_n=576, kpe_stride_b=4096 * 576, kpe_stride_n=576, rope_base=0.0,
+                dtype=mla.MLA_BF16, reserved=0)
+    base.update(kw)
+    return binding.AppendParams(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_r=63), "UNSUPPORTED"),          # rotation pairs need an even width
+    (dict(d_c=511), "UNSUPPORTED"),
+    (dict(d_model=7170), "UNSUPPORTED"),    # not a whole number of 16-byte pieces
+    (dict(dtype=7), "UNSUPPORTED"),
+    (dict(reserved=1), "INVALID_ARG"),
+    (dict(n_max=0), "INVALID_ARG"),
+    (dict(ckv_stride_n=500), "INVALID_ARG"),
+    (dict(ckv_stride_b=576), "INVALID_ARG"),
+    (dict(rope_base=1.0), "INVALID_ARG"),
+    (dict(rope_base=-5.0), "INVALID_ARG"),
+])
+def test_append_rejects_bad_params_before_launch(kw, status):
+    lib = binding.lib()
+    vp = ctypes.c_void_p
+    p = _append_params(**kw)
+    rc = lib.mla_cache_append(ctypes.byref(p), *[vp(0x1000)] * 6, None)
+    assert rc == getattr(mla, "MLA_ERR_" + status)
+
+
+def test_append_rejects_null_and_misaligned_pointers():
+    lib = binding.lib()
+    vp = ctypes.c_void_p
+    p = _append_params()
+    good = [vp(0x1000)] * 6
+    for i in range(6):
+        bad = list(good)
+        bad[i] = vp(0)
+        assert lib.mla_cache_append(ctypes.byref(p), *bad, None) == mla.MLA_ERR_INVALID_ARG
+    bad = list(good)
+    bad[0] = vp(0x1008)                  # h not 16-byte aligned
+    assert lib.mla_cache_append(ctypes.byref(p), *bad, None) == mla.MLA_ERR_INVALID_ARG
+    # an empty batch is a no-op that needs no pointers
+    assert lib.mla_cache_append(ctypes.byref(_append_params(batch=0)), *[vp(0)] * 6, None) == 0
 
 
 def test_bf16_rounding_is_nearest_even():
