@@ -425,6 +425,8 @@ mla_status mla_cache_append(const mla_append_params *p, const void *h, const voi
     if (p->batch > (1 << 24) || p->d_model > (1 << 24) || p->d_c + p->d_r > (1 << 20) ||
         p->n_max > (1 << 30))
         return fail(MLA_ERR_UNSUPPORTED, "sizes beyond the supported range");
+    if ((uint64_t)p->batch * (uint64_t)p->d_model * (bf16 ? 2u : 4u) >= (1ull << 32))
+        return fail(MLA_ERR_UNSUPPORTED, "the hidden states must span < 4 GiB");
     if (p->ckv_stride_n < p->d_c || (p->d_r > 0 && p->kpe_stride_n < p->d_r) ||
         p->ckv_stride_b < 0 || p->kpe_stride_b < 0)
         return fail(MLA_ERR_INVALID_ARG, "cache strides smaller than the row width");
