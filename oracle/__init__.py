@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for MLA decode and naive causal prefill.
+"""fp64 CPU oracle for MLA decode, causal prefill (naive and absorbed) and the
+cache-row producer.
 
 Test infrastructure only: the tests, the smoke check and the benchmark's
 CPU-baseline leg use it; the product path (the HIP library and its binding)
@@ -13,6 +14,7 @@ from .oracle import (  # noqa: F401
     decode_naive,
     kv_cache_bytes,
     max_threads,
+    prefill_absorbed,
     prefill_naive,
     rope,
     set_threads,

@@ -263,15 +263,17 @@ int oracle_absorb_q(const oracle_dims *d, const void *q_nope, const void *w_uk, 
 }
 
 /*
- * O3 -- naive causal prefill.  T queries per sequence, q_nope [B][T][H][dn],
- * q_rope [B][T][H][dr].  Query t of sequence b sits at position
- * pos = L_b - T + t (the queries are the last T cached rows) and attends to
- * cached rows 0..pos inclusive, through the same decompress-then-attend
- * definition as O1.  rows lists (b, t) pairs; out is [nrows][H][dv].
+ * Causal prefill over selected query rows.  T queries per sequence,
+ * q_nope [B][T][H][dn], q_rope [B][T][H][dr].  Query t of sequence b sits at
+ * position pos = L_b - T + t (the queries are the last T cached rows) and
+ * attends to cached rows 0..pos inclusive through `fn`.  A query with
+ * pos < 0 (possible when L_b < T) sees no row and its output is zero, as for
+ * an empty decode.  rows lists (b, t) pairs; out is [nrows][H][dv].
  */
-int oracle_prefill_naive(const oracle_dims *d, int64_t T, const void *q_nope, const void *q_rope,
-                         const void *w_uk, const void *w_uv, const void *ckv, const void *kpe,
-                         const int32_t *seqlens, const int64_t *rows, int64_t nrows, double *out)
+static int prefill_common(one_fn fn, const oracle_dims *d, int64_t T, const void *q_nope,
+                          const void *q_rope, const void *w_uk, const void *w_uv,
+                          const void *ckv, const void *kpe, const int32_t *seqlens,
+                          const int64_t *rows, int64_t nrows, double *out)
 {
     if (check_dims(d) || T <= 0 || !rows || !out || !seqlens) return 1;
     int bad = 0;
@@ -280,16 +282,44 @@ int oracle_prefill_naive(const oracle_dims *d, int64_t T, const void *q_nope, co
     for (int64_t k = 0; k < work; ++k) {
         const int64_t r = k / d->H, h = k % d->H;
         const int64_t b = rows[2 * r], t = rows[2 * r + 1];
-        if (b < 0 || b >= d->B || t < 0 || t >= T || seqlens[b] < T) { bad = 1; continue; }
+        if (b < 0 || b >= d->B || t < 0 || t >= T) { bad = 1; continue; }
         const int64_t pos = (int64_t)seqlens[b] - T + t;
         double *qn = malloc(sizeof(double) * (size_t)d->dn);
         double *qr = malloc(sizeof(double) * (size_t)(d->dr > 0 ? d->dr : 1));
         widen_row(q_nope, d->dtype, ((b * T + t) * d->H + h) * d->dn, d->dn, qn);
         widen_row(q_rope, d->dtype, ((b * T + t) * d->H + h) * d->dr, d->dr, qr);
-        naive_one(d, qn, qr, w_uk, w_uv, ckv, kpe, b, h, pos + 1, out + k * d->dv);
+        fn(d, qn, qr, w_uk, w_uv, ckv, kpe, b, h, pos + 1, out + k * d->dv);
         free(qn); free(qr);
     }
     return bad;
+}
+
+/*
+ * O3 -- naive causal prefill: every query row through the decompress-then-
+ * attend definition O1 ("Deep-Dive ...", section 3, with the causal mask).
+ */
+int oracle_prefill_naive(const oracle_dims *d, int64_t T, const void *q_nope, const void *q_rope,
+                         const void *w_uk, const void *w_uv, const void *ckv, const void *kpe,
+                         const int32_t *seqlens, const int64_t *rows, int64_t nrows, double *out)
+{
+    return prefill_common(naive_one, d, T, q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, rows,
+                          nrows, out);
+}
+
+/*
+ * O5 -- absorbed causal prefill: every query row through the absorbed
+ * definition O2 (the query folded through W_UK, attention over the latent
+ * rows, one W_UV up-projection), the same associativity that makes absorbed
+ * decode exact ("mla-from-scratch" README, "Absorption, and why RoPE breaks
+ * it"), applied to T > 1 queries that share one latent cache.
+ */
+int oracle_prefill_absorbed(const oracle_dims *d, int64_t T, const void *q_nope,
+                            const void *q_rope, const void *w_uk, const void *w_uv,
+                            const void *ckv, const void *kpe, const int32_t *seqlens,
+                            const int64_t *rows, int64_t nrows, double *out)
+{
+    return prefill_common(absorbed_one, d, T, q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens,
+                          rows, nrows, out);
 }
 
 /*

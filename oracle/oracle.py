@@ -13,6 +13,9 @@ Parity status of each function (the pins live in ``tests/test_oracle_pins.py``):
                    RoPE-width grid, plus the same closed forms.
   prefill_naive    pinned: torch fp64 attention with an explicit bottom-right
                    causal mask; T=1 reduces to decode.
+  prefill_absorbed pinned: equals prefill_naive over a grid of widths, query
+                   counts and lengths (L < T included); each row equals
+                   decode_absorbed over its causal prefix.
   kv_cache_bytes   pinned: the cache tables printed on the pages.
   rope             pinned: the relative-position property (scores depend only on
                    the position difference), norm preservation, position 0 is
@@ -73,9 +76,10 @@ def _open(path: str) -> ctypes.CDLL:
         f.restype = ctypes.c_int
     lib.oracle_absorb_q.argtypes = [ctypes.POINTER(_Dims), vp, vp, dp]
     lib.oracle_absorb_q.restype = ctypes.c_int
-    lib.oracle_prefill_naive.argtypes = [ctypes.POINTER(_Dims), i64, vp, vp, vp, vp, vp, vp,
-                                         vp, vp, i64, dp]
-    lib.oracle_prefill_naive.restype = ctypes.c_int
+    for name in ("oracle_prefill_naive", "oracle_prefill_absorbed"):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.POINTER(_Dims), i64, vp, vp, vp, vp, vp, vp, vp, vp, i64, dp]
+        f.restype = ctypes.c_int
     lib.oracle_kv_cache_bytes.argtypes = [i64] * 6
     lib.oracle_rope.argtypes = [i64, dp, ctypes.c_double, ctypes.c_double, dp]
     lib.oracle_rope.restype = None
@@ -202,13 +206,7 @@ def absorb_q(q_nope, w_uk):
     return out
 
 
-def prefill_naive(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, rows):
-    """O3: naive causal prefill for selected query rows.
-
-    q_nope [B,T,H,dn], q_rope [B,T,H,dr]; query t of sequence b sits at
-    position seqlens[b] - T + t and sees cached rows up to and including it.
-    rows = [(b, t), ...]; returns [len(rows), H, dv].
-    """
+def _prefill(fname, q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, rows):
     q_nope = np.ascontiguousarray(q_nope)
     q_rope = np.ascontiguousarray(q_rope)
     w_uk = np.ascontiguousarray(w_uk)
@@ -218,12 +216,32 @@ def prefill_naive(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, rows):
     seq = np.ascontiguousarray(seqlens, dtype=np.int32)
     rr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
     out = np.zeros((rr.shape[0], d.H, d.dv), dtype=np.float64)
-    rc = _load().oracle_prefill_naive(ctypes.byref(d), T, _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
-                                      _ptr(w_uv), _base_ptr(ckv), _base_ptr(kpe), _ptr(seq),
-                                      _ptr(rr), rr.shape[0], _ptr(out))
+    rc = getattr(_load(), fname)(ctypes.byref(d), T, _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                 _ptr(w_uv), _base_ptr(ckv), _base_ptr(kpe), _ptr(seq),
+                                 _ptr(rr), rr.shape[0], _ptr(out))
     if rc != 0:
-        raise OracleError("oracle_prefill_naive rejected its arguments")
+        raise OracleError(f"{fname} rejected its arguments")
     return out
+
+
+def prefill_naive(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, rows):
+    """O3: naive causal prefill for selected query rows.
+
+    q_nope [B,T,H,dn], q_rope [B,T,H,dr]; query t of sequence b sits at
+    position seqlens[b] - T + t and sees cached rows up to and including it
+    (none, giving a zero row, when that position is negative).
+    rows = [(b, t), ...]; returns [len(rows), H, dv].
+    """
+    return _prefill("oracle_prefill_naive", q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens,
+                    scale, rows)
+
+
+def prefill_absorbed(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, rows):
+    """O5: absorbed causal prefill (each query row through the absorbed decode
+    definition over its causal prefix).  Same arguments and result as
+    :func:`prefill_naive`."""
+    return _prefill("oracle_prefill_absorbed", q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens,
+                    scale, rows)
 
 
 def rope(x, pos, base=10000.0):

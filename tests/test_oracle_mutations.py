@@ -57,8 +57,14 @@ MUTATIONS = [
     ("decode: cached length off by one",
      "(int64_t)seqlens[b], out + k * d->dv);", "(int64_t)seqlens[b] - 1, out + k * d->dv);"),
     ("prefill: diagonal masked out",
-     "naive_one(d, qn, qr, w_uk, w_uv, ckv, kpe, b, h, pos + 1, out + k * d->dv);",
-     "naive_one(d, qn, qr, w_uk, w_uv, ckv, kpe, b, h, pos > 0 ? pos : 1, out + k * d->dv);"),
+     "fn(d, qn, qr, w_uk, w_uv, ckv, kpe, b, h, pos + 1, out + k * d->dv);",
+     "fn(d, qn, qr, w_uk, w_uv, ckv, kpe, b, h, pos > 0 ? pos : 1, out + k * d->dv);"),
+    ("prefill: queries before the cache see row 0",
+     "fn(d, qn, qr, w_uk, w_uv, ckv, kpe, b, h, pos + 1, out + k * d->dv);",
+     "fn(d, qn, qr, w_uk, w_uv, ckv, kpe, b, h, pos < 0 ? 1 : pos + 1, out + k * d->dv);"),
+    ("absorbed prefill: through the naive definition with W_UK for W_UV",
+     "return prefill_common(absorbed_one, d, T, q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens,",
+     "return prefill_common(absorbed_one, d, T, q_nope, q_rope, w_uk, w_uk, ckv, kpe, seqlens,"),
     ("prefill: queries aligned top-left",
      "const int64_t pos = (int64_t)seqlens[b] - T + t;", "const int64_t pos = t;"),
     ("absorb_q: W_UK read transposed",
@@ -106,6 +112,10 @@ PINS = {
     "prefill vs masked SDPA, L>T": lambda: pins.test_prefill_matches_masked_sdpa(4, 11),
     "prefill vs masked SDPA, L=T": lambda: pins.test_prefill_matches_masked_sdpa(9, 9),
     "prefill row == decode prefix": pins.test_prefill_row_equals_decode_prefix,
+    "prefill rows before the cache": lambda: pins.test_prefill_rows_before_the_cache(6, 4),
+    "absorbed prefill == naive prefill":
+        lambda: pins.test_prefill_absorbed_equals_naive(64, 16, 5, 13),
+    "absorbed prefill row == decode prefix": pins.test_prefill_absorbed_row_equals_decode_prefix,
     "absorb_q content identity": pins.test_absorb_content_score_identity,
     "eyestech telemetry table": pins.test_cache_bytes_eyestech_telemetry,
     "mla-from-scratch table": pins.test_cache_bytes_mla_from_scratch_table,

@@ -358,6 +358,73 @@ def test_prefill_row_equals_decode_prefix():
         assert np.array_equal(pre[t], dec[0])
 
 
+@pytest.mark.parametrize("T,L", [(3, 9), (6, 4)])
+def test_prefill_rows_before_the_cache(T, L):
+    """Queries whose position L - T + t is negative (L < T) see no row and give
+    exact zeros; the remaining rows still match the masked SDPA reference."""
+    rng = np.random.default_rng(200 + 10 * T + L)
+    B, H, dc, dr, dn, dv = 1, 2, 24, 8, 16, 12
+    q_nope = rng.standard_normal((B, T, H, dn))
+    q_rope = rng.standard_normal((B, T, H, dr))
+    w_uk = rng.standard_normal((H, dn, dc)) / math.sqrt(dc)
+    w_uv = rng.standard_normal((H, dv, dc)) / math.sqrt(dc)
+    cache = rng.standard_normal((B, max(L, 1), dc + dr))
+    rows = [(0, t) for t in range(T)]
+    for fn in (oracle.prefill_naive, oracle.prefill_absorbed):
+        out = fn(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc], cache[:, :, dc:], [L], 0.3, rows)
+        first = max(T - L, 0)                      # first query with a non-negative position
+        assert np.all(out[:first] == 0.0)
+        live = list(range(first, T))
+        # the live rows are the last L - (T - T') queries of a prefill with T' = T - first
+        ref = _sdpa_prefill(q_nope[:, first:], q_rope[:, first:], w_uk, w_uv, cache,
+                            np.array([L], np.int32), 0.3, 0, [t - first for t in live])
+        assert np.max(np.abs(out[first:] - ref)) <= 1e-12
+
+
+# --------------------------------------------------------------------------
+# O5: absorbed causal prefill == naive causal prefill
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dc,dr", [(16, 0), (64, 16), (512, 64)])
+@pytest.mark.parametrize("T,L", [(1, 1), (4, 4), (5, 13), (7, 3)])
+def test_prefill_absorbed_equals_naive(dc, dr, T, L):
+    """The associativity behind absorbed decode, for T > 1 causal queries that
+    share one latent cache (ragged, L < T included)."""
+    rng = np.random.default_rng(3000 + dc + 10 * dr + 100 * T + L)
+    B, H, dn, dv = 2, 2, 16, 12
+    q_nope = rng.standard_normal((B, T, H, dn))
+    q_rope = rng.standard_normal((B, T, H, dr))
+    w_uk = rng.standard_normal((H, dn, dc)) / math.sqrt(dc)
+    w_uv = rng.standard_normal((H, dv, dc)) / math.sqrt(dc)
+    N = max(L, T)
+    cache = rng.standard_normal((B, N, dc + dr))
+    seqlens = np.array([L, N], np.int32)            # second sequence: its own length
+    rows = [(b, t) for b in range(B) for t in range(T)]
+    args = (q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc], cache[:, :, dc:], seqlens,
+            1.0 / math.sqrt(dn + dr), rows)
+    naive = oracle.prefill_naive(*args)
+    absorbed = oracle.prefill_absorbed(*args)
+    assert _rel(absorbed, naive) <= 1e-12
+
+
+def test_prefill_absorbed_row_equals_decode_prefix():
+    """Each absorbed prefill row is bitwise the absorbed decode over the first
+    pos_t + 1 cached rows."""
+    rng = np.random.default_rng(8)
+    B, T, H, dc, dr, dn, dv, L = 1, 5, 2, 32, 8, 16, 16, 9
+    q_nope = rng.standard_normal((B, T, H, dn))
+    q_rope = rng.standard_normal((B, T, H, dr))
+    w_uk = rng.standard_normal((H, dn, dc)) / math.sqrt(dc)
+    w_uv = rng.standard_normal((H, dv, dc)) / math.sqrt(dc)
+    cache = rng.standard_normal((B, L, dc + dr))
+    pre = oracle.prefill_absorbed(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc],
+                                  cache[:, :, dc:], [L], 0.3, [(0, t) for t in range(T)])
+    for t in range(T):
+        dec, _ = oracle.decode_absorbed(q_nope[:, t], q_rope[:, t], w_uk, w_uv,
+                                        cache[:, :, :dc], cache[:, :, dc:], [L - T + t + 1], 0.3)
+        assert np.array_equal(pre[t], dec[0])
+
+
 # --------------------------------------------------------------------------
 # Mutations: each plausible oracle mistake is caught by the pins above
 # --------------------------------------------------------------------------
