@@ -137,7 +137,8 @@ def bench_prefill(args, mla, datagen):
     w_uk, w_uv = to_device(case.w_uk, dt), to_device(case.w_uv, dt)
     ckv, kpe = cache[:, :, : case.dc], cache[:, :, case.dc:]
     seqlens = torch.from_numpy(case.seqlens.astype(np.int32)).cuda()
-    params = mla.prefill_params(q_nope, q_rope, w_uk, w_uv, ckv, kpe, softmax_scale=case.scale)
+    params = mla.prefill_params(q_nope, q_rope, w_uk, w_uv, ckv, kpe, softmax_scale=case.scale,
+                                q_rope_base=args.q_rope_base or None)
     ws = torch.empty(mla.prefill_workspace_bytes(params), dtype=torch.uint8, device="cuda")
     out = torch.empty((case.B, case.T, case.H, case.dv), dtype=torch.bfloat16, device="cuda")
 
@@ -170,11 +171,77 @@ def bench_prefill(args, mla, datagen):
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "bf16",
         "data": "synthetic (seeded normals; c = W_DKV x from x of width 7168)",
         "config": {"workload": case.name, "batch": case.B, "tokens": case.T, "heads": case.H,
-                   "cached_tokens_total": rows},
+                   "cached_tokens_total": rows, "q_rope_base": args.q_rope_base},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                      "algorithmic_flops_per_call": flops, "decompress_flops": f_decomp,
                      "attention_flops": f_attn},
+        "ms_p10_p90": [float(np.percentile(per, 10)), float(np.percentile(per, 90))]}),
+        flush=True)
+    return 0
+
+
+def bench_chunk(args, mla, datagen):
+    """Absorbed causal prefill (a chunk of new queries attending to a long cached
+    context in latent space) on the V3 shape: batch 4, 64 queries each over
+    32768 cached rows; one JSON line with the whole call's bf16 MFMA
+    throughput against the dense peak."""
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_12_amd.tensors import to_device
+
+    case = datagen.make_workload("v3-chunk-32k")
+    dt = case.dtype
+    cache = to_device(case.cache, dt)
+    q_nope, q_rope = to_device(case.q_nope, dt), to_device(case.q_rope, dt)
+    w_uk, w_uv = to_device(case.w_uk, dt), to_device(case.w_uv, dt)
+    ckv, kpe = cache[:, :, : case.dc], cache[:, :, case.dc:]
+    seqlens = torch.from_numpy(case.seqlens.astype(np.int32)).cuda()
+    params = mla.prefill_params(q_nope, q_rope, w_uk, w_uv, ckv, kpe, softmax_scale=case.scale,
+                                num_splits=args.splits,
+                                q_rope_base=args.q_rope_base or None)
+    ws = torch.empty(mla.prefill_absorbed_workspace_bytes(params), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((case.B, case.T, case.H, case.dv), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        mla.prefill_absorbed(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, out=out, workspace=ws,
+                             params=params)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    ms = float(np.mean(per))
+    L = case.seqlens.astype(np.int64)
+    rows = case.B * case.T
+    pairs = int(sum(int(l) * case.T - case.T * (case.T - 1) // 2 for l in L))
+    f_absorb = 2 * rows * case.H * case.dn * case.dc
+    f_attn = 2 * pairs * case.H * (2 * case.dc + case.dr)
+    f_up = 2 * rows * case.H * case.dv * case.dc
+    flops = f_absorb + f_attn + f_up
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "mode": "chunk", "metric": "absorbed causal prefill bf16 MFMA TFLOP/s (% of dense peak)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic (seeded normals)",
+        "config": {"workload": case.name, "batch": case.B, "tokens": case.T, "heads": case.H,
+                   "cached_tokens_total": int(L.sum()),
+                   "splits": mla.prefill_absorbed_num_splits(params),
+                   "q_rope_base": args.q_rope_base},
+        "query_tokens_per_s": rows / (ms * 1e-3),
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "algorithmic_flops_per_call": flops, "attention_flops": f_attn,
+                     "absorb_and_upproj_flops": f_absorb + f_up},
         "ms_p10_p90": [float(np.percentile(per, 10)), float(np.percentile(per, 90))]}),
         flush=True)
     return 0
@@ -238,9 +305,15 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0, help="context splits (0 = library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["decode", "prefill", "append", "copy"], default="decode",
+    ap.add_argument("--q-rope-base", type=float, default=0.0,
+                    help="rotate q_rope in the library at each query's position with this base "
+                         "(0: q_rope is taken as already rotated)")
+    ap.add_argument("--mode", choices=["decode", "prefill", "chunk", "append", "copy"],
+                    default="decode",
                     help="prefill: the naive causal prefill (V3 shape, T=4096) against the bf16 "
-                         "MFMA peak; append: the cache-row producer (batch 8, d_model 7168) "
+                         "MFMA peak; chunk: the absorbed prefill of 64 queries per sequence over "
+                         "32768 cached rows (batch 4); append: the cache-row producer (batch 8, "
+                         "d_model 7168) "
                          "against HBM; copy: a plain device-to-device copy of --copy-bytes, the "
                          "reference that scales the profiler's byte counters")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
@@ -283,6 +356,8 @@ def main(argv=None):
 
     if args.mode == "prefill":
         return bench_prefill(args, mla, datagen)
+    if args.mode == "chunk":
+        return bench_chunk(args, mla, datagen)
     if args.mode == "append":
         return bench_append(args, mla, datagen)
 
@@ -293,7 +368,8 @@ def main(argv=None):
     copies = [decode_tensors(case) for _ in range(max(1, args.rotate))]
     t = copies[0]
     params = mla.decode_params(t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv_cache"],
-                               t["kpe_cache"], softmax_scale=case.scale, num_splits=args.splits)
+                               t["kpe_cache"], softmax_scale=case.scale, num_splits=args.splits,
+                               q_rope_base=args.q_rope_base or None)
     splits = mla.decode_num_splits(params)
     ws = torch.empty(mla.decode_workspace_bytes(params), dtype=torch.uint8, device="cuda")
     out = torch.empty((case.B, case.H, case.dv), dtype=torch.bfloat16, device="cuda")
@@ -354,7 +430,8 @@ def main(argv=None):
         "data": "synthetic (seeded normals; random-init weights of the V3 shape)",
         "config": {"workload": case.name, "batch": case.B, "heads": case.H, "d_c": case.dc,
                    "d_r": case.dr, "d_n": case.dn, "d_v": case.dv,
-                   "cached_tokens_total": rows, "splits": splits, "input_copies": len(copies)},
+                   "cached_tokens_total": rows, "splits": splits, "input_copies": len(copies),
+                   "q_rope_base": args.q_rope_base},
         "hbm_gbps_call": call_gbps,
         "hbm_frac_call": call_gbps / HBM_PEAK_GBPS,
         "context_rows_per_s": rows / (ms_per_step * 1e-3),
@@ -367,7 +444,8 @@ def main(argv=None):
                                           1e3 * float(np.percentile(attn, 90))]},
         "roofline": {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": attn_gbps / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(args.workload == "v3-128k" and args.splits in (0, 32)),
+                     "traffic": measured_traffic(args.workload == "v3-128k" and args.splits in (0, 32)
+                                                 and not args.q_rope_base),
                      "kernel": "decode_splitkv_bf16_kernel",
                      "algorithmic_bytes_per_launch": cache_bytes},
     }

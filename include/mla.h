@@ -2,7 +2,9 @@
  * mla.h -- C ABI of the MI355X (gfx950) Multi-Head Latent Attention library.
  *
  * The library computes MLA decode over a compressed latent KV cache with
- * query absorption, and a naive decompress-then-attend causal prefill.
+ * query absorption, causal prefill both as the naive decompress-then-attend
+ * form and in absorbed (latent-space) form, and the cache producer that
+ * writes a new token's latent and rotated RoPE key.
  *
  * Notation (the pages' own): each cached token holds a latent row c of d_c
  * scalars and a decoupled-RoPE key k^R of d_r scalars (512 + 64 = 576 for the
@@ -94,7 +96,24 @@ typedef struct mla_decode_params {
     int32_t dtype;        /* mla_dtype of q_nope, q_rope, weights and caches   */
     int32_t out_dtype;    /* mla_dtype of out                                   */
     int32_t num_splits;   /* context splits per sequence; 0 -> chosen by size  */
+    double q_rope_base;   /* 0: q_rope arrives rotated for its position; > 1:
+                             the library rotates it (see below) with this base */
 } mla_decode_params;
+
+/*
+ * Query-side rotary embedding (q_rope_base > 1).  The query of sequence b at
+ * position p has its q_rope rotated before use: consecutive pairs (2i, 2i+1)
+ * turn by p * theta_i, theta_i = q_rope_base^(-2i/d_r) (RoFormer, the rotary
+ * embedding the "mla-from-scratch" README cites; the same convention as the
+ * key rotation of mla_cache_append).  The position is that of the query's own
+ * cache row: p = L_b - 1 for decode and p = L_b - T + t for query t of a
+ * prefill (L_b clamped to [0, n_max]).  Angles are formed and the rotation
+ * applied in fp64; the rotated vector is rounded to `dtype` and used in
+ * place of q_rope.  A query with p < 0 sees no key and gets a zero row.  d_r
+ * must be even.  With keys written by mla_cache_append at their row index,
+ * the positional score term then depends only on the distance between the
+ * query's row and the key's row (RoFormer's relative-position property).
+ */
 
 /*
  * Query absorption: q_abs[b][h][:] = W_UK[h]^T q_nope[b][h][:]
@@ -133,10 +152,12 @@ size_t mla_decode_workspace_bytes(const mla_decode_params *p);
  * [W_UK[h] c_n ; k^R_n] and values W_UV[h] c_n ("mla-from-scratch" README,
  * "Absorption, and why RoPE breaks it"; distaisys deep-dive, section 3).
  *   q_nope    [B][H][d_n]  dtype
- *   q_rope    [B][H][d_r]  dtype (already rotated for this position)
+ *   q_rope    [B][H][d_r]  dtype (rotated for the query's position, or
+ *             rotated here when q_rope_base > 1, see above)
  *   w_uk      [H][d_n][d_c], w_uv [H][d_v][d_c]  dtype
  *   ckv_cache latent rows, element (b, n, j) at b*ckv_stride_b + n*ckv_stride_n + j
- *   kpe_cache RoPE keys (already rotated), likewise with the kpe strides
+ *   kpe_cache RoPE keys, rotated for their rows (as mla_cache_append writes
+ *             them), likewise with the kpe strides
  *   seqlens   [B] int32 (see the conventions above)
  *   out       [B][H][d_v]  out_dtype, written
  *   workspace >= mla_decode_workspace_bytes(p) bytes, 256-byte aligned;
@@ -179,16 +200,20 @@ typedef struct mla_prefill_params {
     float softmax_scale;  /* 0 -> 1/sqrt(d_n + d_r)                             */
     int32_t dtype;
     int32_t out_dtype;
-    int32_t reserved;     /* must be 0                                          */
+    int32_t num_splits;   /* mla_prefill_absorbed: context splits per query row,
+                             0 -> chosen by size; mla_prefill_naive: must be 0 */
+    double q_rope_base;   /* 0: q_rope arrives rotated; > 1: rotated by the
+                             library at each query's position (see above)     */
 } mla_prefill_params;
 
 /* Bytes of device workspace mla_prefill_naive needs (host; 0 if invalid). */
 size_t mla_prefill_workspace_bytes(const mla_prefill_params *p);
 
 /*
- * Naive causal prefill: decompress every cached latent row into
- * K_nope[b][n][h] = W_UK[h] c[b][n] and V[b][n][h] = W_UV[h] c[b][n] (kept in
- * the workspace, i.e. materialised in HBM on purpose), then for query t at
+ * Naive causal prefill: decompress every cached latent row into the key and
+ * value of every head, K_nope = W_UK[h] c[b][n] and V = W_UV[h] c[b][n] (kept
+ * in the workspace, i.e. materialised in HBM on purpose, in a layout private
+ * to the library), then for query t at
  * position pos = L_b - T + t attend over rows n <= pos with keys
  * [K_nope ; k^R] and values V (distaisys deep-dive, section 3, with a causal
  * mask that includes the diagonal; songhuiming walk-through, MLA step 2).
@@ -203,6 +228,41 @@ mla_status mla_prefill_naive(const mla_prefill_params *p, const void *q_nope,
                              const void *ckv_cache, const void *kpe_cache,
                              const int32_t *seqlens, void *out, void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/* Context splits per query row that mla_prefill_absorbed will use (host;
+ * 0 if `p` is invalid). */
+int mla_prefill_absorbed_num_splits(const mla_prefill_params *p);
+
+/* Bytes of device workspace mla_prefill_absorbed needs (host; 0 if invalid).
+ * Depends on batch, tokens, heads, dims and the split count. */
+size_t mla_prefill_absorbed_workspace_bytes(const mla_prefill_params *p);
+
+/*
+ * Absorbed causal prefill (chunked prefill in latent space): the T new
+ * queries of each sequence, the last T of its L_b cached rows, attend to the
+ * latent cache directly, each exactly as an absorbed decode over its causal
+ * prefix: for query t at position pos = L_b - T + t,
+ *   q~  = W_UK[h]^T q_nope[b][t][h]
+ *   s_n = scale * (q~ . c[b][n] + q_rope[b][t][h] . k^R[b][n]),  n <= pos
+ *   out[b][t][h] = W_UV[h] sum_n softmax_n(s) c[b][n]
+ * The associativity that makes absorbed decode exact ("mla-from-scratch"
+ * README, "Absorption, and why RoPE breaks it") applied to T > 1 queries
+ * sharing one cache; no key or value is decompressed, so the cost grows with
+ * T x L_b at 2 (2 d_c + d_r) flop per (query, key, head) and the cache is
+ * read as for decode.  It pays when T is small beside L_b (a chunk appended
+ * to a long context); for a whole prompt the naive path does fewer flops.
+ *   Arguments, layouts and the causal alignment as for mla_prefill_naive;
+ *   workspace >= mla_prefill_absorbed_workspace_bytes(p), 256-byte aligned.
+ * Supported: the decode limits (dtype MLA_BF16: the V3 widths and heads a
+ * multiple of 128; MLA_F32: the fp32 limits), batch * tokens <= 65535.
+ * Results are bitwise reproducible for a fixed split count; a query with
+ * pos < 0 gets a zero row.
+ */
+mla_status mla_prefill_absorbed(const mla_prefill_params *p, const void *q_nope,
+                                const void *q_rope, const void *w_uk, const void *w_uv,
+                                const void *ckv_cache, const void *kpe_cache,
+                                const int32_t *seqlens, void *out, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * Shape of a cache-append call: one new token per sequence.

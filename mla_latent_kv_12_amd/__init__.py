@@ -1,6 +1,6 @@
 """MI355X (gfx950) Multi-Head Latent Attention: absorbed decode over a latent
-KV cache, the cache-row producer (latent and rotated RoPE key) and naive
-causal prefill, as hand-written HIP kernels behind a C ABI
+KV cache, the cache-row producer (latent and rotated RoPE key), and causal
+prefill in naive and absorbed form, as hand-written HIP kernels behind a C ABI
 (include/mla.h).  This package is the thin Python binding over that library.
 """
 from .binding import (  # noqa: F401
@@ -23,6 +23,9 @@ from .binding import (  # noqa: F401
     decode_params,
     decode_workspace_bytes,
     kv_cache_bytes,
+    prefill_absorbed,
+    prefill_absorbed_num_splits,
+    prefill_absorbed_workspace_bytes,
     prefill_naive,
     prefill_params,
     prefill_workspace_bytes,

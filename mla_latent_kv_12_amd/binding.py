@@ -26,6 +26,9 @@ EXPORTS = (
     "mla_decode_profiled",
     "mla_prefill_workspace_bytes",
     "mla_prefill_naive",
+    "mla_prefill_absorbed_num_splits",
+    "mla_prefill_absorbed_workspace_bytes",
+    "mla_prefill_absorbed",
     "mla_cache_append",
     "mla_kv_cache_bytes",
     "mla_status_string",
@@ -49,6 +52,7 @@ class DecodeParams(ctypes.Structure):
         ("kpe_stride_b", ctypes.c_int64), ("kpe_stride_n", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+        ("q_rope_base", ctypes.c_double),
     ]
 
 
@@ -60,7 +64,8 @@ class PrefillParams(ctypes.Structure):
         ("ckv_stride_b", ctypes.c_int64), ("ckv_stride_n", ctypes.c_int64),
         ("kpe_stride_b", ctypes.c_int64), ("kpe_stride_n", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float), ("dtype", ctypes.c_int32),
-        ("out_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+        ("q_rope_base", ctypes.c_double),
     ]
 
 
@@ -103,6 +108,13 @@ def lib() -> ctypes.CDLL:
         L.mla_prefill_naive.argtypes = [ctypes.POINTER(PrefillParams), vp, vp, vp, vp, vp, vp, vp,
                                         vp, vp, sz, vp]
         L.mla_prefill_naive.restype = ctypes.c_int
+        L.mla_prefill_absorbed_num_splits.argtypes = [ctypes.POINTER(PrefillParams)]
+        L.mla_prefill_absorbed_num_splits.restype = ctypes.c_int
+        L.mla_prefill_absorbed_workspace_bytes.argtypes = [ctypes.POINTER(PrefillParams)]
+        L.mla_prefill_absorbed_workspace_bytes.restype = sz
+        L.mla_prefill_absorbed.argtypes = [ctypes.POINTER(PrefillParams), vp, vp, vp, vp, vp, vp,
+                                           vp, vp, vp, sz, vp]
+        L.mla_prefill_absorbed.restype = ctypes.c_int
         L.mla_cache_append.argtypes = [ctypes.POINTER(AppendParams), vp, vp, vp, vp, vp, vp, vp]
         L.mla_cache_append.restype = ctypes.c_int
         L.mla_kv_cache_bytes.argtypes = [ctypes.c_int64] * 6
@@ -147,7 +159,7 @@ def _cache_strides(cache: torch.Tensor, width: int, what: str):
 
 
 def decode_params(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, *, softmax_scale=None,
-                  out_dtype=None, num_splits=0) -> DecodeParams:
+                  out_dtype=None, num_splits=0, q_rope_base=None) -> DecodeParams:
     B, H, dn = q_nope.shape
     dr = q_rope.shape[-1]
     dc = w_uk.shape[2]
@@ -160,7 +172,8 @@ def decode_params(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, *, softmax_s
         softmax_scale=0.0 if softmax_scale is None else float(softmax_scale),
         dtype=_dtype_code(q_nope.dtype),
         out_dtype=_dtype_code(out_dtype if out_dtype is not None else q_nope.dtype),
-        num_splits=int(num_splits))
+        num_splits=int(num_splits),
+        q_rope_base=0.0 if q_rope_base is None else float(q_rope_base))
 
 
 def decode_num_splits(params: DecodeParams) -> int:
@@ -186,16 +199,18 @@ def absorb_q(q_nope: torch.Tensor, w_uk: torch.Tensor, out: torch.Tensor | None 
 
 
 def decode(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, out=None,
-           workspace=None, softmax_scale=None, out_dtype=None, num_splits=0, stream=None,
-           params: DecodeParams | None = None, events=None):
+           workspace=None, softmax_scale=None, out_dtype=None, num_splits=0, q_rope_base=None,
+           stream=None, params: DecodeParams | None = None, events=None):
     """Absorbed MLA decode (``mla_decode``).  Shapes as in include/mla.h;
     caches are [B, N_max, width] views (they may share one buffer).
+    ``q_rope_base``: None if q_rope arrives rotated, else the rotary base with
+    which the library rotates it at position seqlens[b] - 1.
     ``events``: optional ctypes array of 4 hipEvent_t handles, recorded around
     the three kernels (``mla_decode_profiled``)."""
     if params is None:
         params = decode_params(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache,
                                softmax_scale=softmax_scale, out_dtype=out_dtype,
-                               num_splits=num_splits)
+                               num_splits=num_splits, q_rope_base=q_rope_base)
     if out is None:
         odt = torch.float32 if params.out_dtype == MLA_F32 else torch.bfloat16
         out = torch.empty((params.batch, params.heads, params.d_v), dtype=odt,
@@ -220,7 +235,7 @@ def decode(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, out=Non
 
 
 def prefill_params(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, *, softmax_scale=None,
-                   out_dtype=None) -> PrefillParams:
+                   out_dtype=None, num_splits=0, q_rope_base=None) -> PrefillParams:
     B, T, H, dn = q_nope.shape
     dr = q_rope.shape[-1]
     dc = w_uk.shape[2]
@@ -232,7 +247,9 @@ def prefill_params(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, *, softmax_
         ckv_stride_b=csb, ckv_stride_n=csn, kpe_stride_b=ksb, kpe_stride_n=ksn,
         softmax_scale=0.0 if softmax_scale is None else float(softmax_scale),
         dtype=_dtype_code(q_nope.dtype),
-        out_dtype=_dtype_code(out_dtype if out_dtype is not None else q_nope.dtype), reserved=0)
+        out_dtype=_dtype_code(out_dtype if out_dtype is not None else q_nope.dtype),
+        num_splits=int(num_splits),
+        q_rope_base=0.0 if q_rope_base is None else float(q_rope_base))
 
 
 def prefill_workspace_bytes(params: PrefillParams) -> int:
@@ -240,12 +257,13 @@ def prefill_workspace_bytes(params: PrefillParams) -> int:
 
 
 def prefill_naive(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, out=None,
-                  workspace=None, softmax_scale=None, out_dtype=None, stream=None,
-                  params: PrefillParams | None = None):
+                  workspace=None, softmax_scale=None, out_dtype=None, q_rope_base=None,
+                  stream=None, params: PrefillParams | None = None):
     """Naive causal prefill (``mla_prefill_naive``): q [B,T,H,*] -> out [B,T,H,d_v]."""
     if params is None:
         params = prefill_params(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache,
-                                softmax_scale=softmax_scale, out_dtype=out_dtype)
+                                softmax_scale=softmax_scale, out_dtype=out_dtype,
+                                q_rope_base=q_rope_base)
     if out is None:
         odt = torch.float32 if params.out_dtype == MLA_F32 else torch.bfloat16
         out = torch.empty((params.batch, params.tokens, params.heads, params.d_v), dtype=odt,
@@ -260,6 +278,40 @@ def prefill_naive(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, 
                                    _ptr(w_uv), _ptr(ckv_cache), _ptr(kpe_cache), _ptr(seqlens),
                                    _ptr(out), _ptr(workspace), workspace.numel(),
                                    _stream(stream)))
+    return out
+
+
+def prefill_absorbed_num_splits(params: PrefillParams) -> int:
+    return int(lib().mla_prefill_absorbed_num_splits(ctypes.byref(params)))
+
+
+def prefill_absorbed_workspace_bytes(params: PrefillParams) -> int:
+    return int(lib().mla_prefill_absorbed_workspace_bytes(ctypes.byref(params)))
+
+
+def prefill_absorbed(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, out=None,
+                     workspace=None, softmax_scale=None, out_dtype=None, num_splits=0,
+                     q_rope_base=None, stream=None, params: PrefillParams | None = None):
+    """Absorbed causal prefill (``mla_prefill_absorbed``): q [B,T,H,*] ->
+    out [B,T,H,d_v], each query attending to its causal prefix in latent space."""
+    if params is None:
+        params = prefill_params(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache,
+                                softmax_scale=softmax_scale, out_dtype=out_dtype,
+                                num_splits=num_splits, q_rope_base=q_rope_base)
+    if out is None:
+        odt = torch.float32 if params.out_dtype == MLA_F32 else torch.bfloat16
+        out = torch.empty((params.batch, params.tokens, params.heads, params.d_v), dtype=odt,
+                          device=q_nope.device)
+    need = prefill_absorbed_workspace_bytes(params)
+    if need == 0:
+        _check(lib().mla_prefill_absorbed(ctypes.byref(params), None, None, None, None, None,
+                                          None, None, None, None, 0, None))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
+    _check(lib().mla_prefill_absorbed(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope),
+                                      _ptr(w_uk), _ptr(w_uv), _ptr(ckv_cache), _ptr(kpe_cache),
+                                      _ptr(seqlens), _ptr(out), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)))
     return out
 
 

@@ -173,7 +173,7 @@ constexpr float kRefSlack = 64.0f;              // log2 headroom above the refer
 constexpr int kLook = MLA_DECODE_LOOKAHEAD;
 
 __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
-    int H, int S, int64_t n_max, const uint16_t *__restrict__ ckv, int64_t ckv_sb, int ckv_rowb,
+    int T, int H, int S, int64_t n_max, const uint16_t *__restrict__ ckv, int64_t ckv_sb, int ckv_rowb,
     const uint16_t *__restrict__ kpe, int64_t kpe_sb, int kpe_rowb,
     const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ qa, float c2,
     float *__restrict__ part_o, float *__restrict__ part_ml)
@@ -181,17 +181,20 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) unsigned char tiles[3 * kTileBytes];
     __shared__ __attribute__((aligned(16))) unsigned char qrope_lds[4 * kQRopeBytes];
 
-    const int sp = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+    // Query row v = b * T + t: query t of sequence b (T = 1 for decode)
+    // attends to the causal prefix of its sequence's cache.
+    const int sp = blockIdx.x, hg = blockIdx.y, v = blockIdx.z;
+    const int b = v / T, tq = v - b * T;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int half = lane >> 5, l32 = lane & 31;
     const int hq = hg * 128 + w * 32 + l32;  // this lane's head (score column)
 
-    const int L = static_cast<int>(min<int64_t>(max(seqlens[b], 0), n_max));
+    const int L = query_len(seqlens[b], n_max, T, tq);
     const int ntiles_seq = (L + kTile - 1) / kTile;
     const int tps = (ntiles_seq + S - 1) / S;
     const int start = sp * tps * kTile;
     const int end = min(L, start + tps * kTile);
-    const int64_t prow = (static_cast<int64_t>(b) * S + sp) * H + hq;
+    const int64_t prow = (static_cast<int64_t>(v) * S + sp) * H + hq;
 
     if (start >= end) {  // empty split: weight zero in the merge, O never read
         if (half == 0) {
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     // B[k][j = head], lane holds k = 16 s + 8 half + 0..7.  Latent channels
     // (s < 32) in registers; RoPE channels (s = 32..35) in this wave's LDS
     // slice (head row l32 at a 144-byte stride).
-    const uint16_t *qrow = qa + (static_cast<int64_t>(b) * H + hq) * DQK + 8 * half;
+    const uint16_t *qrow = qa + (static_cast<int64_t>(v) * H + hq) * DQK + 8 * half;
     u32x4 qreg[DC / 16];
 #pragma unroll
     for (int s = 0; s < DC / 16; ++s) qreg[s] = *reinterpret_cast<const u32x4 *>(qrow + 16 * s);
@@ -378,7 +381,8 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// 3. merge + up-project: grid (H, B), 256 threads, one (head, sequence) each.
+// 3. merge + up-project: grid (H, B * T), 256 threads, one (head, query row)
+//    each.
 //    M = max_s m_s, w_s = 2^(m_s - M), o_lat = sum_s w_s O_s / sum_s w_s l_s,
 //    every sum in a fixed order (bitwise repeatable), then out = W_UV[h] o_lat.
 //    A split marked with a NaN maximum (its weights could have overflowed) is
@@ -390,13 +394,14 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
 constexpr int kMergeLoads = 8;  // partial pieces per thread in flight
 
 struct CacheView {
+    int T;                   // query tokens per sequence (1 for decode)
     int64_t n_max;
     const uint16_t *ckv;
     int64_t ckv_sb, ckv_sn;  // elements
     const uint16_t *kpe;
     int64_t kpe_sb, kpe_sn;
     const int32_t *seqlens;
-    const uint16_t *qa;      // [B][H][576] absorbed queries (bf16)
+    const uint16_t *qa;      // [B * T][H][576] absorbed queries (bf16)
     float c2;                // softmax scale * log2(e)
 };
 
@@ -414,21 +419,22 @@ __device__ float block_reduce(float v, float *red, bool is_max)
     return r;
 }
 
-// Recompute one (sequence, split, head) partial: scores against the split's
+// Recompute one (query row, split, head) partial: scores against the split's
 // rows, their maximum, then weights, mass and the weighted latent sum.
-__device__ void recompute_partial(const CacheView &cv, int H, int S, int b, int sp, int h,
+__device__ void recompute_partial(const CacheView &cv, int H, int S, int v, int sp, int h,
                                   float *part_o, float *part_ml)
 {
     __shared__ float q[DQK];
     __shared__ float pw[256];
     __shared__ float red[4];
     const int tid = threadIdx.x;
-    const int L = static_cast<int>(min<int64_t>(max(cv.seqlens[b], 0), cv.n_max));
+    const int b = v / cv.T;
+    const int L = query_len(cv.seqlens[b], cv.n_max, cv.T, v - b * cv.T);
     const int ntiles_seq = (L + kSplitGranule - 1) / kSplitGranule;
     const int tps = (ntiles_seq + S - 1) / S;
     const int start = sp * tps * kSplitGranule;
     const int end = min(L, start + tps * kSplitGranule);
-    const uint16_t *qrow = cv.qa + (static_cast<int64_t>(b) * H + h) * DQK;
+    const uint16_t *qrow = cv.qa + (static_cast<int64_t>(v) * H + h) * DQK;
     for (int k = tid; k < DQK; k += 256) q[k] = bf16lo(qrow[k]);
     __syncthreads();
     auto score = [&](int n) {
@@ -457,7 +463,7 @@ __device__ void recompute_partial(const CacheView &cv, int H, int S, int b, int 
         }
         __syncthreads();
     }
-    const int64_t prow = (static_cast<int64_t>(b) * S + sp) * H + h;
+    const int64_t prow = (static_cast<int64_t>(v) * S + sp) * H + h;
     part_o[prow * DC + 2 * tid] = o0;
     part_o[prow * DC + 2 * tid + 1] = o1;
     if (tid == 0) {
@@ -474,7 +480,7 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
                                                                 void *__restrict__ out, int out_bf16,
                                                                 CacheView cv)
 {
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int h = blockIdx.x, v = blockIdx.y, tid = threadIdx.x;  // v: query row
     const int lane = tid & 63, wv_id = tid >> 6;
     __shared__ float wt[kMaxSplits];      // split weights 2^(m_s - M), 0 for empty splits
     __shared__ float red[4];
@@ -485,7 +491,7 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
     // Every load is issued up front, in the order the data is needed, so the
     // whole merge costs one memory round trip: (m, l) of split tid, then this
     // thread's first 16 partial pieces, then its W_UV pieces.
-    const int64_t base = static_cast<int64_t>(b) * S * H + h;  // row of split 0
+    const int64_t base = static_cast<int64_t>(v) * S * H + h;  // row of split 0
     // Loads are unconditional (indices past the last split are clamped) so
     // that no branch makes the compiler wait on them early; the surplus values
     // are discarded by selects.
@@ -526,7 +532,7 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
     if (any_nan) {
         for (int sp = 0; sp < S; ++sp)
             if (__builtin_isnan(part_ml[(base + static_cast<int64_t>(sp) * H) * 2]))
-                recompute_partial(cv, H, S, b, sp, h, part_o, part_ml);
+                recompute_partial(cv, H, S, v, sp, h, part_o, part_ml);
         if (tid < S) {
             ms = part_ml[(base + static_cast<int64_t>(tid) * H) * 2];
             ls = part_ml[(base + static_cast<int64_t>(tid) * H) * 2 + 1];
@@ -585,8 +591,8 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
         a += __shfl_xor(a, 2);
         a += __shfl_xor(a, 4);
         if (p8 == 0) {
-            const int v = 32 * wv_id + 8 * j + r8;
-            const int64_t oi = (static_cast<int64_t>(b) * H + h) * DV + v;
+            const int vr = 32 * wv_id + 8 * j + r8;  // output row of W_UV
+            const int64_t oi = (static_cast<int64_t>(v) * H + h) * DV + vr;
             if (out_bf16)
                 reinterpret_cast<__bf16 *>(out)[oi] = static_cast<__bf16>(a);
             else
@@ -605,10 +611,17 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
                               const DecodeWorkspace &ws, hipStream_t st, hipEvent_t const *events)
 {
     uint16_t *qa = static_cast<uint16_t *>(ws.q);
+    const int rows = s.B * s.T;  // query rows
     if (events) (void)hipEventRecord(events[0], st);
+    if (s.q_rope_base > 0.0) {   // rotate the queries' RoPE channels at their positions
+        hipError_t e = launch_rope_q(s.B, s.T, s.H, DR, s.n_max, s.q_rope_base, true, seqlens,
+                                     q_rope, ws.q_rope, st);
+        if (e != hipSuccess) return e;
+        q_rope = ws.q_rope;
+    }
     {
-        dim3 grid(4, s.H, (s.B + kAbsorbBatch - 1) / kAbsorbBatch);
-        absorb_bf16_kernel<<<grid, 256, 0, st>>>(s.B, s.H, static_cast<const uint16_t *>(q_nope),
+        dim3 grid(4, s.H, (rows + kAbsorbBatch - 1) / kAbsorbBatch);
+        absorb_bf16_kernel<<<grid, 256, 0, st>>>(rows, s.H, static_cast<const uint16_t *>(q_nope),
                                                  static_cast<const uint16_t *>(q_rope),
                                                  static_cast<const uint16_t *>(w_uk), qa);
         hipError_t e = hipGetLastError();
@@ -616,17 +629,17 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
     }
     if (events) (void)hipEventRecord(events[1], st);
     {
-        dim3 grid(s.S, s.H / 128, s.B);
+        dim3 grid(s.S, s.H / 128, rows);
         decode_splitkv_bf16_kernel<<<grid, kThreadsDec, 0, st>>>(
-            s.H, s.S, s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb,
+            s.T, s.H, s.S, s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb,
             static_cast<int>(s.ckv_sn * 2), static_cast<const uint16_t *>(kpe), s.kpe_sb,
             static_cast<int>(s.kpe_sn * 2), seqlens, qa, s.scale * kLog2e, ws.part_o, ws.part_ml);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (events) (void)hipEventRecord(events[2], st);
-    dim3 grid(s.H, s.B);
-    CacheView cv{s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb, s.ckv_sn,
+    dim3 grid(s.H, rows);
+    CacheView cv{s.T, s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb, s.ckv_sn,
                  static_cast<const uint16_t *>(kpe), s.kpe_sb, s.kpe_sn, seqlens, qa,
                  s.scale * kLog2e};
     merge_upproj_bf16_kernel<<<grid, 256, 0, st>>>(s.H, s.S, ws.part_o, ws.part_ml,

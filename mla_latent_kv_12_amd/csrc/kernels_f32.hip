@@ -103,7 +103,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
     DecodeShape s, const float *q_abs, const float *q_rope, const float *ckv, const float *kpe,
     const int32_t *seqlens, float *part_o, float *part_ml)
 {
-    const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int sp = blockIdx.x, h = blockIdx.y, v = blockIdx.z;  // v = b * T + t: query row
+    const int b = v / s.T;
     const int tid = threadIdx.x;
     extern __shared__ float sm[];
     float *qa = sm;                 // [dc]
@@ -111,11 +112,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
     float *pt = qr + s.dr;          // [kThreads] scores / probabilities of a tile
     float *red = pt + kThreads;     // [kThreads / 64]
 
-    const int64_t qoff = static_cast<int64_t>(b) * s.H + h;
+    const int64_t qoff = static_cast<int64_t>(v) * s.H + h;
     for (int j = tid; j < s.dc; j += kThreads) qa[j] = q_abs[qoff * s.dc + j];
     for (int r = tid; r < s.dr; r += kThreads) qr[r] = q_rope[qoff * s.dr + r];
 
-    const int L = static_cast<int>(min<int64_t>(max(seqlens[b], 0), s.n_max));
+    const int L = query_len(seqlens[b], s.n_max, s.T, v - b * s.T);
     int start, end;
     split_range(L, s.S, sp, &start, &end);
 
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
         __syncthreads();
     }
 
-    const int64_t prow = (static_cast<int64_t>(b) * s.S + sp) * s.H + h;
+    const int64_t prow = (static_cast<int64_t>(v) * s.S + sp) * s.H + h;
 #pragma unroll
     for (int i = 0; i < kMaxCols; ++i) {
         const int j = tid + i * kThreads;
@@ -175,14 +176,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
 
 }  // namespace
 
-// Fixed-order merge of the S split partials of one (head, sequence) followed
-// by out = W_UV[h] o_lat.  Shared by both decode paths' small shapes.
+// Fixed-order merge of the S split partials of one (head, query row) followed
+// by out = W_UV[h] o_lat.
 template <typename TW>
 __global__ __launch_bounds__(kThreads) void merge_upproj_generic_kernel(
     int H, int S, int dc, int dv, const float *part_o, const float *part_ml, const TW *w_uv,
     void *out, int out_bf16)
 {
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;  // b: query row
     extern __shared__ float sm[];
     float *ol = sm;            // [dc]
     float *wt = ol + dc;       // [S]
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void merge_upproj_generic_kernel(
 hipError_t launch_merge_upproj_generic(const DecodeShape &s, const DecodeWorkspace &ws,
                                        const void *w_uv, bool w_bf16, void *out, hipStream_t st)
 {
-    dim3 grid(s.H, s.B);
+    dim3 grid(s.H, s.B * s.T);
     size_t shm = sizeof(float) * (s.dc + s.S + kThreads / 64);
     if (w_bf16)
         merge_upproj_generic_kernel<uint16_t><<<grid, kThreads, shm, st>>>(
@@ -252,12 +253,20 @@ hipError_t launch_decode_f32(const DecodeShape &s, const float *q_nope, const fl
                              const DecodeWorkspace &ws, hipStream_t st, hipEvent_t const *events)
 {
     float *qabs = static_cast<float *>(ws.q);
+    const int rows = s.B * s.T;  // query rows
     if (events) (void)hipEventRecord(events[0], st);
-    hipError_t e = launch_absorb_f32(s.B, s.H, s.dn, s.dc, false, q_nope, w_uk, qabs, st);
+    hipError_t e;
+    if (s.q_rope_base > 0.0 && s.dr > 0) {  // rotate the queries' RoPE channels at their positions
+        e = launch_rope_q(s.B, s.T, s.H, s.dr, s.n_max, s.q_rope_base, false, seqlens, q_rope,
+                          ws.q_rope, st);
+        if (e != hipSuccess) return e;
+        q_rope = static_cast<const float *>(ws.q_rope);
+    }
+    e = launch_absorb_f32(rows, s.H, s.dn, s.dc, false, q_nope, w_uk, qabs, st);
     if (e != hipSuccess) return e;
     if (events) (void)hipEventRecord(events[1], st);
     {
-        dim3 grid(s.S, s.H, s.B);
+        dim3 grid(s.S, s.H, rows);
         size_t shm = sizeof(float) * (s.dc + s.dr + kThreads + kThreads / 64);
         decode_split_f32_kernel<<<grid, kThreads, shm, st>>>(s, qabs, q_rope, ckv, kpe, seqlens,
                                                              ws.part_o, ws.part_ml);

@@ -58,27 +58,32 @@ bool bf16_dims_ok(int64_t H, int64_t dc, int64_t dr, int64_t dn, int64_t dv)
     return dc == 512 && dr == 64 && dn == 128 && dv == 128 && H % 128 == 0;
 }
 
-int auto_splits(const mla_decode_params *p)
+// rows = query rows (batch for decode, batch * tokens for absorbed prefill).
+int auto_splits(int32_t dtype, int64_t rows, int64_t heads, int64_t n_max)
 {
-    // Enough (sequence, split) blocks to cover the 256 compute units about
+    // Enough (query row, split) blocks to cover the 256 compute units about
     // once, but at least four 32-token tiles of context per split so the
     // split partials stay small next to the cache rows they summarise.
-    const int64_t tiles = (p->n_max + mla::kSplitGranule - 1) / mla::kSplitGranule;
-    int64_t groups;
-    int64_t target;
-    if (p->dtype == MLA_BF16) {
-        groups = p->batch * (p->heads / mla::decode_bf16_heads_per_block((int)p->heads));
-        target = 256;
-    } else {
-        groups = p->batch * p->heads;
-        target = 256;
-    }
+    const int64_t tiles = (n_max + mla::kSplitGranule - 1) / mla::kSplitGranule;
+    const int64_t groups =
+        dtype == MLA_BF16 ? rows * (heads / mla::decode_bf16_heads_per_block((int)heads))
+                          : rows * heads;
+    const int64_t target = 256;
     int64_t s = (target + groups - 1) / groups;
     int64_t cap = tiles / 4;
     if (s > cap) s = cap;
     if (s < 1) s = 1;
     if (s > mla::kMaxSplits) s = mla::kMaxSplits;
     return (int)s;
+}
+
+mla_status check_rope_base(double base, int64_t dr)
+{
+    if (!(base >= 0.0) || isinf(base) || (base > 0.0 && base <= 1.0))
+        return fail(MLA_ERR_INVALID_ARG, "q_rope_base must be 0 (q_rope already rotated) or a finite value > 1");
+    if (base > 0.0 && (dr & 1))
+        return fail(MLA_ERR_UNSUPPORTED, "rotating q_rope needs an even d_r (rotation pairs)");
+    return MLA_OK;
 }
 
 // Structural validation shared by the workspace query and the decode call.
@@ -119,13 +124,14 @@ mla_status check_decode_params(const mla_decode_params *p)
         return fail(MLA_ERR_INVALID_ARG, "num_splits must be in [0, %d]", mla::kMaxSplits);
     if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
         return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
-    return MLA_OK;
+    return check_rope_base(p->q_rope_base, p->d_r);
 }
 
 mla::DecodeShape make_shape(const mla_decode_params *p)
 {
     mla::DecodeShape s;
     s.B = (int)p->batch;
+    s.T = 1;
     s.H = (int)p->heads;
     s.dc = (int)p->d_c;
     s.dr = (int)p->d_r;
@@ -138,8 +144,9 @@ mla::DecodeShape make_shape(const mla_decode_params *p)
     s.kpe_sn = p->kpe_stride_n;
     s.scale = p->softmax_scale > 0.f ? p->softmax_scale
                                      : (float)(1.0 / sqrt((double)(p->d_n + p->d_r)));
-    s.S = p->num_splits > 0 ? p->num_splits : auto_splits(p);
+    s.S = p->num_splits > 0 ? p->num_splits : auto_splits(p->dtype, p->batch, p->heads, p->n_max);
     s.out_bf16 = p->out_dtype == MLA_BF16;
+    s.q_rope_base = p->q_rope_base;
     return s;
 }
 
@@ -164,18 +171,21 @@ namespace mla {
 
 size_t decode_workspace_layout(const DecodeShape &s, bool bf16, DecodeWorkspace *ws, void *base)
 {
-    const size_t rows = (size_t)s.B * s.H;
+    const size_t rows = (size_t)s.B * (size_t)s.T * (size_t)s.H;  // (query row, head) pairs
     const size_t qbytes = bf16 ? rows * (size_t)(s.dc + s.dr) * 2 : rows * (size_t)s.dc * 4;
     const size_t obytes = rows * (size_t)s.S * (size_t)s.dc * 4;
     const size_t mlbytes = rows * (size_t)s.S * 2 * 4;
+    const size_t rbytes = s.q_rope_base > 0.0 ? rows * (size_t)s.dr * (bf16 ? 2 : 4) : 0;
     const size_t off_o = round_up(qbytes, kAlign);
     const size_t off_ml = off_o + round_up(obytes, kAlign);
-    const size_t total = off_ml + round_up(mlbytes, kAlign);
+    const size_t off_r = off_ml + round_up(mlbytes, kAlign);
+    const size_t total = off_r + round_up(rbytes, kAlign);
     if (ws) {
         char *b = static_cast<char *>(base);
         ws->q = b;
         ws->part_o = reinterpret_cast<float *>(b + off_o);
         ws->part_ml = reinterpret_cast<float *>(b + off_ml);
+        ws->q_rope = rbytes ? b + off_r : nullptr;
     }
     return total;
 }
@@ -290,7 +300,6 @@ mla_status check_prefill_params(const mla_prefill_params *p)
         p->d_n < 1 || p->d_v < 1 || p->d_r < 0)
         return fail(MLA_ERR_INVALID_ARG, "non-positive size");
     if (p->tokens > p->n_max) return fail(MLA_ERR_INVALID_ARG, "tokens exceeds n_max");
-    if (p->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "reserved field must be 0");
     if (p->batch > 65535 || p->heads > 65535 || p->tokens > (1 << 24) || p->n_max > (1 << 24))
         return fail(MLA_ERR_UNSUPPORTED, "sizes beyond the supported range");
     if ((p->dtype != MLA_F32 && p->dtype != MLA_BF16) ||
@@ -313,7 +322,59 @@ mla_status check_prefill_params(const mla_prefill_params *p)
         return fail(MLA_ERR_INVALID_ARG, "negative cache stride");
     if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
         return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    return check_rope_base(p->q_rope_base, p->d_r);
+}
+
+mla_status check_prefill_naive_params(const mla_prefill_params *p)
+{
+    mla_status st = check_prefill_params(p);
+    if (st != MLA_OK) return st;
+    if (p->num_splits != 0) return fail(MLA_ERR_INVALID_ARG, "num_splits must be 0 for the naive prefill");
     return MLA_OK;
+}
+
+// The absorbed prefill runs the decode kernels over batch * tokens query
+// rows, so it takes the decode limits on top of the common prefill checks.
+mla_status check_prefill_absorbed_params(const mla_prefill_params *p)
+{
+    mla_status st = check_prefill_params(p);
+    if (st != MLA_OK) return st;
+    if (p->batch * p->tokens > 65535)
+        return fail(MLA_ERR_UNSUPPORTED, "absorbed prefill supports batch * tokens <= 65535");
+    if (p->dtype == MLA_BF16 && !bf16_dims_ok(p->heads, p->d_c, p->d_r, p->d_n, p->d_v))
+        return fail(MLA_ERR_UNSUPPORTED,
+                    "bf16 absorbed prefill supports d_c=512, d_r=64, d_n=d_v=128 and heads %% 128 == 0");
+    if (p->dtype == MLA_BF16 && (p->n_max * p->ckv_stride_n * 2 >= ((int64_t)1 << 32) ||
+                                 p->n_max * p->kpe_stride_n * 2 >= ((int64_t)1 << 32)))
+        return fail(MLA_ERR_UNSUPPORTED, "bf16 absorbed prefill addresses one sequence's cache with 32-bit offsets");
+    if (p->num_splits < 0 || p->num_splits > mla::kMaxSplits)
+        return fail(MLA_ERR_INVALID_ARG, "num_splits must be in [0, %d]", mla::kMaxSplits);
+    return MLA_OK;
+}
+
+// Decode shape of an absorbed prefill: T query rows per sequence.
+mla::DecodeShape make_absorbed_shape(const mla_prefill_params *p)
+{
+    mla::DecodeShape s;
+    s.B = (int)p->batch;
+    s.T = (int)p->tokens;
+    s.H = (int)p->heads;
+    s.dc = (int)p->d_c;
+    s.dr = (int)p->d_r;
+    s.dn = (int)p->d_n;
+    s.dv = (int)p->d_v;
+    s.n_max = p->n_max;
+    s.ckv_sb = p->ckv_stride_b;
+    s.ckv_sn = p->ckv_stride_n;
+    s.kpe_sb = p->kpe_stride_b;
+    s.kpe_sn = p->kpe_stride_n;
+    s.scale = p->softmax_scale > 0.f ? p->softmax_scale
+                                     : (float)(1.0 / sqrt((double)(p->d_n + p->d_r)));
+    s.S = p->num_splits > 0 ? p->num_splits
+                            : auto_splits(p->dtype, p->batch * p->tokens, p->heads, p->n_max);
+    s.out_bf16 = p->out_dtype == MLA_BF16;
+    s.q_rope_base = p->q_rope_base;
+    return s;
 }
 
 mla::PrefillShape make_pshape(const mla_prefill_params *p)
@@ -334,6 +395,7 @@ mla::PrefillShape make_pshape(const mla_prefill_params *p)
     s.scale = p->softmax_scale > 0.f ? p->softmax_scale
                                      : (float)(1.0 / sqrt((double)(p->d_n + p->d_r)));
     s.out_bf16 = p->out_dtype == MLA_BF16;
+    s.q_rope_base = p->q_rope_base;
     return s;
 }
 
@@ -342,15 +404,19 @@ mla::PrefillShape make_pshape(const mla_prefill_params *p)
 namespace mla {
 
 size_t prefill_workspace_layout(const PrefillShape &s, bool bf16, void *base, void **k_out,
-                                void **v_out)
+                                void **v_out, void **qr_out)
 {
     const size_t elt = bf16 ? 2 : 4;
     const size_t rows = (size_t)s.B * (size_t)s.n_max * (size_t)s.H;
     const size_t kb = round_up(rows * (size_t)s.dn * elt, kAlign);
     const size_t vb = round_up(rows * (size_t)s.dv * elt, kAlign);
+    const size_t rb = s.q_rope_base > 0.0
+                          ? round_up((size_t)s.B * (size_t)s.T * (size_t)s.H * (size_t)s.dr * elt, kAlign)
+                          : 0;
     if (k_out) *k_out = base;
     if (v_out) *v_out = static_cast<char *>(base) + kb;
-    return kb + vb;
+    if (qr_out) *qr_out = rb ? static_cast<char *>(base) + kb + vb : nullptr;
+    return kb + vb + rb;
 }
 
 }  // namespace mla
@@ -359,9 +425,10 @@ extern "C" {
 
 size_t mla_prefill_workspace_bytes(const mla_prefill_params *p)
 {
-    if (check_prefill_params(p) != MLA_OK) return 0;
+    if (check_prefill_naive_params(p) != MLA_OK) return 0;
     mla::PrefillShape s = make_pshape(p);
-    return mla::prefill_workspace_layout(s, p->dtype == MLA_BF16, nullptr, nullptr, nullptr);
+    return mla::prefill_workspace_layout(s, p->dtype == MLA_BF16, nullptr, nullptr, nullptr,
+                                         nullptr);
 }
 
 mla_status mla_prefill_naive(const mla_prefill_params *p, const void *q_nope, const void *q_rope,
@@ -369,7 +436,7 @@ mla_status mla_prefill_naive(const mla_prefill_params *p, const void *q_nope, co
                              const void *kpe_cache, const int32_t *seqlens, void *out,
                              void *workspace, size_t workspace_bytes, void *stream)
 {
-    mla_status st = check_prefill_params(p);
+    mla_status st = check_prefill_naive_params(p);
     if (st != MLA_OK) return st;
     if (!q_nope || !w_uk || !w_uv || !ckv_cache || !seqlens || !out)
         return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
@@ -384,8 +451,8 @@ mla_status mla_prefill_naive(const mla_prefill_params *p, const void *q_nope, co
                  p->kpe_stride_b % 8))
         return fail(MLA_ERR_INVALID_ARG, "bf16 cache strides must be multiples of 8 elements");
     mla::PrefillShape s = make_pshape(p);
-    void *kbuf = nullptr, *vbuf = nullptr;
-    const size_t need = mla::prefill_workspace_layout(s, bf16, workspace, &kbuf, &vbuf);
+    void *kbuf = nullptr, *vbuf = nullptr, *qrbuf = nullptr;
+    const size_t need = mla::prefill_workspace_layout(s, bf16, workspace, &kbuf, &vbuf, &qrbuf);
     if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign))
         return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu)",
                     need, workspace_bytes);
@@ -395,6 +462,12 @@ mla_status mla_prefill_naive(const mla_prefill_params *p, const void *q_nope, co
         if (st != MLA_OK) return st;
     }
     hipError_t e;
+    if (qrbuf && p->d_r > 0) {  // rotate the queries' RoPE channels at their positions first
+        e = mla::launch_rope_q(s.B, s.T, s.H, s.dr, s.n_max, s.q_rope_base, bf16, seqlens, q_rope,
+                               qrbuf, hs);
+        if (e != hipSuccess) return fail(MLA_ERR_HIP, "rope launch failed: %s", hipGetErrorString(e));
+        q_rope = qrbuf;
+    }
     if (bf16)
         e = mla::launch_prefill_bf16(s, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens,
                                      out, kbuf, vbuf, hs);
@@ -404,6 +477,70 @@ mla_status mla_prefill_naive(const mla_prefill_params *p, const void *q_nope, co
                                     static_cast<const float *>(w_uv), static_cast<const float *>(ckv_cache),
                                     static_cast<const float *>(kpe_cache), seqlens, out, kbuf, vbuf, hs);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int mla_prefill_absorbed_num_splits(const mla_prefill_params *p)
+{
+    if (check_prefill_absorbed_params(p) != MLA_OK) return 0;
+    return make_absorbed_shape(p).S;
+}
+
+size_t mla_prefill_absorbed_workspace_bytes(const mla_prefill_params *p)
+{
+    if (check_prefill_absorbed_params(p) != MLA_OK) return 0;
+    return mla::decode_workspace_layout(make_absorbed_shape(p), p->dtype == MLA_BF16, nullptr,
+                                        nullptr);
+}
+
+mla_status mla_prefill_absorbed(const mla_prefill_params *p, const void *q_nope,
+                                const void *q_rope, const void *w_uk, const void *w_uv,
+                                const void *ckv_cache, const void *kpe_cache,
+                                const int32_t *seqlens, void *out, void *workspace,
+                                size_t workspace_bytes, void *stream)
+{
+    mla_status st = check_prefill_absorbed_params(p);
+    if (st != MLA_OK) return st;
+    if (!q_nope || !w_uk || !w_uv || !ckv_cache || !seqlens || !out)
+        return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (p->d_r > 0 && (!q_rope || !kpe_cache))
+        return fail(MLA_ERR_INVALID_ARG, "NULL q_rope or kpe_cache with d_r > 0");
+    const bool bf16 = p->dtype == MLA_BF16;
+    if (bf16) {
+        if (!aligned(ckv_cache, 16) || !aligned(kpe_cache, 16) || p->ckv_stride_n % 8 ||
+            p->kpe_stride_n % 8 || p->ckv_stride_b % 8 || p->kpe_stride_b % 8)
+            return fail(MLA_ERR_INVALID_ARG,
+                        "bf16 caches need 16-byte aligned rows (pointers %% 16, strides %% 8 elements)");
+        if (!aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(w_uk, 16) ||
+            !aligned(w_uv, 16) || !aligned(out, 16))
+            return fail(MLA_ERR_INVALID_ARG, "bf16 path needs 16-byte aligned q, weights and out");
+    } else {
+        if (!aligned(q_nope, 4) || (q_rope && !aligned(q_rope, 4)) || !aligned(w_uk, 4) ||
+            !aligned(w_uv, 4) || !aligned(ckv_cache, 4) || (kpe_cache && !aligned(kpe_cache, 4)) ||
+            !aligned(out, 4))
+            return fail(MLA_ERR_INVALID_ARG, "fp32 tensors must be 4-byte aligned");
+    }
+    mla::DecodeShape s = make_absorbed_shape(p);
+    mla::DecodeWorkspace ws;
+    const size_t need = mla::decode_workspace_layout(s, bf16, &ws, workspace);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign))
+        return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu at %p)",
+                    need, workspace_bytes, workspace);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (debug_checks()) {
+        st = check_seqlens_debug(seqlens, p->batch, p->n_max, hs, p->tokens);
+        if (st != MLA_OK) return st;
+    }
+    hipError_t e;
+    if (bf16)
+        e = mla::launch_decode_bf16(s, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens,
+                                    out, ws, hs, nullptr);
+    else
+        e = mla::launch_decode_f32(s, static_cast<const float *>(q_nope),
+                                   static_cast<const float *>(q_rope), static_cast<const float *>(w_uk),
+                                   static_cast<const float *>(w_uv), static_cast<const float *>(ckv_cache),
+                                   static_cast<const float *>(kpe_cache), seqlens, out, ws, hs, nullptr);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "absorbed prefill launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 
@@ -482,6 +619,6 @@ const char *mla_status_string(mla_status s)
 
 const char *mla_last_error(void) { return g_err; }
 
-int mla_version(void) { return 10000; }
+int mla_version(void) { return 10100; }
 
 }  // extern "C"

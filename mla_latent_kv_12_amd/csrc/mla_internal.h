@@ -13,25 +13,41 @@ namespace mla {
 constexpr int kSplitGranule = 32;
 constexpr int kMaxSplits = 256;
 
+// A decode call, or an absorbed prefill of T query tokens per sequence.  The
+// kernels see B * T query rows ("virtual sequences" v = b * T + t); row v
+// reads the cache of sequence b = v / T and attends to its first
+// clamp(L_b) - (T - 1 - t) rows (the causal prefix of query t).  T = 1 is
+// plain decode.
 struct DecodeShape {
-    int B, H, dc, dr, dn, dv;
+    int B, T, H, dc, dr, dn, dv;
     int64_t n_max;
     int64_t ckv_sb, ckv_sn, kpe_sb, kpe_sn;
-    float scale;     // softmax scale (natural-log units)
-    int S;           // context splits per sequence
-    int out_bf16;    // output stored as bf16 (else fp32)
+    float scale;         // softmax scale (natural-log units)
+    int S;               // context splits per query row
+    int out_bf16;        // output stored as bf16 (else fp32)
+    double q_rope_base;  // > 0: rotate q_rope at each query's position first
 };
 
 // Workspace carving, identical for the fp32 and bf16 paths except for the
-// query buffer's element type and width.
+// query buffer's element type and width.  Rows are the B * T query rows.
 struct DecodeWorkspace {
-    void *q;          // bf16 path: [B][H][dc+dr] bf16 pre-absorbed query; fp32: [B][H][dc] fp32
-    float *part_o;    // [B][S][H][dc]   un-normalised latent accumulators per split
-    float *part_ml;   // [B][S][H][2]    running max (log2 units) and softmax mass per split
+    void *q;          // bf16 path: [rows][H][dc+dr] bf16 pre-absorbed query; fp32: [rows][H][dc] fp32
+    float *part_o;    // [rows][S][H][dc]   un-normalised latent accumulators per split
+    float *part_ml;   // [rows][S][H][2]    running max (log2 units) and softmax mass per split
+    void *q_rope;     // [rows][H][dr] q_rope rotated at its position (storage dtype)
 };
 
 size_t decode_workspace_layout(const DecodeShape &s, bool bf16, DecodeWorkspace *ws_or_null,
                                void *base);
+
+// Rows visible to query t of a sequence with `seqlen` cached rows (clamped to
+// [0, n_max]) when its T queries are the last T rows: the causal prefix up to
+// and including the query's own row, L - (T - 1 - t), or none.
+__device__ __forceinline__ int query_len(int32_t seqlen, int64_t n_max, int T, int t)
+{
+    const int L = static_cast<int>(min<int64_t>(max(seqlen, 0), n_max));
+    return max(L - (T - 1 - t), 0);
+}
 
 // fp32 path (any supported small shape)
 hipError_t launch_absorb_f32(int B, int H, int dn, int dc, bool in_bf16, const void *q_nope,
@@ -62,9 +78,18 @@ struct PrefillShape {
     int64_t ckv_sb, ckv_sn, kpe_sb, kpe_sn;
     float scale;
     int out_bf16;
+    double q_rope_base;  // > 0: rotate q_rope at each query's position first
 };
+// K, V and (when rotating) the rotated q_rope [B][T][H][dr] in the workspace.
 size_t prefill_workspace_layout(const PrefillShape &s, bool bf16, void *base, void **k_out,
-                                void **v_out);
+                                void **v_out, void **qr_out);
+
+// Rotary embedding of the queries: out[v][h] = RoPE_p(q_rope[v][h]) for the
+// rows = B * T query rows v = b * T + t at position p = clamp(L_b) - T + t,
+// pairs (2i, 2i+1) turned by p * base^(-2i/dr) in fp64 and rounded to the
+// storage type; rows with p < 0 are copied unrotated.
+hipError_t launch_rope_q(int B, int T, int H, int dr, int64_t n_max, double base, bool bf16,
+                         const int32_t *seqlens, const void *q_rope, void *out, hipStream_t st);
 hipError_t launch_prefill_f32(const PrefillShape &s, const float *q_nope, const float *q_rope,
                               const float *w_uk, const float *w_uv, const float *ckv,
                               const float *kpe, const int32_t *seqlens, void *out, void *kbuf,

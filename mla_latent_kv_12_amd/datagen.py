@@ -18,6 +18,11 @@ in float32, scaled where a standard deviation is given):
            ~ N(0,1).  Queries' RoPE channels and k^R are taken as already
            rotated: a rotation maps i.i.d. standard normals to i.i.d. standard
            normals, so the rotated values are drawn directly.
+  chunk:   (a chunk of T new queries over a cached context, for the absorbed
+           prefill) q_nope [B,T,H,dn], q_rope [B,T,H,dr], W_UK, W_UV as for
+           decode, the cache rows [B,Nmax,dc+dr] ~ N(0,1) sequence by
+           sequence, then (ragged workloads only) the lengths uniform in
+           [T, Nmax].
 """
 from __future__ import annotations
 
@@ -85,8 +90,8 @@ class PrefillCase:
     q_rope: np.ndarray    # [B,T,H,dr]
     w_uk: np.ndarray
     w_uv: np.ndarray
-    cache: np.ndarray     # [B,T,dc+dr]
-    seqlens: np.ndarray   # int32 [B] (== T: the prompt is the whole cache)
+    cache: np.ndarray     # [B,N,dc+dr] (N = T for a whole prompt)
+    seqlens: np.ndarray   # int32 [B]; the T queries are the last T of L_b rows
 
     @property
     def ckv(self) -> np.ndarray:
@@ -158,6 +163,29 @@ def make_prefill_case(*, B, T, H, dc, dr, dn, dv, d_model, dtype="bf16", seed=SE
                        w_uk, w_uv, cache, np.full(B, T, dtype=np.int32))
 
 
+def make_chunk_case(*, B, T, H, dc, dr, dn, dv, n_max, dtype="bf16", seed=SEED_BASE,
+                    seqlens=None, ragged=False, scale=None, name="custom"):
+    """T new queries per sequence over a cached context of up to n_max rows
+    (the queries are the last T of the L_b cached rows).  ``seqlens`` None ->
+    every sequence full (n_max) unless ``ragged`` (uniform in [T, n_max])."""
+    rng = np.random.default_rng(seed)
+    w_std = 1.0 / math.sqrt(dc)
+    q_nope = _store(_normal(rng, (B, T, H, dn)), dtype)
+    q_rope = _store(_normal(rng, (B, T, H, dr)), dtype)
+    w_uk = _store(_normal(rng, (H, dn, dc), w_std), dtype)
+    w_uv = _store(_normal(rng, (H, dv, dc), w_std), dtype)
+    width = dc + dr
+    cache = np.empty((B, n_max, width), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    for b in range(B):
+        cache[b] = _store(_normal(rng, (n_max, width)), dtype)
+    if seqlens is None:
+        seqlens = rng.integers(T, n_max + 1, size=B) if ragged else np.full(B, n_max)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dn + dr)
+    return PrefillCase(name, dtype, B, T, H, dc, dr, dn, dv, float(scale), q_nope, q_rope,
+                       w_uk, w_uv, cache, np.asarray(seqlens, dtype=np.int32))
+
+
 @dataclasses.dataclass
 class AppendCase:
     """One new token per sequence: hidden states and the two producer weights."""
@@ -200,6 +228,9 @@ WORKLOADS = {
     "v3-prefill-4k": ("prefill", 4, dict(name="V3 bf16 causal prefill B1 T4096", dtype="bf16",
                                          B=1, T=4096, H=128, dc=512, dr=64, dn=128, dv=128,
                                          d_model=7168)),
+    "v3-chunk-32k": ("chunk", 6, dict(name="V3 bf16 absorbed prefill B4 T64 over L32768",
+                                      dtype="bf16", B=4, T=64, H=128, dc=512, dr=64, dn=128,
+                                      dv=128, n_max=32768)),
 }
 
 
@@ -210,4 +241,6 @@ def make_workload(name: str, seed: int | None = None):
         return make_decode_case(seed=seed, **kw)
     if kind == "append":
         return make_append_case(seed=seed, **kw)
+    if kind == "chunk":
+        return make_chunk_case(seed=seed, **kw)
     return make_prefill_case(seed=seed, **kw)

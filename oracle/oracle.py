@@ -245,12 +245,16 @@ def prefill_absorbed(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, rows)
 
 
 def rope(x, pos, base=10000.0):
-    """Rotary embedding of the d_r-vector x at position pos (fp64)."""
+    """Rotary embedding at position pos (fp64) of every d_r-vector along the
+    last axis of x (x may hold several vectors, e.g. one per head)."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     out = np.empty_like(x)
-    if x.shape[-1] % 2:
+    dr = x.shape[-1]
+    if dr % 2:
         raise OracleError("rotary width must be even")
-    _load().oracle_rope(x.shape[-1], _ptr(x), float(pos), float(base), _ptr(out))
+    xs, os_ = x.reshape(-1, dr), out.reshape(-1, dr)
+    for i in range(xs.shape[0]):
+        _load().oracle_rope(dr, _ptr(xs[i]), float(pos), float(base), _ptr(os_[i]))
     return out
 
 

@@ -34,9 +34,11 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layouts_match_header():
-    # field order and C sizes (int64 x 11, float, int32 x 3 -> 104 bytes)
-    assert ctypes.sizeof(binding.DecodeParams) == 104
-    assert ctypes.sizeof(binding.PrefillParams) == 12 * 8 + 4 * 4
+    # field order and C sizes: int64 x 11, float, int32 x 3, double
+    assert ctypes.sizeof(binding.DecodeParams) == 11 * 8 + 4 * 4 + 8
+    assert binding.DecodeParams.q_rope_base.offset == 104
+    assert ctypes.sizeof(binding.PrefillParams) == 12 * 8 + 4 * 4 + 8
+    assert binding.PrefillParams.q_rope_base.offset == 112
     assert ctypes.sizeof(binding.AppendParams) == 9 * 8 + 8 + 2 * 4   # + double rope_base
 
 
@@ -75,6 +77,9 @@ def test_decode_workspace_size():
     ml = 8 * 32 * 128 * 2 * 4
     rnd = lambda x: (x + 255) // 256 * 256
     assert ws == rnd(q) + rnd(o) + rnd(ml)
+    # rotating q_rope in the library adds room for the rotated copy
+    assert mla.decode_workspace_bytes(_v3_params(num_splits=32, q_rope_base=10000.0)) == \
+        ws + rnd(8 * 128 * 64 * 2)
     assert mla.decode_workspace_bytes(_v3_params()) > 0            # auto split count
     assert mla.decode_workspace_bytes(_v3_params(d_c=256)) == 0    # unsupported -> 0
     assert mla.decode_workspace_bytes(_v3_params(batch=0)) == 0
@@ -108,6 +113,9 @@ def _msg():
     (dict(num_splits=-1), mla.MLA_ERR_INVALID_ARG),
     (dict(num_splits=100000), mla.MLA_ERR_INVALID_ARG),
     (dict(softmax_scale=float("nan")), mla.MLA_ERR_INVALID_ARG),
+    (dict(q_rope_base=1.0), mla.MLA_ERR_INVALID_ARG),
+    (dict(q_rope_base=-2.0), mla.MLA_ERR_INVALID_ARG),
+    (dict(q_rope_base=float("inf")), mla.MLA_ERR_INVALID_ARG),
     (dict(ckv_stride_n=580, kpe_stride_n=580, ckv_stride_b=131072 * 580,
           kpe_stride_b=131072 * 580), mla.MLA_ERR_INVALID_ARG),  # rows not 16-byte aligned
 ])
@@ -151,7 +159,7 @@ def _prefill_params(**kw):
     base = dict(batch=1, tokens=4096, heads=128, d_c=512, d_r=64, d_n=128, d_v=128, n_max=4096,
                 ckv_stride_b=4096 * 576, ckv_stride_n=576, kpe_stride_b=4096 * 576,
                 kpe_stride_n=576, softmax_scale=0.0, dtype=mla.MLA_BF16, out_dtype=mla.MLA_BF16,
-                reserved=0)
+                num_splits=0, q_rope_base=0.0)
     base.update(kw)
     return binding.PrefillParams(**base)
 
@@ -159,8 +167,11 @@ def _prefill_params(**kw):
 def test_prefill_workspace_and_validation():
     p = _prefill_params()
     assert mla.prefill_workspace_bytes(p) == 2 * 4096 * 128 * 128 * 2
+    assert mla.prefill_workspace_bytes(_prefill_params(q_rope_base=10000.0)) == \
+        2 * 4096 * 128 * 128 * 2 + 4096 * 128 * 64 * 2                # + rotated q_rope
     assert mla.prefill_workspace_bytes(_prefill_params(tokens=5000)) == 0   # T > n_max
-    assert mla.prefill_workspace_bytes(_prefill_params(reserved=1)) == 0
+    assert mla.prefill_workspace_bytes(_prefill_params(num_splits=1)) == 0  # naive: no splits
+    assert mla.prefill_workspace_bytes(_prefill_params(q_rope_base=0.5)) == 0
     lib = binding.lib()
     vp = ctypes.c_void_p
     args = [vp(0x1000)] * 8
@@ -172,6 +183,59 @@ def test_prefill_workspace_and_validation():
     assert call(_prefill_params(tokens=0)) == mla.MLA_ERR_INVALID_ARG
     assert call(p, nbytes=10) == mla.MLA_ERR_WORKSPACE
     assert call(p, ptrs=[vp(0)] + args[1:]) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_prefill_absorbed_workspace_and_splits():
+    T = 16
+    p = _prefill_params(tokens=T, n_max=131072, ckv_stride_b=131072 * 576,
+                        kpe_stride_b=131072 * 576, num_splits=4)
+    rows = T * 128
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert mla.prefill_absorbed_num_splits(p) == 4
+    assert mla.prefill_absorbed_workspace_bytes(p) == \
+        rnd(rows * 576 * 2) + rnd(rows * 4 * 512 * 4) + rnd(rows * 4 * 2 * 4)
+    # auto split count: enough (query row, split) blocks for the chip
+    auto = _prefill_params(tokens=T, n_max=131072, ckv_stride_b=131072 * 576,
+                           kpe_stride_b=131072 * 576)
+    assert mla.prefill_absorbed_num_splits(auto) == 16
+    assert mla.prefill_absorbed_num_splits(_prefill_params()) == 1      # 4096 rows already
+    assert mla.prefill_absorbed_workspace_bytes(_prefill_params(heads=96)) == 0
+    assert mla.prefill_absorbed_workspace_bytes(_prefill_params(batch=20)) == 0  # B*T > 65535
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(heads=96), "UNSUPPORTED"),
+    (dict(d_c=128), "UNSUPPORTED"),
+    (dict(batch=17), "UNSUPPORTED"),       # batch * tokens beyond 65535
+    (dict(tokens=5000), "INVALID_ARG"),    # more queries than cache rows
+    (dict(num_splits=-1), "INVALID_ARG"),
+    (dict(num_splits=300), "INVALID_ARG"),
+    (dict(q_rope_base=1.0), "INVALID_ARG"),
+    (dict(softmax_scale=-1.0), "INVALID_ARG"),
+])
+def test_prefill_absorbed_rejects_bad_params_before_launch(kw, status):
+    lib = binding.lib()
+    vp = ctypes.c_void_p
+    pp = _prefill_params(**kw)
+    rc = lib.mla_prefill_absorbed(ctypes.byref(pp), *([vp(0x1000)] * 8), vp(0x100000), 1 << 40,
+                                  None)
+    assert rc == getattr(mla, "MLA_ERR_" + status)
+    assert _msg() != ""
+
+
+def test_prefill_absorbed_rejects_null_pointers_and_small_workspace():
+    lib = binding.lib()
+    vp = ctypes.c_void_p
+    pp = _prefill_params(tokens=8, num_splits=2)
+    ptrs = [vp(0x1000)] * 8
+    for i in range(8):
+        bad = list(ptrs)
+        bad[i] = vp(0)
+        assert lib.mla_prefill_absorbed(ctypes.byref(pp), *bad, vp(0x100000), 1 << 40,
+                                        None) == mla.MLA_ERR_INVALID_ARG, i
+    need = mla.prefill_absorbed_workspace_bytes(pp)
+    assert lib.mla_prefill_absorbed(ctypes.byref(pp), *ptrs, vp(0x100000), need - 1,
+                                    None) == mla.MLA_ERR_WORKSPACE
 
 
 def _append_params(**kw):

@@ -517,6 +517,17 @@ def test_rope_closed_forms(base):
                                      x[2] * math.sin(a) + x[3] * math.cos(a)], rtol=0, atol=1e-12)
 
 
+def test_rope_rotates_every_vector_of_an_array():
+    """A stack of vectors (one per head) is rotated vector by vector."""
+    rng = np.random.default_rng(44)
+    x = rng.standard_normal((3, 5, 16))
+    got = oracle.rope(x, 123, 10000.0)
+    for i in range(3):
+        for j in range(5):
+            assert np.array_equal(got[i, j], oracle.rope(x[i, j], 123, 10000.0))
+    assert not np.array_equal(got[2, 4], x[2, 4])
+
+
 def test_cache_rows_are_projections_then_rotation():
     rng = np.random.default_rng(63)
     B, d_model, dc, dr = 3, 96, 32, 8

@@ -1,0 +1,145 @@
+"""GPU parity of mla_prefill_absorbed (causal prefill in latent space: T new
+queries per sequence over the cached context) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_12_amd as mla
+import oracle
+from gpu_util import assert_close, metrics, run_decode, say, to_device, to_host_f64
+from mla_latent_kv_12_amd import datagen
+
+pytestmark = pytest.mark.gpu
+
+V3 = dict(dc=512, dr=64, dn=128, dv=128)
+TINY = dict(dc=64, dr=16, dn=32, dv=32)
+
+
+def chunk_case(B, T, L, H, dtype, seed, dims=V3, n_max=None):
+    n_max = n_max or max(max(L), T)
+    return datagen.make_chunk_case(B=B, T=T, H=H, n_max=n_max, seqlens=L, dtype=dtype,
+                                   seed=seed, **dims)
+
+
+def tensors(case):
+    dt = case.dtype
+    cache = to_device(case.cache, dt)
+    return dict(q_nope=to_device(case.q_nope, dt), q_rope=to_device(case.q_rope, dt),
+                w_uk=to_device(case.w_uk, dt), w_uv=to_device(case.w_uv, dt), cache=cache,
+                ckv=cache[:, :, : case.dc], kpe=cache[:, :, case.dc:],
+                seqlens=torch.from_numpy(case.seqlens.astype(np.int32)).cuda())
+
+
+def run_absorbed(case, t=None, out_dtype="f32", num_splits=0):
+    t = t or tensors(case)
+    odt = {None: None, "f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    out = mla.prefill_absorbed(t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv"],
+                               t["kpe"], t["seqlens"], softmax_scale=case.scale, out_dtype=odt,
+                               num_splits=num_splits)
+    torch.cuda.synchronize()
+    return to_host_f64(out)
+
+
+def oracle_all(case, fn=oracle.prefill_absorbed):
+    rows = [(b, t) for b in range(case.B) for t in range(case.T)]
+    ref = fn(case.q_nope, case.q_rope, case.w_uk, case.w_uv, case.ckv, case.kpe, case.seqlens,
+             case.scale, rows)
+    return ref.reshape(case.B, case.T, case.H, case.dv)
+
+
+@pytest.mark.parametrize("T,L", [(9, [9, 13]), (9, [5, 13]), (1, [1, 40])])
+def test_absorbed_prefill_f32_all_rows(T, L):
+    say(f"absorbed prefill f32 T={T} L={L}")
+    case = chunk_case(2, T, L, 3, "f32", 2100 + T + L[0], dims=TINY)
+    out = run_absorbed(case)
+    assert_close(out, oracle_all(case), "f32", "all rows vs absorbed oracle")
+    assert_close(out, oracle_all(case, oracle.prefill_naive), "f32", "all rows vs naive oracle")
+    first = max(T - L[0], 0)                        # queries placed before the cache
+    assert np.all(out[0, :first] == 0.0)
+
+
+@pytest.mark.parametrize("T,L", [
+    (1, [300, 77]),
+    (5, [300, 5]),
+    (64, [1000, 64]),
+    (40, [25, 333]),        # L < T: the first 15 queries of sequence 0 see no row
+    (33, [33, 97]),         # a query count that is not a multiple of 8 (absorb batches)
+])
+def test_absorbed_prefill_bf16_all_rows(T, L):
+    say(f"absorbed prefill bf16 B=2 T={T} L={L} H=128")
+    case = chunk_case(2, T, L, 128, "bf16", 2200 + T)
+    out = run_absorbed(case)
+    assert_close(out, oracle_all(case), "bf16", "all rows, 128 heads")
+    first = max(T - L[0], 0)
+    assert np.all(out[0, :first] == 0.0)
+
+
+def test_absorbed_prefill_bf16_split_counts_and_repeatability():
+    say("absorbed prefill bf16 split counts 1, 2, 7 and auto")
+    case = chunk_case(2, 12, [700, 333], 128, "bf16", 2301)
+    t = tensors(case)
+    ref = oracle_all(case)
+    for s in (1, 2, 7, 0):
+        out = run_absorbed(case, t, num_splits=s)
+        assert_close(out, ref, "bf16", f"S={s}")
+        again = run_absorbed(case, t, num_splits=s)
+        assert np.array_equal(out, again), f"S={s}: two runs differ"
+
+
+def test_absorbed_prefill_single_token_is_decode_bitwise():
+    say("absorbed prefill T=1 vs decode, same split count (bitwise)")
+    case = chunk_case(3, 1, [200, 33, 1], 128, "bf16", 2401)
+    pre = run_absorbed(case, num_splits=3)[:, 0]
+    dcase = datagen.DecodeCase("p11", "bf16", 3, 128, 512, 64, 128, 128, case.cache.shape[1],
+                               case.scale, np.ascontiguousarray(case.q_nope[:, 0]),
+                               np.ascontiguousarray(case.q_rope[:, 0]), case.w_uk, case.w_uv,
+                               case.cache, case.seqlens)
+    dec = to_host_f64(run_decode(dcase, out_dtype="f32", num_splits=3))
+    assert np.array_equal(pre, dec)
+
+
+@pytest.mark.parametrize("dtype,dims,H", [("bf16", V3, 128), ("f32", TINY, 4)])
+def test_absorbed_prefill_nan_padding_is_never_read(dtype, dims, H):
+    say(f"absorbed prefill {dtype}: NaN rows past each length")
+    case = chunk_case(2, 6, [50, 71], H, dtype, 2501, dims=dims, n_max=96)
+    t = tensors(case)
+    clean = run_absorbed(case, t)
+    for b, L in enumerate(case.seqlens):
+        t["cache"][b, int(L):] = float("nan")
+    dirty = run_absorbed(case, t)
+    assert np.array_equal(clean, dirty)
+
+
+def test_absorbed_prefill_matches_naive_gpu_path():
+    say("absorbed vs naive prefill (bf16, T=300, L=[300, 700], H=128)")
+    case = chunk_case(2, 300, [300, 700], 128, "bf16", 2601)
+    t = tensors(case)
+    absorbed = run_absorbed(case, t)
+    naive = to_host_f64(mla.prefill_naive(t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"],
+                                          t["ckv"], t["kpe"], t["seqlens"],
+                                          softmax_scale=case.scale, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    rows = [(b, q) for b in range(2) for q in (0, 1, 150, 298, 299)]
+    ref = oracle.prefill_absorbed(case.q_nope, case.q_rope, case.w_uk, case.w_uv, case.ckv,
+                                  case.kpe, case.seqlens, case.scale, rows)
+    assert_close(np.stack([absorbed[b, q] for b, q in rows]), ref, "bf16", "absorbed, 10 rows")
+    assert_close(np.stack([naive[b, q] for b, q in rows]), ref, "bf16", "naive, 10 rows")
+    # the two GPU paths agree on every row within the sum of their own bounds
+    m = metrics(absorbed, naive)
+    say(f"  absorbed vs naive, all rows: {m}")
+    assert m["finite"] and m["max_over_row_rms"] <= 2 * 2e-2 and m["zero_row_err"] == 0.0
+
+
+def test_absorbed_prefill_chunk_workload_sampled():
+    case = datagen.make_workload("v3-chunk-32k")
+    say(f"absorbed prefill {case.name}")
+    out = run_absorbed(case, out_dtype="f32")
+    rng = np.random.default_rng(6)
+    rows = [(int(b), int(q)) for b, q in zip(rng.integers(0, case.B, 6), rng.integers(0, case.T, 6))]
+    rows += [(0, 0), (case.B - 1, case.T - 1)]
+    heads = [0, 63, 127]
+    ref = oracle.prefill_absorbed(case.q_nope[:, :, heads], case.q_rope[:, :, heads],
+                                  case.w_uk[heads], case.w_uv[heads], case.ckv, case.kpe,
+                                  case.seqlens, case.scale, rows)
+    got = np.stack([out[b, q][heads] for b, q in rows])
+    assert_close(got, ref, "bf16", "8 rows x 3 heads")
