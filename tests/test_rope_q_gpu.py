@@ -1,7 +1,9 @@
 """GPU parity of the query-side rotary embedding (q_rope_base > 1): decode,
 naive prefill and absorbed prefill rotate q_rope at each query's own position
 before attending.  The expected values rotate the stored q_rope with the
-oracle's RoPE (fp64) and run the oracle on the widened inputs."""
+oracle's RoPE (fp64), round the rotated vector to the storage type as the
+library's contract states (it replaces q_rope, an MFMA operand in bf16), and
+run the oracle on the widened inputs."""
 import numpy as np
 import pytest
 import torch
@@ -23,16 +25,20 @@ def wide(a, dtype):
     return (datagen.bf16_to_f32(a) if dtype == "bf16" else a).astype(np.float64)
 
 
-def rotated_queries(q_rope, positions, base):
-    """q_rope [..., dr] widened to fp64 and rotated at positions[...] (rows with a
-    negative position are left as they are: they see no key)."""
+def rotated_queries(q_rope, positions, base, dtype):
+    """q_rope [..., H, dr] (widened to fp64) rotated at positions[...] by the
+    oracle and rounded to the storage type; rows with a negative position are
+    left as they are (they see no key)."""
     out = q_rope.copy()
     flat = out.reshape(-1, out.shape[-2], out.shape[-1])     # [rows, H, dr]
     pos = np.asarray(positions).reshape(-1)
     for r, p in enumerate(pos):
         if p >= 0:
             flat[r] = oracle.rope(flat[r], float(p), base)
-    return out
+    f32 = out.astype(np.float32)
+    if dtype == "bf16":
+        return datagen.bf16_to_f32(datagen.bf16_bits(f32)).astype(np.float64)
+    return f32.astype(np.float64)
 
 
 def widened(case):
@@ -56,7 +62,7 @@ def test_decode_rotates_queries_at_their_position(dtype, dims, H, L):
                      out_dtype=torch.float32, q_rope_base=BASE)
     torch.cuda.synchronize()
     w, cache = widened(case)
-    qr = rotated_queries(w["q_rope"], case.seqlens - 1, BASE)
+    qr = rotated_queries(w["q_rope"], case.seqlens - 1, BASE, dtype)
     ref, _ = oracle.decode_absorbed(w["q_nope"], qr, w["w_uk"], w["w_uv"], cache[:, :, :case.dc],
                                     cache[:, :, case.dc:], case.seqlens, case.scale)
     assert_close(to_host_f64(out), ref, dtype, "rotated at L-1")
@@ -86,7 +92,7 @@ def test_prefill_rotates_queries_at_their_position(path):
     torch.cuda.synchronize()
     w, wc = widened(case)
     pos = case.seqlens[:, None] - case.T + np.arange(case.T)[None, :]
-    qr = rotated_queries(w["q_rope"], pos, BASE)
+    qr = rotated_queries(w["q_rope"], pos, BASE, "bf16")
     rows = [(b, q) for b in range(2) for q in range(case.T)]
     ref = oracle.prefill_absorbed(w["q_nope"], qr, w["w_uk"], w["w_uv"], wc[:, :, :case.dc],
                                   wc[:, :, case.dc:], case.seqlens, case.scale, rows)
@@ -121,7 +127,7 @@ def test_append_then_decode_with_rotation_matches_oracle():
     rows = np.concatenate([c, kr], axis=1).reshape(B, L, -1)
     cache = wide(datagen.bf16_bits(rows.astype(np.float32)), "bf16")
     w = {k: wide(getattr(dec, k), "bf16") for k in ("q_nope", "q_rope", "w_uk", "w_uv")}
-    qr = rotated_queries(w["q_rope"], dec.seqlens - 1, BASE)
+    qr = rotated_queries(w["q_rope"], dec.seqlens - 1, BASE, "bf16")
     ref, _ = oracle.decode_absorbed(w["q_nope"], qr, w["w_uk"], w["w_uv"], cache[:, :, :512],
                                     cache[:, :, 512:], dec.seqlens, dec.scale)
     assert_close(to_host_f64(out), ref, "bf16", "producer + rotated decode")
