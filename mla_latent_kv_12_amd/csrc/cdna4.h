@@ -65,19 +65,26 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t range)
     return r;
 }
 
-// One wave-wide direct-to-LDS load: lane i's 16 bytes at byte offset voff of
-// the buffer land at LDS address lds_dst + 16 i.  Issued as inline assembly
-// so that the compiler does not track it: it would otherwise make every later
-// LDS read wait for all loads in flight.  Completion is awaited explicitly
-// (wait_then_barrier) before any wave reads the destination.  M0 carries the
-// LDS base; the kernels using this have no other M0 user.  The instruction
-// has no register result.
-__device__ __forceinline__ void lds_dma16(i32x4 rsrc, const unsigned char *lds_dst, unsigned voff)
+// LDS byte address of a __shared__ array (or of an element of one), as the
+// 32-bit value M0 and the LDS instructions take.
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char *shared)
 {
-    const unsigned m0v = __builtin_amdgcn_readfirstlane(
-        static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_byte *)lds_dst)));
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_byte *)shared));
+}
+
+// One wave-wide direct-to-LDS load: lane i's 16 bytes at byte offset voff of
+// the buffer land at LDS byte address lds_dst + 16 i.  lds_dst is
+// wave-uniform (lds_addr of the array plus uniform offsets, kept in SGPRs),
+// so no per-lane address arithmetic is spent on it.  Issued as inline
+// assembly so that the compiler does not track it: it would otherwise make
+// every later LDS read wait for all loads in flight.  Completion is awaited
+// explicitly (wait_then_barrier) before any wave reads the destination.  M0
+// carries the LDS address; the kernels using this have no other M0 user.
+// The instruction has no register result.
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t lds_dst, unsigned voff)
+{
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(m0v), "v"(voff), "s"(rsrc) : "memory");
+                 :: "s"(lds_dst), "v"(voff), "s"(rsrc) : "memory");
 }
 
 // Transposing LDS read (gfx950): within each group of 16 lanes, lane j gets

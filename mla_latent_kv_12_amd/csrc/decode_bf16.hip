@@ -31,12 +31,18 @@ using namespace cdna4;
 constexpr int DC = 512, DR = 64, DQK = DC + DR, DN = 128, DV = 128;
 
 // ---------------------------------------------------------------------------
-// 1. absorb: grid (4 column quarters, H, ceil(B/8)), 256 threads.
-//    Wave w reduces rows i in [32w, 32w+32) of W_UK[h]; lane holds 2 columns.
+// 1. absorb: grid (4 column quarters, H, ceil(B/8)), 256 threads, B = query
+//    rows.  Wave w reduces rows i in [32w, 32w+32) of W_UK[h]; lane holds 2
+//    columns.  The quarter-0 workgroups also place the RoPE query channels
+//    beside q~, rotated at the query's position when rope_base > 0 (RoFormer
+//    pairs (2i, 2i+1) turned by pos * rope_base^(-2i/d_r), angle and rotation
+//    in fp64, rounded through fp32 to bf16).
 // ---------------------------------------------------------------------------
 constexpr int kAbsorbBatch = 8;
 
-__global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, const uint16_t *q_nope,
+__global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, int T, int64_t n_max,
+                                                          const int32_t *seqlens, double rope_base,
+                                                          const uint16_t *q_nope,
                                                           const uint16_t *q_rope,
                                                           const uint16_t *w_uk, uint16_t *qa)
 {
@@ -85,11 +91,24 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, const ui
         reinterpret_cast<__bf16 *>(qa)[(static_cast<int64_t>(b0 + bb) * H + h) * DQK + qtr * 128 + c] =
             static_cast<__bf16>(v);
     }
-    if (qtr == 0) {  // RoPE query channels are copied unchanged
-        for (int e = tid; e < nb * DR; e += 256) {
-            const int bb = e / DR, r = e % DR;
-            qa[(static_cast<int64_t>(b0 + bb) * H + h) * DQK + DC + r] =
-                q_rope[(static_cast<int64_t>(b0 + bb) * H + h) * DR + r];
+    if (qtr == 0) {  // RoPE query channels, one rotation pair per thread
+        for (int e = tid; e < nb * (DR / 2); e += 256) {
+            const int v = b0 + e / (DR / 2), i = e % (DR / 2);
+            const int64_t row = static_cast<int64_t>(v) * H + h;
+            uint32_t two = *reinterpret_cast<const uint32_t *>(q_rope + row * DR + 2 * i);
+            if (rope_base > 0.0) {
+                const int b = v / T;
+                const int pos = static_cast<int>(min<int64_t>(max(seqlens[b], 0), n_max)) - T + (v - b * T);
+                if (pos > 0) {
+                    const double theta = pow(rope_base, -2.0 * i / DR);
+                    double sn, cs;
+                    sincos(static_cast<double>(pos) * theta, &sn, &cs);
+                    const double x0 = bf16lo(two), x1 = bf16hi(two);
+                    two = pack_bf16(static_cast<float>(x0 * cs - x1 * sn),
+                                    static_cast<float>(x0 * sn + x1 * cs));
+                }
+            }
+            *reinterpret_cast<uint32_t *>(qa + row * DQK + DC + 2 * i) = two;
         }
     }
 }
@@ -159,6 +178,14 @@ static_assert(16 * 15 + kLatRow <= kLatSlot, "a staggered row stays inside its s
 // Rows 16 ks + 8 + j and 16 ks + j differ by 8 * 1280 plus this stagger delta,
 // the same for every j in 0..7 and every ks, so the second transposing read
 // of a K step is the first one's address plus an immediate.
+// The loads address row 8 w + k of a tile through this closed form of lat_slot.
+__host__ __device__ constexpr int lat_slot_wk(int w, int k)
+{
+    return (8 * w + k) * kLatSlot + 16 * (4 * (k & 3) + ((2 * w + (k >> 2)) & 3));
+}
+static_assert(lat_slot_wk(0, 0) == lat_slot(0) && lat_slot_wk(1, 5) == lat_slot(13) &&
+              lat_slot_wk(2, 7) == lat_slot(23) && lat_slot_wk(3, 6) == lat_slot(30) &&
+              lat_slot_wk(3, 3) == lat_slot(27), "closed form of the load slots");
 constexpr int kTrHiStagger = lat_slot(8) - 8 * kLatSlot;
 static_assert(kTrHiStagger == lat_slot(9) - lat_slot(1) - 8 * kLatSlot &&
               kTrHiStagger == lat_slot(15) - lat_slot(7) - 8 * kLatSlot &&
@@ -236,14 +263,18 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     const unsigned lat_src = static_cast<unsigned>(8 * w * ckv_rowb + 16 * lane);
     const int rr = 8 * w + (lane >> 3);
     const unsigned rope_src = static_cast<unsigned>(rr * kpe_rowb + 16 * ((lane & 7) ^ ((rr >> 1) & 7)));
-    auto issue_tile = [&](int n0, unsigned char *dst) {
+    // LDS addresses of this wave's rows (wave-uniform, scalar arithmetic).
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const uint32_t tiles_lds = lds_addr(tiles);
+    auto issue_tile = [&](int n0, int dst_buf) {
         const unsigned lat_base = static_cast<unsigned>(n0) * static_cast<unsigned>(ckv_rowb);
+        const uint32_t dst = tiles_lds + static_cast<uint32_t>(dst_buf) * kTileBytes;
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            lds_dma16(rs_lat, dst + lat_slot(8 * w + k),
-                      lat_src + lat_base + static_cast<unsigned>(k * ckv_rowb));
-        lds_dma16(rs_rope, dst + kRopeBase + w * 8 * kRopeRow,
-                  rope_src + static_cast<unsigned>(n0) * static_cast<unsigned>(kpe_rowb));
+            lds_dma16(rs_lat, dst + lat_slot_wk(wu, k),
+                         lat_src + lat_base + static_cast<unsigned>(k * ckv_rowb));
+        lds_dma16(rs_rope, dst + kRopeBase + wu * 8 * kRopeRow,
+                     rope_src + static_cast<unsigned>(n0) * static_cast<unsigned>(kpe_rowb));
     };
 
     // Per-lane LDS offsets within a tile (immediates are added per access).
@@ -268,13 +299,13 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
 
     // One tile: wait for it, hand the next-but-one tile's loads to the
     // hardware, then scores, softmax weights and the latent accumulation.
-    auto tile_step = [&](int t, const unsigned char *tb, unsigned char *next_dst) {
+    auto tile_step = [&](int t, const unsigned char *tb, int next_buf) {
         const int n0 = start + t * kTile;
         if (t + 1 < ntiles)
             wait_then_barrier<kLoadsPerWave>();
         else
             wait_then_barrier<0>();
-        if (t + 2 < ntiles) issue_tile(n0 + 2 * kTile, next_dst);
+        if (t + 2 < ntiles) issue_tile(n0 + 2 * kTile, next_buf);
 
         // ---- scores: S^T[token i][head j] = sum_k C[i][k] Qa[j][k] ----
         const unsigned char *sa = tb + s_lat;
@@ -352,12 +383,12 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
         }
     };
 
-    issue_tile(start, tiles);
-    if (ntiles > 1) issue_tile(start + kTile, tiles + kTileBytes);
+    issue_tile(start, 0);
+    if (ntiles > 1) issue_tile(start + kTile, 1);
     int buf = 0;  // tile t lives in buffer t % 3
     for (int t = 0; t < ntiles; ++t) {
         const int nxt = buf == 0 ? 2 : buf - 1;  // (t + 2) % 3
-        tile_step(t, tiles + buf * kTileBytes, tiles + nxt * kTileBytes);
+        tile_step(t, tiles + buf * kTileBytes, nxt);
         buf = buf == 2 ? 0 : buf + 1;
     }
 
@@ -613,15 +644,10 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
     uint16_t *qa = static_cast<uint16_t *>(ws.q);
     const int rows = s.B * s.T;  // query rows
     if (events) (void)hipEventRecord(events[0], st);
-    if (s.q_rope_base > 0.0) {   // rotate the queries' RoPE channels at their positions
-        hipError_t e = launch_rope_q(s.B, s.T, s.H, DR, s.n_max, s.q_rope_base, true, seqlens,
-                                     q_rope, ws.q_rope, st);
-        if (e != hipSuccess) return e;
-        q_rope = ws.q_rope;
-    }
     {
         dim3 grid(4, s.H, (rows + kAbsorbBatch - 1) / kAbsorbBatch);
-        absorb_bf16_kernel<<<grid, 256, 0, st>>>(rows, s.H, static_cast<const uint16_t *>(q_nope),
+        absorb_bf16_kernel<<<grid, 256, 0, st>>>(rows, s.H, s.T, s.n_max, seqlens, s.q_rope_base,
+                                                 static_cast<const uint16_t *>(q_nope),
                                                  static_cast<const uint16_t *>(q_rope),
                                                  static_cast<const uint16_t *>(w_uk), qa);
         hipError_t e = hipGetLastError();

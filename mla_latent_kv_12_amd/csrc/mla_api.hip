@@ -175,7 +175,9 @@ size_t decode_workspace_layout(const DecodeShape &s, bool bf16, DecodeWorkspace 
     const size_t qbytes = bf16 ? rows * (size_t)(s.dc + s.dr) * 2 : rows * (size_t)s.dc * 4;
     const size_t obytes = rows * (size_t)s.S * (size_t)s.dc * 4;
     const size_t mlbytes = rows * (size_t)s.S * 2 * 4;
-    const size_t rbytes = s.q_rope_base > 0.0 ? rows * (size_t)s.dr * (bf16 ? 2 : 4) : 0;
+    // the fp32 path rotates q_rope into its own buffer; the bf16 absorb kernel
+    // rotates while it copies q_rope beside q~
+    const size_t rbytes = (s.q_rope_base > 0.0 && !bf16) ? rows * (size_t)s.dr * 4 : 0;
     const size_t off_o = round_up(qbytes, kAlign);
     const size_t off_ml = off_o + round_up(obytes, kAlign);
     const size_t off_r = off_ml + round_up(mlbytes, kAlign);

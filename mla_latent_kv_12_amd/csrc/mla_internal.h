@@ -34,7 +34,7 @@ struct DecodeWorkspace {
     void *q;          // bf16 path: [rows][H][dc+dr] bf16 pre-absorbed query; fp32: [rows][H][dc] fp32
     float *part_o;    // [rows][S][H][dc]   un-normalised latent accumulators per split
     float *part_ml;   // [rows][S][H][2]    running max (log2 units) and softmax mass per split
-    void *q_rope;     // [rows][H][dr] q_rope rotated at its position (storage dtype)
+    void *q_rope;     // fp32 path with q rotation: [rows][H][dr] q_rope rotated at its position
 };
 
 size_t decode_workspace_layout(const DecodeShape &s, bool bf16, DecodeWorkspace *ws_or_null,

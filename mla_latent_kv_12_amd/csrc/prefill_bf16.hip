@@ -104,15 +104,17 @@ __global__ __launch_bounds__(kGThreads, 2) void decompress_gemm_bf16_kernel(
         voff[e] = d < kGWLoads ? static_cast<unsigned>(row * DC * 2 + 16 * piece)
                                : static_cast<unsigned>((n0 + row) * ckv_rowb + 16 * piece);
     }
-    auto issue_chunk = [&](int kc, unsigned char *stage) {
+    // LDS address of this wave's first 1-KiB load slot (wave-uniform).
+    const uint32_t wave_lds = lds_addr(lds) + 1024 * __builtin_amdgcn_readfirstlane(wv);
+    auto issue_chunk = [&](int kc, int stage) {
         const unsigned k_byte = static_cast<unsigned>(kc * kGK * 2);
+        const uint32_t dst = wave_lds + static_cast<uint32_t>(stage) * kGStage;
 #pragma unroll
         for (int e = 0; e < kGDmaPerWave; ++e) {
-            const int d = wv + kGWaves * e;
             if (kGWaves * e < kGWLoads)
-                lds_dma16(rs_w, stage + 1024 * d, voff[e] + k_byte);
+                lds_dma16(rs_w, dst + 1024 * kGWaves * e, voff[e] + k_byte);
             else
-                lds_dma16(rs_c, stage + kGWBytes + 1024 * (d - kGWLoads), voff[e] + k_byte);
+                lds_dma16(rs_c, dst + kGWBytes + 1024 * (kGWaves * e - kGWLoads), voff[e] + k_byte);
         }
     };
 
@@ -131,15 +133,15 @@ __global__ __launch_bounds__(kGThreads, 2) void decompress_gemm_bf16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    issue_chunk(0, lds);
-    issue_chunk(1, lds + kGStage);
+    issue_chunk(0, 0);
+    issue_chunk(1, 1);
     int buf = 0;
     for (int kc = 0; kc < kGChunks; ++kc) {
         if (kc + 1 < kGChunks)
             wait_then_barrier<kGDmaPerWave>();
         else
             wait_then_barrier<0>();
-        if (kc + 2 < kGChunks) issue_chunk(kc + 2, lds + (buf == 0 ? 2 : buf - 1) * kGStage);
+        if (kc + 2 < kGChunks) issue_chunk(kc + 2, buf == 0 ? 2 : buf - 1);
         const unsigned char *st = lds + buf * kGStage;
 #pragma unroll
         for (int ks = 0; ks < kGK / 16; ++ks) {
@@ -215,6 +217,7 @@ constexpr int kVOff = kKrOff + kAT * DR * 2;            // 24 KiB
 constexpr int kATile = kVOff + kAT * DV * 2;            // 40 KiB
 constexpr int kADmaPerWave = kATile / 1024 / kAW;       // 5
 constexpr float kRescaleThreshold = 8.0f;
+
 static_assert(kADmaPerWave * 1024 * kAW == kATile, "whole loads per wave");
 static_assert(kKrOff / 1024 == 2 * kAW && (kVOff - kKrOff) / 1024 == kAW &&
               (kATile - kVOff) / 1024 == 2 * kAW, "load d = w + 8 e: e 0-1 K, 2 k^R, 3-4 V");
@@ -298,14 +301,17 @@ __global__ __launch_bounds__(kAThreads, 1) void prefill_attn_bf16_kernel(
         voff[3] = static_cast<unsigned>(rk0 * DV * 2 + 16 * ((lane & 15) ^ (4 * (rk0 & 3))));
         voff[4] = static_cast<unsigned>(rk1 * DV * 2 + 16 * ((lane & 15) ^ (4 * (rk1 & 3))));
     }
-    auto issue_tile = [&](int n0, unsigned char *dst) {
+    // LDS address of this wave's first 1-KiB load slot (wave-uniform).
+    const uint32_t wave_lds = lds_addr(tiles) + 1024 * __builtin_amdgcn_readfirstlane(w);
+    auto issue_tile = [&](int n0, int dst_buf) {
         const unsigned kb = static_cast<unsigned>(n0) * (DN * 2);
         const unsigned rb = static_cast<unsigned>(n0) * static_cast<unsigned>(kpe_rowb);
-        lds_dma16(rs_k, dst + kKnOff + 1024 * w, voff[0] + kb);
-        lds_dma16(rs_k, dst + kKnOff + 1024 * (w + 8), voff[1] + kb);
-        lds_dma16(rs_r, dst + kKrOff + 1024 * w, voff[2] + rb);
-        lds_dma16(rs_v, dst + kVOff + 1024 * w, voff[3] + kb);
-        lds_dma16(rs_v, dst + kVOff + 1024 * (w + 8), voff[4] + kb);
+        const uint32_t dst = wave_lds + static_cast<uint32_t>(dst_buf) * kATile;
+        lds_dma16(rs_k, dst + kKnOff, voff[0] + kb);
+        lds_dma16(rs_k, dst + kKnOff + 1024 * 8, voff[1] + kb);
+        lds_dma16(rs_r, dst + kKrOff, voff[2] + rb);
+        lds_dma16(rs_v, dst + kVOff, voff[3] + kb);
+        lds_dma16(rs_v, dst + kVOff + 1024 * 8, voff[4] + kb);
     };
 
     // Score A operand (key row 32 kb + l32, K elements 16 s + 8 half + 0..7):
@@ -334,13 +340,13 @@ __global__ __launch_bounds__(kAThreads, 1) void prefill_attn_bf16_kernel(
         for (int r = 0; r < 16; ++r) oacc[q][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    auto tile_step = [&](int it, const unsigned char *tb, unsigned char *next_dst) {
+    auto tile_step = [&](int it, const unsigned char *tb, int next_buf) {
         const int n0 = it * kAT;
         if (it + 1 < ntiles)
             wait_then_barrier<kADmaPerWave>();
         else
             wait_then_barrier<0>();
-        if (it + 2 < ntiles) issue_tile(n0 + 2 * kAT, next_dst);
+        if (it + 2 < ntiles) issue_tile(n0 + 2 * kAT, next_buf);
         if (n0 > wave_last) return;  // every key of the tile is in this wave's future
 
         // ---- scores: two 32-key blocks, interleaved accumulation chains ----
@@ -357,12 +363,18 @@ __global__ __launch_bounds__(kAThreads, 1) void prefill_attn_bf16_kernel(
         u32x4 abuf[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) abuf[i] = a_at(i);
+        // Raised wave priority over each MFMA block: of the two waves sharing a
+        // SIMD, the one in its MFMA phase issues first, so the other's softmax
+        // arithmetic fills the matrix core's busy cycles instead of both
+        // waves running the same phase in lockstep after the barrier.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < 2 * (DQK / 16); ++i) {
             sacc[i & 1] = mfma32(abuf[i & 3], qreg[i >> 1], sacc[i & 1]);
             if (i + 4 < 2 * (DQK / 16)) abuf[i & 3] = a_at(i + 4);
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
 
         // ---- online softmax (lane = query column; sacc[kb][r] is key
         //      n0 + 32 kb + 8 (r / 4) + 4 half + r % 4) ----
@@ -419,20 +431,22 @@ __global__ __launch_bounds__(kAThreads, 1) void prefill_attn_bf16_kernel(
         u32x4 av[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) av[i] = a_tr(0, i);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {  // i = 4 ks + q
             oacc[i & 3] = mfma32(av[i & 3], pk[i >> 2], oacc[i & 3]);
             if (i + 4 < 16) av[i & 3] = a_tr((i + 4) >> 2, (i + 4) & 3);
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
-    if (ntiles > 0) issue_tile(0, tiles);
-    if (ntiles > 1) issue_tile(kAT, tiles + kATile);
+    if (ntiles > 0) issue_tile(0, 0);
+    if (ntiles > 1) issue_tile(kAT, 1);
     int buf = 0;  // tile it lives in buffer it % 3
     for (int it = 0; it < ntiles; ++it) {
         const int nxt = buf == 0 ? 2 : buf - 1;  // (it + 2) % 3
-        tile_step(it, tiles + buf * kATile, tiles + nxt * kATile);
+        tile_step(it, tiles + buf * kATile, nxt);
         buf = buf == 2 ? 0 : buf + 1;
     }
 

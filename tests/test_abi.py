@@ -77,9 +77,12 @@ def test_decode_workspace_size():
     ml = 8 * 32 * 128 * 2 * 4
     rnd = lambda x: (x + 255) // 256 * 256
     assert ws == rnd(q) + rnd(o) + rnd(ml)
-    # rotating q_rope in the library adds room for the rotated copy
-    assert mla.decode_workspace_bytes(_v3_params(num_splits=32, q_rope_base=10000.0)) == \
-        ws + rnd(8 * 128 * 64 * 2)
+    # the bf16 path rotates q_rope while placing it beside q~ (no extra room);
+    # the fp32 path keeps a rotated copy
+    assert mla.decode_workspace_bytes(_v3_params(num_splits=32, q_rope_base=10000.0)) == ws
+    f32 = dict(dtype=mla.MLA_F32, out_dtype=mla.MLA_F32, num_splits=32)
+    assert mla.decode_workspace_bytes(_v3_params(q_rope_base=10000.0, **f32)) == \
+        mla.decode_workspace_bytes(_v3_params(**f32)) + rnd(8 * 128 * 64 * 4)
     assert mla.decode_workspace_bytes(_v3_params()) > 0            # auto split count
     assert mla.decode_workspace_bytes(_v3_params(d_c=256)) == 0    # unsupported -> 0
     assert mla.decode_workspace_bytes(_v3_params(batch=0)) == 0
