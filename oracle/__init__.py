@@ -11,9 +11,12 @@ from .oracle import (  # noqa: F401
     build,
     cache_rows,
     decode_absorbed,
+    decode_latent,
     decode_naive,
+    fold_value_output,
     kv_cache_bytes,
     max_threads,
+    output_proj,
     prefill_absorbed,
     prefill_naive,
     rope,

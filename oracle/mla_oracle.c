@@ -133,19 +133,18 @@ static double naive_one(const oracle_dims *d, const double *qn, const double *qr
 }
 
 /*
- * O2 -- absorbed decode for one (b, h): q~ = W_UK[h]^T q_nope,
- * s_n = scale * (q~ . c_n + q_rope . k^R_n), the same softmax,
- * o = sum_n p_n c_n (attention accumulated in latent space),
- * out = W_UV[h] o (one up-projection at the end).
+ * O2, latent part -- absorbed attention for one (b, h) up to the merged
+ * latent: q~ = W_UK[h]^T q_nope, s_n = scale * (q~ . c_n + q_rope . k^R_n),
+ * the same softmax, o = sum_n p_n c_n (attention accumulated in latent
+ * space).  o has d_c entries; returns the softmax mass.
  */
-static double absorbed_one(const oracle_dims *d, const double *qn, const double *qr,
-                           const void *w_uk, const void *w_uv,
-                           const void *ckv, const void *kpe, int64_t b, int64_t h,
-                           int64_t L, double *out)
+static double absorbed_latent(const oracle_dims *d, const double *qn, const double *qr,
+                              const void *w_uk, const void *ckv, const void *kpe, int64_t b,
+                              int64_t h, int64_t L, double *o)
 {
     const int dt = d->dtype;
-    const int64_t dc = d->dc, dr = d->dr, dn = d->dn, dv = d->dv;
-    for (int64_t i = 0; i < dv; ++i) out[i] = 0.0;
+    const int64_t dc = d->dc, dr = d->dr, dn = d->dn;
+    for (int64_t j = 0; j < dc; ++j) o[j] = 0.0;
     if (L <= 0) return 0.0;
 
     double *qa = malloc(sizeof(double) * (size_t)dc);
@@ -153,7 +152,6 @@ static double absorbed_one(const oracle_dims *d, const double *qn, const double 
     double *kr = malloc(sizeof(double) * (size_t)(dr > 0 ? dr : 1));
     double *s = malloc(sizeof(double) * (size_t)L);
     double *p = malloc(sizeof(double) * (size_t)L);
-    double *o = malloc(sizeof(double) * (size_t)dc);
 
     for (int64_t j = 0; j < dc; ++j) { /* q~[j] = sum_i W_UK[h][i][j] q_nope[i] */
         double acc = 0.0;
@@ -169,17 +167,33 @@ static double absorbed_one(const oracle_dims *d, const double *qn, const double 
         s[n] = d->scale * (content + pos);
     }
     double total = softmax(s, L, p);
-    for (int64_t j = 0; j < dc; ++j) o[j] = 0.0;
     for (int64_t n = 0; n < L; ++n) {
         widen_row(ckv, dt, b * d->ckv_sb + n * d->ckv_sn, dc, c);
         for (int64_t j = 0; j < dc; ++j) o[j] += p[n] * c[j];
     }
+    free(qa); free(c); free(kr); free(s); free(p);
+    return total;
+}
+
+/*
+ * O2 -- absorbed decode for one (b, h): the merged latent o above, then
+ * out = W_UV[h] o (one up-projection at the end).
+ */
+static double absorbed_one(const oracle_dims *d, const double *qn, const double *qr,
+                           const void *w_uk, const void *w_uv,
+                           const void *ckv, const void *kpe, int64_t b, int64_t h,
+                           int64_t L, double *out)
+{
+    const int dt = d->dtype;
+    const int64_t dc = d->dc, dv = d->dv;
+    double *o = malloc(sizeof(double) * (size_t)dc);
+    const double total = absorbed_latent(d, qn, qr, w_uk, ckv, kpe, b, h, L, o);
     for (int64_t i = 0; i < dv; ++i) { /* out[i] = sum_j W_UV[h][i][j] o[j] */
         double acc = 0.0;
         for (int64_t j = 0; j < dc; ++j) acc += widen(w_uv, dt, (h * dv + i) * dc + j) * o[j];
-        out[i] = acc;
+        out[i] = L > 0 ? acc : 0.0;
     }
-    free(qa); free(c); free(kr); free(s); free(p); free(o);
+    free(o);
     return total;
 }
 
@@ -238,6 +252,84 @@ int oracle_decode_absorbed(const oracle_dims *d, const void *q_nope, const void 
 {
     return decode_common(absorbed_one, d, q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens,
                          pairs, npairs, out, psum);
+}
+
+/*
+ * The merged latent of absorbed decode, o[b][h] = sum_n p_n c[b][n] (before
+ * the W_UV up-projection), for a list of (b, h) pairs or every pair
+ * (b-major) when pairs == NULL.  out is [npairs][dc].
+ */
+int oracle_decode_latent(const oracle_dims *d, const void *q_nope, const void *q_rope,
+                         const void *w_uk, const void *ckv, const void *kpe,
+                         const int32_t *seqlens, const int64_t *pairs, int64_t npairs,
+                         double *out)
+{
+    if (check_dims(d) || !out || !seqlens) return 1;
+    const int64_t total = pairs ? npairs : d->B * d->H;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t k = 0; k < total; ++k) {
+        const int64_t b = pairs ? pairs[2 * k] : k / d->H;
+        const int64_t h = pairs ? pairs[2 * k + 1] : k % d->H;
+        if (b < 0 || b >= d->B || h < 0 || h >= d->H) { bad = 1; continue; }
+        double *qn = malloc(sizeof(double) * (size_t)d->dn);
+        double *qr = malloc(sizeof(double) * (size_t)(d->dr > 0 ? d->dr : 1));
+        widen_row(q_nope, d->dtype, (b * d->H + h) * d->dn, d->dn, qn);
+        widen_row(q_rope, d->dtype, (b * d->H + h) * d->dr, d->dr, qr);
+        absorbed_latent(d, qn, qr, w_uk, ckv, kpe, b, h, (int64_t)seqlens[b], out + k * d->dc);
+        free(qn); free(qr);
+    }
+    return bad;
+}
+
+/*
+ * The attention block's output projection y = W x for every row of x: the
+ * linear map from the concatenated head outputs back to the model width
+ * (the "mla-from-scratch" reference model's out_proj; the distaisys
+ * deep-dive's W_O).  x [B][K] and w [N][K] (row-major, a linear layer's
+ * weight layout), each in its own storage type; y [B][N] fp64.
+ */
+int oracle_output_proj(int64_t B, int64_t K, int64_t N, int32_t dtype_x, const void *x,
+                       int32_t dtype_w, const void *w, double *y)
+{
+    if (B < 0 || K <= 0 || N <= 0 || !y) return 1;
+    if ((dtype_x != OR_F64 && dtype_x != OR_F32 && dtype_x != OR_BF16) ||
+        (dtype_w != OR_F64 && dtype_w != OR_F32 && dtype_w != OR_BF16)) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < B; ++b) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += widen(w, dtype_w, n * K + k) * widen(x, dtype_x, b * K + k);
+            y[b * N + n] = acc;
+        }
+    return 0;
+}
+
+/*
+ * Value-side absorption into the output projection ("mla-from-scratch"
+ * README, "Absorption, and why RoPE breaks it": attending over the latents
+ * and up-projecting once lets W_UV fold into W_O, by associativity):
+ *   W_OV[n][h d_c + j] = sum_i W_O[n][h d_v + i] W_UV[h][i][j],
+ * so that W_O concat_h(W_UV[h] o_h) = W_OV concat_h(o_h).
+ * w_o [N][H d_v], w_uv [H][d_v][d_c] (one storage type); w_ov [N][H d_c] fp64.
+ */
+int oracle_fold_value_output(int64_t N, int64_t H, int64_t dv, int64_t dc, int32_t dtype,
+                             const void *w_o, const void *w_uv, double *w_ov)
+{
+    if (N <= 0 || H <= 0 || dv <= 0 || dc <= 0 || !w_ov) return 1;
+    if (dtype != OR_F64 && dtype != OR_F32 && dtype != OR_BF16) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t j = 0; j < dc; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < dv; ++i)
+                    acc += widen(w_o, dtype, n * H * dv + h * dv + i) *
+                           widen(w_uv, dtype, (h * dv + i) * dc + j);
+                w_ov[n * H * dc + h * dc + j] = acc;
+            }
+    return 0;
 }
 
 /*

@@ -17,6 +17,12 @@ Parity status of each function (the pins live in ``tests/test_oracle_pins.py``):
                    counts and lengths (L < T included); each row equals
                    decode_absorbed over its causal prefix.
   kv_cache_bytes   pinned: the cache tables printed on the pages.
+  decode_latent    pinned: W_UV times it equals decode_absorbed; L=1 gives the
+                   cached latent row exactly.
+  output_proj      pinned: a numpy fp64 matrix product.
+  fold_value_output pinned: selection-matrix W_UV gives W_O's columns exactly in
+                   the selected places; the folded and unfolded projections of
+                   the same decode agree (associativity).
   rope             pinned: the relative-position property (scores depend only on
                    the position difference), norm preservation, position 0 is
                    the identity, closed forms for one and two rotation pairs.
@@ -80,6 +86,13 @@ def _open(path: str) -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = [ctypes.POINTER(_Dims), i64, vp, vp, vp, vp, vp, vp, vp, vp, i64, dp]
         f.restype = ctypes.c_int
+    lib.oracle_decode_latent.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, vp, vp, vp, vp, i64,
+                                         dp]
+    lib.oracle_decode_latent.restype = ctypes.c_int
+    lib.oracle_output_proj.argtypes = [i64, i64, i64, ctypes.c_int32, vp, ctypes.c_int32, vp, dp]
+    lib.oracle_output_proj.restype = ctypes.c_int
+    lib.oracle_fold_value_output.argtypes = [i64, i64, i64, i64, ctypes.c_int32, vp, vp, dp]
+    lib.oracle_fold_value_output.restype = ctypes.c_int
     lib.oracle_kv_cache_bytes.argtypes = [i64] * 6
     lib.oracle_rope.argtypes = [i64, dp, ctypes.c_double, ctypes.c_double, dp]
     lib.oracle_rope.restype = None
@@ -189,6 +202,69 @@ def decode_absorbed(q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens, scale, pairs=
     W_UV up-projection).  Same arguments and returns as :func:`decode_naive`."""
     return _decode("oracle_decode_absorbed", q_nope, q_rope, w_uk, w_uv, ckv, kpe, seqlens,
                    scale, pairs)
+
+
+def decode_latent(q_nope, q_rope, w_uk, ckv, kpe, seqlens, scale, pairs=None):
+    """Merged latent of absorbed decode, o[b,h] = sum_n p_n c[b,n] (before the
+    W_UV up-projection).  Returns [B,H,dc], or [len(pairs), dc] for a pair list."""
+    q_nope = np.ascontiguousarray(q_nope)
+    q_rope = np.ascontiguousarray(q_rope)
+    w_uk = np.ascontiguousarray(w_uk)
+    H, dn, dc = w_uk.shape
+    dr = q_rope.shape[-1]
+    dt = _code(q_nope)
+    for a in (q_rope, w_uk, ckv, kpe):
+        if _code(a) != dt:
+            raise OracleError("all inputs must share one storage dtype")
+    _, csb, csn = _cache_view(ckv, dc)
+    _, ksb, ksn = _cache_view(kpe, dr) if dr > 0 else (kpe, 0, 0)
+    d = _Dims(B=ckv.shape[0], H=H, dc=dc, dr=dr, dn=dn, dv=1, ckv_sb=csb, ckv_sn=csn,
+              kpe_sb=ksb, kpe_sn=ksn, dtype=dt, reserved=0, scale=float(scale))
+    seq = np.ascontiguousarray(seqlens, dtype=np.int32)
+    if pairs is None:
+        n, pp = d.B * d.H, None
+    else:
+        pp = np.ascontiguousarray(np.asarray(pairs, dtype=np.int64).reshape(-1, 2))
+        n = pp.shape[0]
+    out = np.zeros((n, dc), dtype=np.float64)
+    rc = _load().oracle_decode_latent(ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                      _base_ptr(ckv), _base_ptr(kpe), _ptr(seq), _ptr(pp), n,
+                                      _ptr(out))
+    if rc != 0:
+        raise OracleError("oracle_decode_latent rejected its arguments")
+    return out.reshape(d.B, d.H, dc) if pairs is None else out
+
+
+def output_proj(x, w):
+    """y = x W^T in fp64: x [B, K], w [N, K] (each fp64, fp32 or bf16 bits)."""
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w)
+    B, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise OracleError("x and w disagree on the input width")
+    y = np.zeros((B, N), dtype=np.float64)
+    if _load().oracle_output_proj(B, K, N, _code(x), _ptr(x), _code(w), _ptr(w), _ptr(y)) != 0:
+        raise OracleError("oracle_output_proj rejected its arguments")
+    return y
+
+
+def fold_value_output(w_o, w_uv):
+    """W_OV [N, H*dc] with W_OV[:, h*dc:(h+1)*dc] = W_O[:, h*dv:(h+1)*dv] W_UV[h],
+    from w_o [N, H*dv] and w_uv [H, dv, dc] (one storage type), in fp64."""
+    w_o = np.ascontiguousarray(w_o)
+    w_uv = np.ascontiguousarray(w_uv)
+    if _code(w_o) != _code(w_uv):
+        raise OracleError("all inputs must share one storage dtype")
+    H, dv, dc = w_uv.shape
+    N = w_o.shape[0]
+    if w_o.shape[1] != H * dv:
+        raise OracleError("W_O width must be heads * d_v")
+    out = np.zeros((N, H * dc), dtype=np.float64)
+    if _load().oracle_fold_value_output(N, H, dv, dc, _code(w_o), _ptr(w_o), _ptr(w_uv),
+                                        _ptr(out)) != 0:
+        raise OracleError("oracle_fold_value_output rejected its arguments")
+    return out
 
 
 def absorb_q(q_nope, w_uk):

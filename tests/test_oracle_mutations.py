@@ -85,6 +85,15 @@ MUTATIONS = [
     ("cache rows: the key left unrotated",
      "if (dr > 0) oracle_rope(dr, raw, (double)pos[b], base, kr + b * dr);",
      "if (dr > 0) oracle_rope(dr, raw, 0.0, base, kr + b * dr);"),
+    ("output projection: weight read transposed",
+     "acc += widen(w, dtype_w, n * K + k) * widen(x, dtype_x, b * K + k);",
+     "acc += widen(w, dtype_w, (k % N) * K + (n % K)) * widen(x, dtype_x, b * K + k);"),
+    ("fold: W_UV read transposed",
+     "widen(w_uv, dtype, (h * dv + i) * dc + j);",
+     "widen(w_uv, dtype, (h * dv + (j % dv)) * dc + (i % dc));"),
+    ("fold: W_O column of the wrong head",
+     "acc += widen(w_o, dtype, n * H * dv + h * dv + i) *",
+     "acc += widen(w_o, dtype, n * H * dv + ((h + 1) % H) * dv + i) *"),
     ("bf16 widening shifted",
      "uint32_t u = ((uint32_t)((const uint16_t *)base)[i]) << 16;",
      "uint32_t u = ((uint32_t)((const uint16_t *)base)[i]) << 15;"),
@@ -124,6 +133,10 @@ PINS = {
     "rope norm and identity": pins.test_rope_norm_and_identity,
     "rope closed forms": lambda: pins.test_rope_closed_forms(10000.0),
     "cache rows": pins.test_cache_rows_are_projections_then_rotation,
+    "latent up-projected is decode": pins.test_decode_latent_up_projected_is_decode,
+    "output projection": pins.test_output_proj_is_a_matrix_product,
+    "fold with selection weights": pins.test_fold_with_selection_weights_places_columns,
+    "folded == unfolded": lambda: pins.test_folded_projection_equals_unfolded("f64"),
 }
 
 

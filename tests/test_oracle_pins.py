@@ -426,6 +426,75 @@ def test_prefill_absorbed_row_equals_decode_prefix():
 
 
 # --------------------------------------------------------------------------
+# Value side: the merged latent, the output projection and W_UV folded into W_O
+# --------------------------------------------------------------------------
+
+def test_decode_latent_up_projected_is_decode():
+    """W_UV[h] o[b,h] equals the absorbed decode's output, so the latent is the
+    attention output before the single up-projection."""
+    rng = np.random.default_rng(61)
+    B, H, dc, dr, dn, dv, N = 2, 3, 48, 16, 16, 12, 40
+    q_nope, q_rope, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, N)
+    seq = np.array([N, 17], np.int32)
+    o = oracle.decode_latent(q_nope, q_rope, w_uk, cache[:, :, :dc], cache[:, :, dc:], seq, 0.3)
+    out, _ = oracle.decode_absorbed(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc],
+                                    cache[:, :, dc:], seq, 0.3)
+    up = np.einsum("hvc,bhc->bhv", w_uv, o)
+    assert _rel(up, out) <= 1e-13
+    # one cached row: the softmax weight is exactly 1 and o is that row
+    one = oracle.decode_latent(q_nope, q_rope, w_uk, cache[:, :, :dc], cache[:, :, dc:],
+                               np.array([1, 1], np.int32), 0.3)
+    assert np.array_equal(one, np.broadcast_to(cache[:, None, 0, :dc], one.shape))
+
+
+def test_output_proj_is_a_matrix_product():
+    rng = np.random.default_rng(62)
+    x = rng.standard_normal((5, 96))
+    w = datagen.bf16_bits(rng.standard_normal((33, 96)).astype(np.float32))
+    y = oracle.output_proj(x, w)
+    ref = x @ datagen.bf16_to_f32(w).astype(np.float64).T      # numpy's fp64 product
+    assert _rel(y, ref) <= 1e-13
+
+
+def test_fold_with_selection_weights_places_columns():
+    """W_UV[h] row i selecting latent channel sel[h][i] makes W_OV carry W_O's
+    column (h, i) at (h, sel[h][i]) and zeros elsewhere, exactly."""
+    rng = np.random.default_rng(63)
+    N, H, dv, dc = 7, 3, 4, 10
+    w_o = rng.standard_normal((N, H * dv))
+    sel = np.stack([rng.permutation(dc)[:dv] for _ in range(H)])
+    w_uv = np.zeros((H, dv, dc))
+    for h in range(H):
+        w_uv[h, np.arange(dv), sel[h]] = 1.0
+    w_ov = oracle.fold_value_output(w_o, w_uv)
+    expect = np.zeros((N, H * dc))
+    for h in range(H):
+        for i in range(dv):
+            expect[:, h * dc + sel[h][i]] = w_o[:, h * dv + i]
+    assert np.array_equal(w_ov, expect)
+
+
+@pytest.mark.parametrize("dtype", ["f64", "bf16"])
+def test_folded_projection_equals_unfolded(dtype):
+    """Associativity on the value side: W_O concat_h(W_UV[h] o_h) from the
+    absorbed decode equals W_OV concat_h(o_h) from the merged latent."""
+    rng = np.random.default_rng(64)
+    B, H, dc, dr, dn, dv, N, d_model = 2, 3, 32, 8, 16, 12, 25, 20
+    q_nope, q_rope, w_uk, w_uv, cache = _rand_case(rng, B, H, dc, dr, dn, dv, N)
+    w_o = rng.standard_normal((d_model, H * dv)) / math.sqrt(H * dv)
+    if dtype == "bf16":
+        q_nope, q_rope, w_uk, w_uv, cache, w_o = (
+            datagen.bf16_bits(a.astype(np.float32)) for a in (q_nope, q_rope, w_uk, w_uv, cache, w_o))
+    seq = np.array([N, 9], np.int32)
+    out, _ = oracle.decode_absorbed(q_nope, q_rope, w_uk, w_uv, cache[:, :, :dc],
+                                    cache[:, :, dc:], seq, 0.25)
+    y_unfolded = oracle.output_proj(out.reshape(B, H * dv), w_o)
+    o = oracle.decode_latent(q_nope, q_rope, w_uk, cache[:, :, :dc], cache[:, :, dc:], seq, 0.25)
+    y_folded = oracle.output_proj(o.reshape(B, H * dc), oracle.fold_value_output(w_o, w_uv))
+    assert _rel(y_folded, y_unfolded) <= 1e-12
+
+
+# --------------------------------------------------------------------------
 # Mutations: each plausible oracle mistake is caught by the pins above
 # --------------------------------------------------------------------------
 
