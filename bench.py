@@ -247,6 +247,65 @@ def bench_chunk(args, mla, datagen):
     return 0
 
 
+def bench_outproj(args, mla, datagen):
+    """The step after decode, the output projection for batch 8 at the V3
+    shape: y = W_O concat_h(out_h) (W_O 7168 x 16384, the unfolded form) and,
+    for comparison, y = W_OV concat_h(o_lat_h) with W_UV folded in (W_OV 7168 x
+    65536); one JSON line with both kernels' algorithmic HBM rates."""
+    import numpy as np
+    import torch
+
+    B, H, dv, dc, d_model = 8, 128, 128, 512, 7168
+    g = torch.Generator(device="cuda").manual_seed(20260007)
+
+    def randn(*shape, std=1.0):
+        return (torch.randn(*shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+
+    x_unf = randn(B, H * dv)
+    x_fold = randn(B, H * dc)
+    w_o = randn(d_model, H * dv, std=1.0 / np.sqrt(H * dv))
+    w_uv = randn(H, dv, dc, std=1.0 / np.sqrt(dc))
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    w_ov = mla.fold_value_output(w_o, w_uv)
+    t1.record()
+    torch.cuda.synchronize()
+    fold_ms = t0.elapsed_time(t1)
+    res = {}
+    for name, x, w in (("unfolded", x_unf, w_o), ("folded", x_fold, w_ov)):
+        params = mla.proj_params(x, w)
+        ws = torch.empty(mla.output_proj_workspace_bytes(params), dtype=torch.uint8,
+                         device="cuda")
+        y = torch.empty((B, d_model), dtype=torch.bfloat16, device="cuda")
+        for _ in range(args.warmup):
+            mla.output_proj(x, w, out=y, workspace=ws, params=params)
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record()
+        for i in range(args.steps):
+            mla.output_proj(x, w, out=y, workspace=ws, params=params)
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        us = 1e3 * float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]))
+        nbytes = (w.numel() + x.numel() + y.numel()) * 2
+        res[name] = {"us_per_call": us, "weight_bytes": w.numel() * 2,
+                     "gbps": nbytes / (us * 1e-6) / 1e9, "splits": params.num_splits or None}
+    gbps = res["unfolded"]["gbps"]
+    print(json.dumps({
+        "mode": "outproj", "metric": "output projection after decode, HBM GB/s (% of peak)",
+        "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic (seeded normals)",
+        "config": {"workload": "V3 output projection batch 8, d_model 7168", "batch": B,
+                   "heads": H, "d_v": dv, "d_c": dc, "d_model": d_model},
+        "unfolded": res["unfolded"], "folded": res["folded"], "fold_weights_ms": fold_ms,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS,
+                     "kernel": "rowproj_bf16_kernel + rowproj_reduce_kernel (unfolded W_O)"}}),
+        flush=True)
+    return 0
+
+
 def bench_append(args, mla, datagen):
     """The cache-row producer for one decode step: c = W_DKV h and the rotated
     k^R = RoPE(W_KR h) for 8 sequences (d_model 7168), written into a 128k-row
@@ -308,12 +367,13 @@ def main(argv=None):
     ap.add_argument("--q-rope-base", type=float, default=0.0,
                     help="rotate q_rope in the library at each query's position with this base "
                          "(0: q_rope is taken as already rotated)")
-    ap.add_argument("--mode", choices=["decode", "prefill", "chunk", "append", "copy"],
+    ap.add_argument("--mode", choices=["decode", "prefill", "chunk", "append", "outproj", "copy"],
                     default="decode",
                     help="prefill: the naive causal prefill (V3 shape, T=4096) against the bf16 "
                          "MFMA peak; chunk: the absorbed prefill of 64 queries per sequence over "
                          "32768 cached rows (batch 4); append: the cache-row producer (batch 8, "
-                         "d_model 7168) "
+                         "d_model 7168); outproj: the output projection after decode, unfolded "
+                         "and with W_UV folded in "
                          "against HBM; copy: a plain device-to-device copy of --copy-bytes, the "
                          "reference that scales the profiler's byte counters")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
@@ -360,6 +420,8 @@ def main(argv=None):
         return bench_chunk(args, mla, datagen)
     if args.mode == "append":
         return bench_append(args, mla, datagen)
+    if args.mode == "outproj":
+        return bench_outproj(args, mla, datagen)
 
     t_gen = time.perf_counter()
     case = datagen.make_workload(args.workload)

@@ -265,6 +265,74 @@ mla_status mla_prefill_absorbed(const mla_prefill_params *p, const void *q_nope,
                                 size_t workspace_bytes, void *stream);
 
 /*
+ * Absorbed decode up to the merged latent: the same call as mla_decode
+ * without the final up-projection, writing
+ *   o_lat[b][h][:] = sum_n p_n c[b][n]      (d_c values, out_dtype)
+ * the attention output in latent space, for a caller that folds W_UV into
+ * its output projection ("mla-from-scratch" README, "Absorption, and why
+ * RoPE breaks it": attending over the latents and up-projecting once lets
+ * W_UV fold into W_O).  W_UV is not an argument; p->d_v is ignored.  The
+ * workspace is mla_decode_workspace_bytes(p).  Other arguments, checks and
+ * reproducibility as for mla_decode.
+ */
+mla_status mla_decode_latent(const mla_decode_params *p, const void *q_nope, const void *q_rope,
+                             const void *w_uk, const void *ckv_cache, const void *kpe_cache,
+                             const int32_t *seqlens, void *o_lat, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * Shape of an output projection y = x W^T: batch rows of in_features
+ * values each, against a weight of out_features rows.
+ * Supported: dtype MLA_BF16 (x and w; in_features a multiple of 64, x and w
+ * 16-byte aligned; MFMA path) or MLA_F32 (any in_features); out_dtype either.
+ */
+typedef struct mla_proj_params {
+    int64_t batch;         /* B rows of x                                        */
+    int64_t in_features;   /* K: H * d_v (unfolded) or H * d_c (W_UV folded in)  */
+    int64_t out_features;  /* N: the model width                                 */
+    int32_t dtype;         /* mla_dtype of x and w                               */
+    int32_t out_dtype;     /* mla_dtype of y                                     */
+    int32_t num_splits;    /* slices of K summed in a fixed order; 0 -> by size */
+    int32_t reserved;      /* must be 0                                          */
+} mla_proj_params;
+
+/* Bytes of device workspace mla_output_proj needs (host; 0 if invalid):
+ * the fp32 partial sums of every K slice. */
+size_t mla_output_proj_workspace_bytes(const mla_proj_params *p);
+
+/*
+ * The attention block's output projection, the step after decode:
+ *   y[b][n] = sum_k x[b][k] w[n][k]
+ * with x the concatenated head outputs ([B][H][d_v] from mla_decode is
+ * [B][H * d_v]) and w = W_O [d_model][H * d_v] (row-major, a linear layer's
+ * weight), or x the merged latents of mla_decode_latent ([B][H * d_c]) and
+ * w = W_OV from mla_fold_value_output ("mla-from-scratch" reference model,
+ * out_proj; "Absorption, and why RoPE breaks it" for the folded form).
+ *   x [B][K], w [N][K] dtype; y [B][N] out_dtype, written.
+ * Dot products accumulate in fp32 over slices of K whose partial sums are
+ * added in ascending slice order: bitwise reproducible for a fixed split
+ * count.  workspace >= mla_output_proj_workspace_bytes(p), 256-byte aligned.
+ */
+mla_status mla_output_proj(const mla_proj_params *p, const void *x, const void *w, void *y,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Value-side absorption of the weights (a one-off transform, not per step):
+ *   w_ov[n][h * d_c + j] = sum_i w_o[n][h * d_v + i] w_uv[h][i][j]
+ * so that W_O concat_h(W_UV[h] o_h) = W_OV concat_h(o_h) by associativity
+ * ("mla-from-scratch" README, "Absorption, and why RoPE breaks it").
+ *   w_o [d_model][heads * d_v], w_uv [heads][d_v][d_c] (dtype), w_ov
+ *   [d_model][heads * d_c] (dtype), written; fp32 accumulation, bf16 results
+ *   rounded to nearest even.
+ * At the V3 shape W_OV holds 4x the bytes of W_UV and W_O together (d_c =
+ * 512 > d_v = 128), so for decode the unfolded pair is the cheaper one; the
+ * folded form is offered for callers that want the single product.
+ */
+mla_status mla_fold_value_output(int64_t d_model, int64_t heads, int64_t d_v, int64_t d_c,
+                                 int32_t dtype, const void *w_o, const void *w_uv, void *w_ov,
+                                 void *stream);
+
+/*
  * Shape of a cache-append call: one new token per sequence.
  * Supported: dtype MLA_BF16 or MLA_F32 (every tensor the same), d_c >= 2 and
  * even, d_r >= 0 and even, d_model a multiple of 8 (bf16) or 4 (fp32).

@@ -24,11 +24,15 @@ EXPORTS = (
     "mla_decode_workspace_bytes",
     "mla_decode",
     "mla_decode_profiled",
+    "mla_decode_latent",
     "mla_prefill_workspace_bytes",
     "mla_prefill_naive",
     "mla_prefill_absorbed_num_splits",
     "mla_prefill_absorbed_workspace_bytes",
     "mla_prefill_absorbed",
+    "mla_output_proj_workspace_bytes",
+    "mla_output_proj",
+    "mla_fold_value_output",
     "mla_cache_append",
     "mla_kv_cache_bytes",
     "mla_status_string",
@@ -69,6 +73,15 @@ class PrefillParams(ctypes.Structure):
     ]
 
 
+class ProjParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("in_features", ctypes.c_int64),
+        ("out_features", ctypes.c_int64), ("dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
 class AppendParams(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int64), ("d_model", ctypes.c_int64), ("d_c", ctypes.c_int64),
@@ -103,6 +116,15 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_profiled.argtypes = [ctypes.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp,
                                           vp, vp, vp, sz, vp, vp]
         L.mla_decode_profiled.restype = ctypes.c_int
+        L.mla_decode_latent.argtypes = [ctypes.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp, vp,
+                                        vp, sz, vp]
+        L.mla_decode_latent.restype = ctypes.c_int
+        L.mla_output_proj_workspace_bytes.argtypes = [ctypes.POINTER(ProjParams)]
+        L.mla_output_proj_workspace_bytes.restype = sz
+        L.mla_output_proj.argtypes = [ctypes.POINTER(ProjParams), vp, vp, vp, vp, sz, vp]
+        L.mla_output_proj.restype = ctypes.c_int
+        L.mla_fold_value_output.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int32, vp, vp, vp, vp]
+        L.mla_fold_value_output.restype = ctypes.c_int
         L.mla_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillParams)]
         L.mla_prefill_workspace_bytes.restype = sz
         L.mla_prefill_naive.argtypes = [ctypes.POINTER(PrefillParams), vp, vp, vp, vp, vp, vp, vp,
@@ -231,6 +253,78 @@ def decode(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, out=Non
                                          _ptr(kpe_cache), _ptr(seqlens), _ptr(out),
                                          _ptr(workspace), workspace.numel(), _stream(stream),
                                          events))
+    return out
+
+
+def decode_latent(q_nope, q_rope, w_uk, ckv_cache, kpe_cache, seqlens, *, out=None,
+                  workspace=None, softmax_scale=None, out_dtype=None, num_splits=0,
+                  q_rope_base=None, stream=None, params: DecodeParams | None = None):
+    """Absorbed decode up to the merged latent (``mla_decode_latent``):
+    o_lat [B, H, d_c] = sum_n p_n c[b, n], before any up-projection."""
+    B, H, dn = q_nope.shape
+    dc = w_uk.shape[2]
+    if params is None:
+        # d_v plays no part in the latent form; the workspace query checks it
+        # against the implemented widths (128 on the bf16 path)
+        dv = 128 if w_uk.dtype == torch.bfloat16 else 1
+        fake_wuv = torch.empty((H, dv, dc), dtype=w_uk.dtype, device="meta")
+        params = decode_params(q_nope, q_rope, w_uk, fake_wuv, ckv_cache, kpe_cache,
+                               softmax_scale=softmax_scale, out_dtype=out_dtype,
+                               num_splits=num_splits, q_rope_base=q_rope_base)
+    if out is None:
+        odt = torch.float32 if params.out_dtype == MLA_F32 else torch.bfloat16
+        out = torch.empty((B, H, dc), dtype=odt, device=q_nope.device)
+    need = decode_workspace_bytes(params)
+    if need == 0:
+        _check(lib().mla_decode_latent(ctypes.byref(params), None, None, None, None, None, None,
+                                       None, None, 0, None))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
+    _check(lib().mla_decode_latent(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                   _ptr(ckv_cache), _ptr(kpe_cache), _ptr(seqlens), _ptr(out),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def proj_params(x, w, *, out_dtype=None, num_splits=0) -> ProjParams:
+    B, K = x.shape
+    N = w.shape[0]
+    return ProjParams(batch=B, in_features=K, out_features=N, dtype=_dtype_code(x.dtype),
+                      out_dtype=_dtype_code(out_dtype if out_dtype is not None else x.dtype),
+                      num_splits=int(num_splits), reserved=0)
+
+
+def output_proj_workspace_bytes(params: ProjParams) -> int:
+    return int(lib().mla_output_proj_workspace_bytes(ctypes.byref(params)))
+
+
+def output_proj(x, w, *, out=None, workspace=None, out_dtype=None, num_splits=0, stream=None,
+                params: ProjParams | None = None):
+    """Output projection y = x w^T (``mla_output_proj``): x [B, K], w [N, K] -> y [B, N]."""
+    if params is None:
+        params = proj_params(x, w, out_dtype=out_dtype, num_splits=num_splits)
+    if out is None:
+        odt = torch.float32 if params.out_dtype == MLA_F32 else torch.bfloat16
+        out = torch.empty((params.batch, params.out_features), dtype=odt, device=x.device)
+    need = output_proj_workspace_bytes(params)
+    if need == 0:
+        _check(lib().mla_output_proj(ctypes.byref(params), None, None, None, None, 0, None))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().mla_output_proj(ctypes.byref(params), _ptr(x), _ptr(w), _ptr(out),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def fold_value_output(w_o, w_uv, *, out=None, stream=None):
+    """W_OV [d_model, H*d_c] = W_O [d_model, H*d_v] folded with W_UV [H, d_v, d_c]
+    (``mla_fold_value_output``)."""
+    H, dv, dc = w_uv.shape
+    d_model = w_o.shape[0]
+    if out is None:
+        out = torch.empty((d_model, H * dc), dtype=w_o.dtype, device=w_o.device)
+    _check(lib().mla_fold_value_output(d_model, H, dv, dc, _dtype_code(w_o.dtype), _ptr(w_o),
+                                       _ptr(w_uv), _ptr(out), _stream(stream)))
     return out
 
 

@@ -504,6 +504,10 @@ __device__ void recompute_partial(const CacheView &cv, int H, int S, int v, int 
     __syncthreads();
 }
 
+// kUpProj = false: write the merged latent o_lat [rows][H][512] itself (the
+// attention output before the up-projection, for a caller that folds W_UV
+// into its output projection) instead of W_UV[h] o_lat.
+template <bool kUpProj>
 __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
                                                                 float *__restrict__ part_o,
                                                                 float *__restrict__ part_ml,
@@ -549,10 +553,12 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
     const int r8 = lane >> 3, p8 = lane & 7;
     const u32x4 *wbase = reinterpret_cast<const u32x4 *>(w_uv + (static_cast<int64_t>(h) * DV + 32 * wv_id + r8) * DC) + p8;
     u32x4 wq[4][8];
+    if constexpr (kUpProj) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) wq[j][c] = wbase[j * 8 * (DC / 8) + 8 * c];
+            for (int c = 0; c < 8; ++c) wq[j][c] = wbase[j * 8 * (DC / 8) + 8 * c];
+    }
 
     // Marked (NaN) splits are recomputed first, in ascending order, and the
     // partials reloaded.
@@ -595,8 +601,19 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
     __syncthreads();
     if (tid < DC / 4) {
         const f32x4 o = (half_sum[0][tid] + half_sum[1][tid]) * inv_l;
-        *reinterpret_cast<f32x4 *>(ol + 4 * tid) = o;
+        if constexpr (kUpProj) {
+            *reinterpret_cast<f32x4 *>(ol + 4 * tid) = o;
+        } else {
+            const int64_t oi = (static_cast<int64_t>(v) * H + h) * DC + 4 * tid;
+            if (out_bf16) {
+                const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+                *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(out) + oi) = pk;
+            } else {
+                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + oi) = o;
+            }
+        }
     }
+    if constexpr (!kUpProj) return;
     __syncthreads();
 
     // out[b][h][v] = W_UV[h][v] . o_lat: each row's 8 lanes add their 64
@@ -641,6 +658,7 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
                               const void *kpe, const int32_t *seqlens, void *out,
                               const DecodeWorkspace &ws, hipStream_t st, hipEvent_t const *events)
 {
+    // w_uv == nullptr: write the merged latent instead of W_UV[h] o_lat.
     uint16_t *qa = static_cast<uint16_t *>(ws.q);
     const int rows = s.B * s.T;  // query rows
     if (events) (void)hipEventRecord(events[0], st);
@@ -668,9 +686,12 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
     CacheView cv{s.T, s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb, s.ckv_sn,
                  static_cast<const uint16_t *>(kpe), s.kpe_sb, s.kpe_sn, seqlens, qa,
                  s.scale * kLog2e};
-    merge_upproj_bf16_kernel<<<grid, 256, 0, st>>>(s.H, s.S, ws.part_o, ws.part_ml,
-                                                   static_cast<const uint16_t *>(w_uv), out, s.out_bf16,
-                                                   cv);
+    if (w_uv)
+        merge_upproj_bf16_kernel<true><<<grid, 256, 0, st>>>(
+            s.H, s.S, ws.part_o, ws.part_ml, static_cast<const uint16_t *>(w_uv), out, s.out_bf16, cv);
+    else
+        merge_upproj_bf16_kernel<false><<<grid, 256, 0, st>>>(
+            s.H, s.S, ws.part_o, ws.part_ml, nullptr, out, s.out_bf16, cv);
     hipError_t e = hipGetLastError();
     if (events) (void)hipEventRecord(events[3], st);
     return e;

@@ -177,7 +177,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
 }  // namespace
 
 // Fixed-order merge of the S split partials of one (head, query row) followed
-// by out = W_UV[h] o_lat.
+// by out = W_UV[h] o_lat, or (w_uv == nullptr) the merged latent o_lat itself,
+// [rows][H][dc].
 template <typename TW>
 __global__ __launch_bounds__(kThreads) void merge_upproj_generic_kernel(
     int H, int S, int dc, int dv, const float *part_o, const float *part_ml, const TW *w_uv,
@@ -207,7 +208,9 @@ __global__ __launch_bounds__(kThreads) void merge_upproj_generic_kernel(
         for (int sp = 0; sp < S; ++sp)
             if (wt[sp] != 0.f) acc = fmaf(wt[sp], part_o[(base + static_cast<int64_t>(sp) * H) * dc + j], acc);
         ol[j] = acc * inv;
+        if (!w_uv) store_out(out, (static_cast<int64_t>(b) * H + h) * dc + j, acc * inv, out_bf16);
     }
+    if (!w_uv) return;
     __syncthreads();
     for (int v = tid; v < dv; v += kThreads) {
         const int64_t wrow = (static_cast<int64_t>(h) * dv + v) * dc;

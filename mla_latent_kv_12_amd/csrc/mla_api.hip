@@ -279,6 +279,58 @@ mla_status mla_decode_profiled(const mla_decode_params *p, const void *q_nope,
     return ok();
 }
 
+mla_status mla_decode_latent(const mla_decode_params *p, const void *q_nope, const void *q_rope,
+                             const void *w_uk, const void *ckv_cache, const void *kpe_cache,
+                             const int32_t *seqlens, void *o_lat, void *workspace,
+                             size_t workspace_bytes, void *stream)
+{
+    if (!p) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+    mla_decode_params q = *p;  // d_v plays no part: check with the implemented value
+    q.d_v = p->dtype == MLA_BF16 ? 128 : 1;
+    p = &q;
+    mla_status st = check_decode_params(p);
+    if (st != MLA_OK) return st;
+    if (!q_nope || !w_uk || !ckv_cache || !seqlens || !o_lat)
+        return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (p->d_r > 0 && (!q_rope || !kpe_cache))
+        return fail(MLA_ERR_INVALID_ARG, "NULL q_rope or kpe_cache with d_r > 0");
+    const bool bf16 = p->dtype == MLA_BF16;
+    if (bf16) {
+        if (!aligned(ckv_cache, 16) || !aligned(kpe_cache, 16) || p->ckv_stride_n % 8 ||
+            p->kpe_stride_n % 8 || p->ckv_stride_b % 8 || p->kpe_stride_b % 8)
+            return fail(MLA_ERR_INVALID_ARG,
+                        "bf16 caches need 16-byte aligned rows (pointers %% 16, strides %% 8 elements)");
+        if (!aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(w_uk, 16) || !aligned(o_lat, 16))
+            return fail(MLA_ERR_INVALID_ARG, "bf16 path needs 16-byte aligned q, weights and output");
+    } else {
+        if (!aligned(q_nope, 4) || (q_rope && !aligned(q_rope, 4)) || !aligned(w_uk, 4) ||
+            !aligned(ckv_cache, 4) || (kpe_cache && !aligned(kpe_cache, 4)) || !aligned(o_lat, 4))
+            return fail(MLA_ERR_INVALID_ARG, "fp32 tensors must be 4-byte aligned");
+    }
+    mla::DecodeShape s = make_shape(p);
+    mla::DecodeWorkspace ws;
+    const size_t need = mla::decode_workspace_layout(s, bf16, &ws, workspace);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign))
+        return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu at %p)",
+                    need, workspace_bytes, workspace);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (debug_checks()) {
+        st = check_seqlens_debug(seqlens, p->batch, p->n_max, hs, 1);
+        if (st != MLA_OK) return st;
+    }
+    hipError_t e;
+    if (bf16)
+        e = mla::launch_decode_bf16(s, q_nope, q_rope, w_uk, nullptr, ckv_cache, kpe_cache, seqlens,
+                                    o_lat, ws, hs, nullptr);
+    else
+        e = mla::launch_decode_f32(s, static_cast<const float *>(q_nope),
+                                   static_cast<const float *>(q_rope), static_cast<const float *>(w_uk),
+                                   nullptr, static_cast<const float *>(ckv_cache),
+                                   static_cast<const float *>(kpe_cache), seqlens, o_lat, ws, hs, nullptr);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 mla_status mla_decode(const mla_decode_params *p, const void *q_nope, const void *q_rope,
                       const void *w_uk, const void *w_uv, const void *ckv_cache,
                       const void *kpe_cache, const int32_t *seqlens, void *out, void *workspace,
@@ -598,6 +650,106 @@ mla_status mla_cache_append(const mla_append_params *p, const void *h, const voi
     return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+mla_status check_proj_params(const mla_proj_params *p)
+{
+    if (!p) return fail(MLA_ERR_INVALID_ARG, "params is NULL");
+    if (p->batch < 1 || p->in_features < 1 || p->out_features < 1)
+        return fail(MLA_ERR_INVALID_ARG, "non-positive size");
+    if (p->reserved != 0) return fail(MLA_ERR_INVALID_ARG, "reserved field must be 0");
+    if ((p->dtype != MLA_F32 && p->dtype != MLA_BF16) ||
+        (p->out_dtype != MLA_F32 && p->out_dtype != MLA_BF16))
+        return fail(MLA_ERR_UNSUPPORTED, "unknown dtype");
+    if (p->batch > 65535 || p->in_features > (1 << 24) || p->out_features > (1 << 24) ||
+        p->batch * p->out_features >= ((int64_t)1 << 31))
+        return fail(MLA_ERR_UNSUPPORTED, "sizes beyond the supported range");
+    if ((uint64_t)p->out_features * (uint64_t)p->in_features * (p->dtype == MLA_BF16 ? 2u : 4u) >=
+        (1ull << 40))
+        return fail(MLA_ERR_UNSUPPORTED, "weight beyond the supported size");
+    if (p->dtype == MLA_BF16 && p->in_features % 64)
+        return fail(MLA_ERR_UNSUPPORTED, "bf16 projection needs in_features %% 64 == 0");
+    if (p->num_splits < 0 || p->num_splits > mla::kMaxSplits)
+        return fail(MLA_ERR_INVALID_ARG, "num_splits must be in [0, %d]", mla::kMaxSplits);
+    return MLA_OK;
+}
+
+mla::ProjShape make_proj_shape(const mla_proj_params *p)
+{
+    mla::ProjShape s;
+    s.B = (int)p->batch;
+    s.K = (int)p->in_features;
+    s.N = (int)p->out_features;
+    s.bf16 = p->dtype == MLA_BF16;
+    s.out_bf16 = p->out_dtype == MLA_BF16;
+    // Slices of about 1024 input features: enough workgroups to stream the
+    // weight from every CU (e.g. 112 row blocks x 16 slices for 7168 x 16384).
+    int64_t S = p->num_splits > 0 ? p->num_splits : (p->in_features + 1023) / 1024;
+    if (S < 1) S = 1;
+    if (S > mla::kMaxSplits) S = mla::kMaxSplits;
+    s.S = (int)S;
+    return s;
+}
+
+size_t proj_workspace(const mla::ProjShape &s)
+{
+    return round_up((size_t)s.S * (size_t)s.B * (size_t)s.N * 4, kAlign);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_output_proj_workspace_bytes(const mla_proj_params *p)
+{
+    if (check_proj_params(p) != MLA_OK) return 0;
+    return proj_workspace(make_proj_shape(p));
+}
+
+mla_status mla_output_proj(const mla_proj_params *p, const void *x, const void *w, void *y,
+                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    mla_status st = check_proj_params(p);
+    if (st != MLA_OK) return st;
+    if (!x || !w || !y) return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+    const bool bf16 = p->dtype == MLA_BF16;
+    if (!aligned(x, bf16 ? 16 : 4) || !aligned(w, bf16 ? 16 : 4) ||
+        !aligned(y, p->out_dtype == MLA_BF16 ? 2 : 4))
+        return fail(MLA_ERR_INVALID_ARG, "x and w must be %d-byte aligned", bf16 ? 16 : 4);
+    mla::ProjShape s = make_proj_shape(p);
+    const size_t need = proj_workspace(s);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign))
+        return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu)",
+                    need, workspace_bytes);
+    hipError_t e = mla::launch_output_proj(s, x, w, y, static_cast<float *>(workspace),
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "projection launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+mla_status mla_fold_value_output(int64_t d_model, int64_t heads, int64_t d_v, int64_t d_c,
+                                 int32_t dtype, const void *w_o, const void *w_uv, void *w_ov,
+                                 void *stream)
+{
+    if (d_model < 1 || heads < 1 || d_v < 1 || d_c < 1)
+        return fail(MLA_ERR_INVALID_ARG, "non-positive size");
+    if (dtype != MLA_F32 && dtype != MLA_BF16) return fail(MLA_ERR_UNSUPPORTED, "unknown dtype");
+    if (d_model > (1 << 24) || heads > 65535 || d_v > (1 << 20) || d_c > (1 << 20) ||
+        (uint64_t)d_model * (uint64_t)heads * (uint64_t)(d_v > d_c ? d_v : d_c) >= (1ull << 40))
+        return fail(MLA_ERR_UNSUPPORTED, "sizes beyond the supported range");
+    if (!w_o || !w_uv || !w_ov) return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
+    const size_t a = dtype == MLA_BF16 ? 2 : 4;
+    if (!aligned(w_o, a) || !aligned(w_uv, a) || !aligned(w_ov, a))
+        return fail(MLA_ERR_INVALID_ARG, "tensors must be %zu-byte aligned", a);
+    hipError_t e = mla::launch_fold_value_output((int)d_model, (int)heads, (int)d_v, (int)d_c,
+                                                 dtype == MLA_BF16, w_o, w_uv, w_ov,
+                                                 static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "fold launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 uint64_t mla_kv_cache_bytes(int64_t n_layers, int64_t batch, int64_t seq_len, int64_t d_c,
                             int64_t d_r, int64_t bytes_per_elem)
 {
@@ -621,6 +773,6 @@ const char *mla_status_string(mla_status s)
 
 const char *mla_last_error(void) { return g_err; }
 
-int mla_version(void) { return 10100; }
+int mla_version(void) { return 10200; }
 
 }  // extern "C"

@@ -99,6 +99,18 @@ hipError_t launch_prefill_bf16(const PrefillShape &s, const void *q_nope, const 
                                const void *kpe, const int32_t *seqlens, void *out, void *kbuf,
                                void *vbuf, hipStream_t st);
 
+// Output projection y[B][N] = x[B][K] w[N][K]^T, K cut into S slices.
+struct ProjShape {
+    int B, K, N, S;
+    bool bf16;      // x and w bf16 (MFMA path; K % 64 == 0), else fp32
+    int out_bf16;
+};
+// part: S * B * N fp32 of workspace.
+hipError_t launch_output_proj(const ProjShape &p, const void *x, const void *w, void *y,
+                              float *part, hipStream_t st);
+hipError_t launch_fold_value_output(int N, int H, int dv, int dc, bool bf16, const void *w_o,
+                                    const void *w_uv, void *w_ov, hipStream_t st);
+
 struct AppendShape {
     int B, d_model, dc, dr;
     int64_t n_max;

@@ -241,6 +241,58 @@ def test_prefill_absorbed_rejects_null_pointers_and_small_workspace():
                                     None) == mla.MLA_ERR_WORKSPACE
 
 
+def _proj_params(**kw):
+    base = dict(batch=8, in_features=16384, out_features=7168, dtype=mla.MLA_BF16,
+                out_dtype=mla.MLA_BF16, num_splits=0, reserved=0)
+    base.update(kw)
+    return binding.ProjParams(**base)
+
+
+def test_output_proj_workspace_and_validation():
+    assert ctypes.sizeof(binding.ProjParams) == 3 * 8 + 4 * 4
+    # auto: slices of ~1024 input features, fp32 partials of every slice
+    assert mla.output_proj_workspace_bytes(_proj_params()) == 16 * 8 * 7168 * 4
+    assert mla.output_proj_workspace_bytes(_proj_params(in_features=65536)) == 64 * 8 * 7168 * 4
+    assert mla.output_proj_workspace_bytes(_proj_params(num_splits=3)) == 3 * 8 * 7168 * 4
+    assert mla.output_proj_workspace_bytes(_proj_params(in_features=100)) == 0   # bf16: K % 64
+    assert mla.output_proj_workspace_bytes(_proj_params(in_features=100, dtype=mla.MLA_F32)) > 0
+    lib = binding.lib()
+    vp = ctypes.c_void_p
+    for kw, status in [(dict(batch=0), "INVALID_ARG"), (dict(reserved=1), "INVALID_ARG"),
+                       (dict(num_splits=-1), "INVALID_ARG"), (dict(dtype=9), "UNSUPPORTED"),
+                       (dict(in_features=96), "UNSUPPORTED")]:
+        pp = _proj_params(**kw)
+        rc = lib.mla_output_proj(ctypes.byref(pp), vp(0x1000), vp(0x2000), vp(0x3000),
+                                 vp(0x100000), 1 << 40, None)
+        assert rc == getattr(mla, "MLA_ERR_" + status), kw
+    pp = _proj_params()
+    assert lib.mla_output_proj(ctypes.byref(pp), vp(0x1008), vp(0x2000), vp(0x3000),
+                               vp(0x100000), 1 << 40, None) == mla.MLA_ERR_INVALID_ARG  # x % 16
+    assert lib.mla_output_proj(ctypes.byref(pp), vp(0x1000), vp(0x2000), vp(0x3000),
+                               vp(0x100000), 100, None) == mla.MLA_ERR_WORKSPACE
+
+
+def test_fold_and_decode_latent_reject_before_launch():
+    lib = binding.lib()
+    vp = ctypes.c_void_p
+    f = lib.mla_fold_value_output
+    assert f(0, 128, 128, 512, mla.MLA_BF16, vp(0x1000), vp(0x2000), vp(0x3000), None) == \
+        mla.MLA_ERR_INVALID_ARG
+    assert f(7168, 128, 128, 512, 5, vp(0x1000), vp(0x2000), vp(0x3000), None) == \
+        mla.MLA_ERR_UNSUPPORTED
+    assert f(7168, 128, 128, 512, mla.MLA_BF16, vp(0), vp(0x2000), vp(0x3000), None) == \
+        mla.MLA_ERR_INVALID_ARG
+    p = _v3_params(d_v=1)   # d_v is not used by the latent form
+    d = lib.mla_decode_latent
+    assert d(ctypes.byref(p), vp(0x1000), vp(0x2000), vp(0x3000), vp(0x5000), vp(0x5400),
+             vp(0x6000), vp(0x7000), vp(0x100000), 10, None) == mla.MLA_ERR_WORKSPACE
+    assert d(ctypes.byref(p), vp(0x1000), vp(0x2000), vp(0x3000), vp(0x5000), vp(0x5400),
+             vp(0x6000), vp(0), vp(0x100000), 1 << 40, None) == mla.MLA_ERR_INVALID_ARG
+    assert d(ctypes.byref(_v3_params(heads=96)), vp(0x1000), vp(0x2000), vp(0x3000), vp(0x5000),
+             vp(0x5400), vp(0x6000), vp(0x7000), vp(0x100000), 1 << 40, None) == \
+        mla.MLA_ERR_UNSUPPORTED
+
+
 def _append_params(**kw):
     base = dict(batch=8, d_model=7168, d_c=512, d_r=64, n_max=4096, ckv_stride_b=4096 * 576,
                 ckv_stride_n=576, kpe_stride_b=4096 * 576, kpe_stride_n=576, rope_base=0.0,
