@@ -523,10 +523,34 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
     __shared__ __attribute__((aligned(16))) f32x4 half_sum[2][DC / 4];
     __shared__ __attribute__((aligned(16))) float ol[DC];
 
+    const int64_t base = static_cast<int64_t>(v) * S * H + h;  // row of split 0
+    if constexpr (!kUpProj) {
+        if (S == 1) {  // one split: o = O / l, no cross-split weighting
+            float m0 = part_ml[base * 2], l0 = part_ml[base * 2 + 1];
+            if (__builtin_isnan(m0)) {  // marked: recompute with the split's true maximum
+                recompute_partial(cv, H, 1, v, 0, h, part_o, part_ml);
+                m0 = part_ml[base * 2];
+                l0 = part_ml[base * 2 + 1];
+            }
+            if (tid < DC / 4) {
+                // an empty split (m = -inf) never wrote O: its row is zeros
+                const bool live = m0 != -INFINITY && l0 > 0.f;
+                const f32x4 o = live ? *reinterpret_cast<const f32x4 *>(part_o + base * DC + 4 * tid) * (1.f / l0)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+                const int64_t oi = (static_cast<int64_t>(v) * H + h) * DC + 4 * tid;
+                if (out_bf16) {
+                    const u32x2 pk = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+                    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(out) + oi) = pk;
+                } else {
+                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + oi) = o;
+                }
+            }
+            return;
+        }
+    }
     // Every load is issued up front, in the order the data is needed, so the
     // whole merge costs one memory round trip: (m, l) of split tid, then this
     // thread's first 16 partial pieces, then its W_UV pieces.
-    const int64_t base = static_cast<int64_t>(v) * S * H + h;  // row of split 0
     // Loads are unconditional (indices past the last split are clamped) so
     // that no branch makes the compiler wait on them early; the surplus values
     // are discarded by selects.
@@ -649,6 +673,68 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
     }
 }
 
+// Batched up-projection for many query rows: out[v][h][i] = W_UV[h][i] . o[v][h]
+// for 32 query rows per workgroup and the 128 output features of head h
+// (wave w: features 32 w .. 32 w + 31), on MFMA.  A = W_UV rows straight from
+// global memory; B = the fp32 latents, each split into a bf16 high part and
+// a bf16 remainder (x = hi + lo to about 2^-17 relative), two MFMAs per K
+// step, so the product keeps the latent's fp32 precision.  W_UV[h] is read
+// once per 32 query rows.  Grid (H, ceil(rows / 32)), 256 threads.
+__global__ __launch_bounds__(256) void upproj_bf16_kernel(int H, int rows,
+                                                          const float *__restrict__ o_lat,
+                                                          const uint16_t *__restrict__ w_uv,
+                                                          void *__restrict__ out, int out_bf16)
+{
+    const int h = blockIdx.x, v0 = blockIdx.y * 32;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int half = lane >> 5, l32 = lane & 31;
+    // A: W_UV[h] row 32 wv + l32, elements 16 s + 8 half .. + 7 of step s
+    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(w_uv + (static_cast<int64_t>(h) * DV + 32 * wv + l32) * DC) + half;
+    // B: latent of query row v0 + l32 (clamped inside the rows), same elements
+    const int vr = min(v0 + l32, rows - 1);
+    const f32x4 *orow = reinterpret_cast<const f32x4 *>(o_lat + (static_cast<int64_t>(vr) * H + h) * DC) + 2 * half;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    constexpr int kU = 4;
+    for (int s0 = 0; s0 < DC / 16; s0 += kU) {
+        u32x4 a[kU];
+        f32x4 x0[kU], x1[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            a[u] = wrow[2 * (s0 + u)];
+            x0[u] = orow[4 * (s0 + u)];
+            x1[u] = orow[4 * (s0 + u) + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const float x[8] = {x0[u][0], x0[u][1], x0[u][2], x0[u][3],
+                                x1[u][0], x1[u][1], x1[u][2], x1[u][3]};
+            u32x4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hi[e] = pack_bf16(x[2 * e], x[2 * e + 1]);
+                lo[e] = pack_bf16(x[2 * e] - bf16lo(hi[e]), x[2 * e + 1] - bf16hi(hi[e]));
+            }
+            acc = mfma32(a[u], hi, acc);
+            acc = mfma32(a[u], lo, acc);
+        }
+    }
+    // acc[r] is feature 32 wv + 8 (r / 4) + 4 half + r % 4 of query row v0 + l32
+    if (v0 + l32 >= rows) return;
+    const int64_t orow_out = (static_cast<int64_t>(v0 + l32) * H + h) * DV + 32 * wv + 4 * half;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const f32x4 v4 = {acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        if (out_bf16) {
+            const u32x2 pk = {pack_bf16(v4[0], v4[1]), pack_bf16(v4[2], v4[3])};
+            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(out) + orow_out + 8 * g) = pk;
+        } else {
+            *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + orow_out + 8 * g) = v4;
+        }
+    }
+}
+
 }  // namespace
 
 int decode_bf16_heads_per_block(int H) { return H % 128 == 0 ? 128 : 0; }
@@ -686,13 +772,24 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
     CacheView cv{s.T, s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb, s.ckv_sn,
                  static_cast<const uint16_t *>(kpe), s.kpe_sb, s.kpe_sn, seqlens, qa,
                  s.scale * kLog2e};
-    if (w_uv)
+    hipError_t e;
+    if (w_uv && batched_upproj(s, true)) {
+        // many query rows: merge into fp32 latents, then one product per head
+        merge_upproj_bf16_kernel<false><<<grid, 256, 0, st>>>(s.H, s.S, ws.part_o, ws.part_ml,
+                                                              nullptr, ws.o_lat, 0, cv);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        dim3 ugrid(s.H, (rows + 31) / 32);
+        upproj_bf16_kernel<<<ugrid, 256, 0, st>>>(s.H, rows, ws.o_lat,
+                                                  static_cast<const uint16_t *>(w_uv), out, s.out_bf16);
+    } else if (w_uv) {
         merge_upproj_bf16_kernel<true><<<grid, 256, 0, st>>>(
             s.H, s.S, ws.part_o, ws.part_ml, static_cast<const uint16_t *>(w_uv), out, s.out_bf16, cv);
-    else
+    } else {
         merge_upproj_bf16_kernel<false><<<grid, 256, 0, st>>>(
             s.H, s.S, ws.part_o, ws.part_ml, nullptr, out, s.out_bf16, cv);
-    hipError_t e = hipGetLastError();
+    }
+    e = hipGetLastError();
     if (events) (void)hipEventRecord(events[3], st);
     return e;
 }

@@ -178,16 +178,19 @@ size_t decode_workspace_layout(const DecodeShape &s, bool bf16, DecodeWorkspace 
     // the fp32 path rotates q_rope into its own buffer; the bf16 absorb kernel
     // rotates while it copies q_rope beside q~
     const size_t rbytes = (s.q_rope_base > 0.0 && !bf16) ? rows * (size_t)s.dr * 4 : 0;
+    const size_t lbytes = batched_upproj(s, bf16) ? rows * (size_t)s.dc * 4 : 0;
     const size_t off_o = round_up(qbytes, kAlign);
     const size_t off_ml = off_o + round_up(obytes, kAlign);
     const size_t off_r = off_ml + round_up(mlbytes, kAlign);
-    const size_t total = off_r + round_up(rbytes, kAlign);
+    const size_t off_l = off_r + round_up(rbytes, kAlign);
+    const size_t total = off_l + round_up(lbytes, kAlign);
     if (ws) {
         char *b = static_cast<char *>(base);
         ws->q = b;
         ws->part_o = reinterpret_cast<float *>(b + off_o);
         ws->part_ml = reinterpret_cast<float *>(b + off_ml);
         ws->q_rope = rbytes ? b + off_r : nullptr;
+        ws->o_lat = lbytes ? reinterpret_cast<float *>(b + off_l) : nullptr;
     }
     return total;
 }

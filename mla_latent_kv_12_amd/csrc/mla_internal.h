@@ -35,7 +35,16 @@ struct DecodeWorkspace {
     float *part_o;    // [rows][S][H][dc]   un-normalised latent accumulators per split
     float *part_ml;   // [rows][S][H][2]    running max (log2 units) and softmax mass per split
     void *q_rope;     // fp32 path with q rotation: [rows][H][dr] q_rope rotated at its position
+    float *o_lat;     // bf16 path with many query rows: [rows][H][dc] merged latents
 };
+
+// With many (query row, head) pairs (an absorbed prefill) the bf16 path
+// merges into fp32 latents and up-projects them with one batched product per
+// head, instead of re-reading W_UV[h] for every query row.
+inline bool batched_upproj(const DecodeShape &s, bool bf16)
+{
+    return bf16 && static_cast<int64_t>(s.B) * s.T * s.H >= 8192;
+}
 
 size_t decode_workspace_layout(const DecodeShape &s, bool bf16, DecodeWorkspace *ws_or_null,
                                void *base);

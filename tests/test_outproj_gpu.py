@@ -68,16 +68,17 @@ def test_output_proj_shapes_and_slices(dtype, B, K, N, S):
     assert np.array_equal(y, again)
 
 
+@pytest.mark.parametrize("splits", [1, 3])
 @pytest.mark.parametrize("dtype,dims,H,L", [("bf16", V3, 128, [300, 77]),
                                             ("f32", TINY, 4, [128, 9])])
-def test_decode_latent_matches_oracle(dtype, dims, H, L):
-    say(f"decode latent {dtype} H={H} L={L}")
+def test_decode_latent_matches_oracle(dtype, dims, H, L, splits):
+    say(f"decode latent {dtype} H={H} L={L} splits={splits}")
     case = datagen.make_decode_case(B=2, H=H, n_max=max(L), dtype=dtype, seed=4300 + L[1],
                                     seqlens=L, **dims)
     t = decode_tensors(case)
     o = mla.decode_latent(t["q_nope"], t["q_rope"], t["w_uk"], t["ckv_cache"], t["kpe_cache"],
                           t["seqlens"], softmax_scale=case.scale, out_dtype=torch.float32,
-                          num_splits=3)
+                          num_splits=splits)
     torch.cuda.synchronize()
     ref = oracle.decode_latent(case.q_nope, case.q_rope, case.w_uk, case.ckv, case.kpe,
                                case.seqlens, case.scale)
@@ -85,7 +86,7 @@ def test_decode_latent_matches_oracle(dtype, dims, H, L):
     # the up-projected form of the same call is mla_decode's output
     out = mla.decode(t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv_cache"],
                      t["kpe_cache"], t["seqlens"], softmax_scale=case.scale,
-                     out_dtype=torch.float32, num_splits=3)
+                     out_dtype=torch.float32, num_splits=splits)
     torch.cuda.synchronize()
     wuv = (datagen.bf16_to_f32(case.w_uv) if dtype == "bf16" else case.w_uv).astype(np.float64)
     up = np.einsum("hvc,bhc->bhv", wuv, to_host_f64(o))

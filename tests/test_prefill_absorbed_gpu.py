@@ -86,6 +86,23 @@ def test_absorbed_prefill_bf16_split_counts_and_repeatability():
         assert np.array_equal(out, again), f"S={s}: two runs differ"
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_absorbed_prefill_many_rows_with_marked_splits(splits):
+    """64 queries x 128 heads per sequence take the batched up-projection
+    (merge into fp32 latents, then one product per head); sequence 0's queries
+    all put a dominant weight on a late key, so its splits are marked for the
+    recompute with their true maximum."""
+    say(f"absorbed prefill bf16 T=64, dominant late key, splits={splits}")
+    case = chunk_case(2, 64, [1000, 700], 128, "bf16", 2701)
+    star = 900                                   # visible to every query of sequence 0
+    kr = datagen.bf16_to_f32(case.cache[0, star, 512:])
+    qr = datagen.bf16_to_f32(case.q_rope).copy()
+    qr[0] = 40.0 * kr
+    case.q_rope = datagen.bf16_bits(qr)
+    out = run_absorbed(case, num_splits=splits)
+    assert_close(out, oracle_all(case), "bf16", f"all rows, S={splits}")
+
+
 def test_absorbed_prefill_single_token_is_decode_bitwise():
     say("absorbed prefill T=1 vs decode, same split count (bitwise)")
     case = chunk_case(3, 1, [200, 33, 1], 128, "bf16", 2401)
