@@ -6,8 +6,8 @@
 //      purpose: this is the naive form the pages contrast with absorption --
 //      distaisys deep-dive, section 3; songhuiming walk-through, MLA step 2,
 //      where all cached latents are up-projected to K and V).  One MFMA GEMM
-//      per (head, 256-token block, weight), head-major output so that each
-//      head's keys and values are contiguous.
+//      workgroup per (head, 256-token block) computes both, head-major output
+//      so that each head's keys and values are contiguous.
 //   2. causal attention: query t (position L - T + t) attends over rows
 //      n <= its position with key [K_nope ; k^R] (k^R shared by all heads)
 //      and value V.  One workgroup of 8 waves per (256 queries, head,
@@ -34,88 +34,114 @@ __device__ __forceinline__ int clamp_len(int32_t v, int64_t n_max)
 
 // ---------------------------------------------------------------------------
 // 1. decompress GEMM: D[token][feature] = c[token][:] . W[feature][:] for the
-//    128 features of one head and 256 tokens.  8 waves as 2 (features) x 4
-//    (tokens) of 64 x 64.  K (the 512 latent channels) in chunks of 32: each
-//    chunk is 128 W rows + 256 c rows of 64 bytes, loaded direct-to-LDS,
-//    three chunks deep, 72 KiB per workgroup so that two workgroups share a
-//    CU and one's start-up overlaps the other's MFMAs.  Row r's 16-byte
-//    pieces are XOR-swizzled by (r / 4) & 3, so the MFMA operand reads (16
-//    consecutive rows at one piece) touch 16 distinct bank groups.  The bf16
-//    result is staged in LDS and written as whole 256-byte rows of the
-//    head-major output.
+//    128 features of one head, both weights (W_UK -> K_nope, W_UV -> V), and
+//    256 tokens.  16 waves: waves 0-7 take W_UK, waves 8-15 W_UV, each group
+//    as 2 (features) x 4 (tokens) waves of 64 x 64, so every chunk of c is
+//    read from L2 once for both products.  K (the 512 latent channels) in
+//    chunks of 32: each chunk is 2 x 128 W rows + 256 c rows of 64 bytes
+//    (32 KiB, one W load and one c load per wave), loaded direct-to-LDS
+//    into four buffers, three chunks in flight.  Row r's 16-byte pieces are
+//    XOR-swizzled by (r / 4) & 3, so the MFMA operand reads (16 consecutive
+//    rows at one piece) touch 16 distinct bank groups.  The bf16 results are
+//    staged in LDS and written as whole 256-byte rows of the head-major
+//    outputs.
 // ---------------------------------------------------------------------------
-constexpr int kGF = 128;                                // features per workgroup (one head)
+constexpr int kGF = 128;                                // features per weight (one head)
 constexpr int kGN = 256;                                // tokens per workgroup
 constexpr int kGK = 32;                                 // K chunk
-constexpr int kGWaves = 8;
+constexpr int kGWaves = 16;                             // 2 weights x 8 waves
 constexpr int kGThreads = 64 * kGWaves;
+constexpr int kGStages = 4;                             // chunk buffers
 constexpr int kGRowB = kGK * 2;                         // 64 B per LDS row of a chunk
 constexpr int kGPieces = kGRowB / 16;                   // 16-byte pieces per row
-constexpr int kGRowsPerLoad = 1024 / kGRowB;            // rows per 1-KiB load
-constexpr int kGWLoads = kGF / kGRowsPerLoad;           // W loads per chunk
-constexpr int kGWBytes = kGF * kGRowB;                  // 8 KiB
-constexpr int kGStage = kGWBytes + kGN * kGRowB;        // 24 KiB
-constexpr int kGDmaPerWave = kGStage / 1024 / kGWaves;  // 3
+constexpr int kGRowsPerLoad = 1024 / kGRowB;            // 16 rows per 1-KiB load
+constexpr int kGWBytes = kGF * kGRowB;                  // 8 KiB per weight
+constexpr int kGCOff = 2 * kGWBytes;                    // c rows follow both weights
+constexpr int kGStage = kGCOff + kGN * kGRowB;          // 32 KiB
 constexpr int kGChunks = DC / kGK;                      // 16
 constexpr int kGOutRow = DN * 2 + 16;                   // 272 B epilogue staging row
+constexpr int kGOutBytes = kGN * kGOutRow;              // 68 KiB per weight
+constexpr int kGLds = kGStages * kGStage > 2 * kGOutBytes ? kGStages * kGStage : 2 * kGOutBytes;
 static_assert(kGF == DN && kGF == DV, "one workgroup covers one head's features");
-static_assert(kGDmaPerWave * 1024 * kGWaves == kGStage, "whole loads per wave");
-static_assert(kGWLoads % kGWaves == 0, "load e of every wave is a W load or a c load");
-static_assert(2 * (3 * kGStage) <= 160 * 1024, "two workgroups per CU");
-static_assert(kGN * kGOutRow <= 3 * kGStage, "epilogue staging fits in the chunk buffers");
+static_assert(kGCOff == 1024 * kGWaves && kGN * kGRowB == 1024 * kGWaves,
+              "per chunk: load wv is a W load (W_UK for waves 0-7), load 16 + wv a c load");
+static_assert(kGLds <= 160 * 1024, "LDS budget");
 
 // Piece swizzle of chunk row r: the rows of one 16-row group take the 16
 // (row phase, piece) combinations of the 16 bank groups.
 __host__ __device__ constexpr int gemm_swz(int r) { return (r / (16 / kGPieces)) % kGPieces; }
 
-__global__ __launch_bounds__(kGThreads, 2) void decompress_gemm_bf16_kernel(
+constexpr int kGHeadGroup = 4;   // heads per item group of one XCD
+constexpr int kGBlockGroup = 8;  // token blocks per item group
+
+// (head, token block) of workgroup i = blockIdx.x + H blockIdx.y of one
+// sequence.  Workgroups are dispatched round-robin over the 8 XCDs; when H
+// divides by 8, XCD x = i % 8 takes the heads x, x + 8, ... and walks its
+// items in groups of kGHeadGroup heads x kGBlockGroup token blocks, so the
+// weights and latent rows that its resident workgroups read at one time
+// stay within its L2.  The map is a bijection for any H and block count.
+__device__ __forceinline__ void gemm_item(int H, int nblk, int &h, int &nb)
+{
+    const int i = blockIdx.x + H * blockIdx.y;
+    if (H % 8 != 0) {
+        h = blockIdx.x;
+        nb = blockIdx.y;
+        return;
+    }
+    const int hpx = H / 8, x = i & 7;
+    int j = i >> 3;
+    int hg = kGHeadGroup;
+    while (hpx % hg) hg >>= 1;                  // a power-of-two divisor of hpx
+    const int t = j / (hpx * kGBlockGroup);     // token-block group (the last may be partial)
+    j -= t * hpx * kGBlockGroup;
+    const int sz = min(kGBlockGroup, nblk - t * kGBlockGroup);
+    const int g = j / (hg * sz), r = j % (hg * sz);
+    h = x + 8 * (g * hg + r / sz);
+    nb = t * kGBlockGroup + r % sz;
+}
+
+__global__ __launch_bounds__(kGThreads, 1) void decompress_gemm_bf16_kernel(
     int H, int64_t n_max, const uint16_t *__restrict__ w_uk, const uint16_t *__restrict__ w_uv,
     const uint16_t *__restrict__ ckv, int64_t ckv_sb, int ckv_rowb,
     const int32_t *__restrict__ seqlens, uint16_t *__restrict__ kbuf, uint16_t *__restrict__ vbuf)
 {
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[3 * kGStage];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kGLds];
 
-    const int h = blockIdx.x;
-    const int n0 = blockIdx.y * kGN;
-    const int b = blockIdx.z >> 1, which = blockIdx.z & 1;
+    int h, nb;
+    gemm_item(H, gridDim.y, h, nb);
+    const int n0 = nb * kGN;
+    const int b = blockIdx.z;
     const int L = clamp_len(seqlens[b], n_max);
     if (n0 >= L) return;  // rows past the cached length are never attended to
-    const uint16_t *w = which ? w_uv : w_uk;
-    uint16_t *dst = which ? vbuf : kbuf;
 
-    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int which = wv >> 3, g8 = wv & 7;  // weight, wave within its group
     const int half = lane >> 5, l32 = lane & 31;
-    const int wf = (wv & 1) * 64, wt = (wv >> 1) * 64;
+    const int wf = (g8 & 1) * 64, wt = (g8 >> 1) * 64;
 
+    const uint16_t *w = which ? w_uv : w_uk;
     const i32x4 rs_w = make_rsrc(w + static_cast<int64_t>(h) * DN * DC, DN * DC * 2);
     const i32x4 rs_c = make_rsrc(ckv + static_cast<int64_t>(b) * ckv_sb,
                                  static_cast<uint32_t>(L) * static_cast<uint32_t>(ckv_rowb));
 
-    // Load d = wv + 8 e of a chunk: d < kGWLoads are W rows, the rest c rows,
-    // kGRowsPerLoad rows each.  Lane -> row (first row) + lane / pieces, LDS
-    // piece lane % pieces holding source piece (lane % pieces) ^ gemm_swz(row).
-    unsigned voff[kGDmaPerWave];
-#pragma unroll
-    for (int e = 0; e < kGDmaPerWave; ++e) {
-        const int d = wv + kGWaves * e;
-        const int i = d < kGWLoads ? d : d - kGWLoads;
-        const int row = kGRowsPerLoad * i + lane / kGPieces;
-        const int piece = (lane % kGPieces) ^ gemm_swz(row);
-        voff[e] = d < kGWLoads ? static_cast<unsigned>(row * DC * 2 + 16 * piece)
-                               : static_cast<unsigned>((n0 + row) * ckv_rowb + 16 * piece);
-    }
-    // LDS address of this wave's first 1-KiB load slot (wave-uniform).
-    const uint32_t wave_lds = lds_addr(lds) + 1024 * __builtin_amdgcn_readfirstlane(wv);
-    auto issue_chunk = [&](int kc, int stage) {
+    // The wave's two loads of a chunk: W rows 16 g8 .. + 15 of its weight
+    // and c rows 16 wv .. + 15.  Lane -> row (first row) + lane / 4, LDS
+    // piece lane % 4 holding source piece (lane % 4) ^ gemm_swz(row).
+    const int rw = kGRowsPerLoad * g8 + lane / kGPieces;
+    const int rc = kGRowsPerLoad * wv + lane / kGPieces;
+    const unsigned voff_w =
+        static_cast<unsigned>(rw * DC * 2 + 16 * ((lane % kGPieces) ^ gemm_swz(rw)));
+    const unsigned voff_c = static_cast<unsigned>((n0 + rc) * ckv_rowb +
+                                                  16 * ((lane % kGPieces) ^ gemm_swz(rc)));
+    // LDS address of this wave's 1-KiB W slot (wave-uniform); its c slot
+    // is kGCOff further.
+    const uint32_t wave_lds = lds_addr(lds) + 1024 * wv;
+    auto issue_chunk = [&](int kc) {
         const unsigned k_byte = static_cast<unsigned>(kc * kGK * 2);
-        const uint32_t dst = wave_lds + static_cast<uint32_t>(stage) * kGStage;
-#pragma unroll
-        for (int e = 0; e < kGDmaPerWave; ++e) {
-            if (kGWaves * e < kGWLoads)
-                lds_dma16(rs_w, dst + 1024 * kGWaves * e, voff[e] + k_byte);
-            else
-                lds_dma16(rs_c, dst + kGWBytes + 1024 * (kGWaves * e - kGWLoads), voff[e] + k_byte);
-        }
+        const uint32_t dst = wave_lds + static_cast<uint32_t>(kc & (kGStages - 1)) * kGStage;
+        lds_dma16(rs_w, dst, voff_w + k_byte);
+        lds_dma16(rs_c, dst + kGCOff, voff_c + k_byte);
     };
 
     // Operand reads: row base + 32 rows per block (immediate), piece
@@ -124,6 +150,7 @@ __global__ __launch_bounds__(kGThreads, 2) void decompress_gemm_bf16_kernel(
 #pragma unroll
     for (int ks = 0; ks < kGK / 16; ++ks)
         aoff[ks] = l32 * kGRowB + 16 * ((2 * ks + half) ^ gemm_swz(l32));
+    const int a_base = which * kGWBytes + wf * kGRowB, c_base = kGCOff + wt * kGRowB;
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -133,23 +160,29 @@ __global__ __launch_bounds__(kGThreads, 2) void decompress_gemm_bf16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    issue_chunk(0, 0);
-    issue_chunk(1, 1);
-    int buf = 0;
+    static_assert(kGStages == 4 && kGChunks >= 3, "three chunks in flight");
+    issue_chunk(0);
+    issue_chunk(1);
+    issue_chunk(2);
     for (int kc = 0; kc < kGChunks; ++kc) {
-        if (kc + 1 < kGChunks)
-            wait_then_barrier<kGDmaPerWave>();
+        // chunk kc has landed once at most the loads of the chunks issued
+        // after it (two loads each) are still in flight
+        if (kc + 2 < kGChunks)
+            wait_then_barrier<4>();
+        else if (kc + 1 < kGChunks)
+            wait_then_barrier<2>();
         else
             wait_then_barrier<0>();
-        if (kc + 2 < kGChunks) issue_chunk(kc + 2, buf == 0 ? 2 : buf - 1);
-        const unsigned char *st = lds + buf * kGStage;
+        // the buffer of chunk kc - 1, which every wave has finished reading
+        if (kc + 3 < kGChunks) issue_chunk(kc + 3);
+        const unsigned char *st = lds + (kc & (kGStages - 1)) * kGStage;
 #pragma unroll
         for (int ks = 0; ks < kGK / 16; ++ks) {
             u32x4 a[2], c[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                a[i] = *reinterpret_cast<const u32x4 *>(st + (wf + 32 * i) * kGRowB + aoff[ks]);
-                c[i] = *reinterpret_cast<const u32x4 *>(st + kGWBytes + (wt + 32 * i) * kGRowB + aoff[ks]);
+                a[i] = *reinterpret_cast<const u32x4 *>(st + a_base + 32 * i * kGRowB + aoff[ks]);
+                c[i] = *reinterpret_cast<const u32x4 *>(st + c_base + 32 * i * kGRowB + aoff[ks]);
             }
             // D^T[feature][token]: A = W rows, B = c rows
 #pragma unroll
@@ -157,16 +190,16 @@ __global__ __launch_bounds__(kGThreads, 2) void decompress_gemm_bf16_kernel(
 #pragma unroll
                 for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], c[j], acc[i][j]);
         }
-        buf = buf == 2 ? 0 : buf + 1;
     }
 
-    // Epilogue: stage [token][feature] bf16 rows, then whole-row stores.
+    // Epilogue: stage [token][feature] bf16 rows of both weights, then
+    // whole-row stores.
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            unsigned char *row = lds + (wt + 32 * j + l32) * kGOutRow;
+            unsigned char *row = lds + which * kGOutBytes + (wt + 32 * j + l32) * kGOutRow;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int feat = wf + 32 * i + 8 * g + 4 * half;
@@ -176,13 +209,16 @@ __global__ __launch_bounds__(kGThreads, 2) void decompress_gemm_bf16_kernel(
             }
         }
     __syncthreads();
-    uint16_t *dbase = dst + ((static_cast<int64_t>(b) * H + h) * n_max + n0) * DN;
+    const int64_t obase = ((static_cast<int64_t>(b) * H + h) * n_max + n0) * DN;
 #pragma unroll
-    for (int e = 0; e < kGN * 16 / kGThreads; ++e) {
-        const int id = tid + kGThreads * e, row = id >> 4, piece = id & 15;
+    for (int e = 0; e < 2 * kGN * 16 / kGThreads; ++e) {
+        const int id = tid + kGThreads * e;
+        const int out = id / (kGN * 16), row = (id >> 4) % kGN, piece = id & 15;
+        uint16_t *dst = (out ? vbuf : kbuf) + obase;
         if (n0 + row < L)
-            *reinterpret_cast<u32x4 *>(dbase + static_cast<int64_t>(row) * DN + 8 * piece) =
-                *reinterpret_cast<const u32x4 *>(lds + row * kGOutRow + 16 * piece);
+            *reinterpret_cast<u32x4 *>(dst + static_cast<int64_t>(row) * DN + 8 * piece) =
+                *reinterpret_cast<const u32x4 *>(lds + out * kGOutBytes + row * kGOutRow +
+                                                 16 * piece);
     }
 }
 
@@ -480,7 +516,7 @@ hipError_t launch_prefill_bf16(const PrefillShape &s, const void *q_nope, const 
                                void *vbuf, hipStream_t st)
 {
     // K and V are [B][H][n_max][128] bf16 in the workspace.
-    dim3 ggrid(s.H, static_cast<unsigned>((s.n_max + kGN - 1) / kGN), 2 * s.B);
+    dim3 ggrid(s.H, static_cast<unsigned>((s.n_max + kGN - 1) / kGN), s.B);
     decompress_gemm_bf16_kernel<<<ggrid, kGThreads, 0, st>>>(
         s.H, s.n_max, static_cast<const uint16_t *>(w_uk), static_cast<const uint16_t *>(w_uv),
         static_cast<const uint16_t *>(ckv), s.ckv_sb, static_cast<int>(s.ckv_sn * 2), seqlens,

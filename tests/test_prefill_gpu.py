@@ -91,6 +91,7 @@ def test_prefill_bf16_against_naive(T, L):
     (1, 40, [50], 3),               # 3 (sequence, head) pairs: plain block order
     (3, 300, [300, 310, 555], 8),   # two query blocks, a ragged tail, keys beyond T
     (2, 257, [257, 700], 4),        # one query past a 256-query block
+    (1, 70, [2200], 24),            # 3 heads per XCD, 9 token blocks: a partial block group
 ])
 def test_prefill_bf16_block_mapping_and_ragged(B, T, L, H):
     say(f"prefill bf16 B={B} T={T} L={L} H={H}")
