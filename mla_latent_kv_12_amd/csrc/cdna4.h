@@ -87,6 +87,15 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t lds_dst, unsigned
                  :: "s"(lds_dst), "v"(voff), "s"(rsrc) : "memory");
 }
 
+// The same load with the non-temporal cache policy, for data that one call
+// streams through exactly once (the decode's cache rows): the lines are not
+// kept in the caches for reuse.
+__device__ __forceinline__ void lds_dma16_stream(i32x4 rsrc, uint32_t lds_dst, unsigned voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 :: "s"(lds_dst), "v"(voff), "s"(rsrc) : "memory");
+}
+
 // Transposing LDS read (gfx950): within each group of 16 lanes, lane j gets
 // element (j & 3) of the 4 consecutive bf16 that lanes 4k + (j >> 2) address,
 // for k = 0..3.  Packed two per dword, k = 0 in the low half of dword 0.

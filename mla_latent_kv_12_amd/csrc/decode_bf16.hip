@@ -118,8 +118,9 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, int T, i
 //
 // Workgroup = 4 waves = 128 heads of one sequence over one context split.
 // Cache tiles of 32 rows x 576 bf16 (36 KiB) are copied HBM -> LDS with
-// direct-to-LDS 16-byte buffer loads (buffer_load_dwordx4 ... lds) into three
-// LDS buffers, so two tiles are in flight while one is consumed.  The buffer
+// direct-to-LDS 16-byte buffer loads (buffer_load_dwordx4 ... lds, with the
+// non-temporal policy: a decode call reads each row once) into three LDS
+// buffers, so two tiles are in flight while one is consumed.  The buffer
 // descriptor's range ends at the split's last row: rows past it arrive as
 // zeros (weight zero, and they can never inject NaN/Inf).  The cross-wave
 // hand-off is an explicit "wait for my tile loads, then s_barrier".
@@ -271,9 +272,9 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
         const uint32_t dst = tiles_lds + static_cast<uint32_t>(dst_buf) * kTileBytes;
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            lds_dma16(rs_lat, dst + lat_slot_wk(wu, k),
+            lds_dma16_stream(rs_lat, dst + lat_slot_wk(wu, k),
                          lat_src + lat_base + static_cast<unsigned>(k * ckv_rowb));
-        lds_dma16(rs_rope, dst + kRopeBase + wu * 8 * kRopeRow,
+        lds_dma16_stream(rs_rope, dst + kRopeBase + wu * 8 * kRopeRow,
                      rope_src + static_cast<unsigned>(n0) * static_cast<unsigned>(kpe_rowb));
     };
 
