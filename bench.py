@@ -290,7 +290,8 @@ def bench_outproj(args, mla, datagen):
         us = 1e3 * float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]))
         nbytes = (w.numel() + x.numel() + y.numel()) * 2
         res[name] = {"us_per_call": us, "weight_bytes": w.numel() * 2,
-                     "gbps": nbytes / (us * 1e-6) / 1e9, "splits": params.num_splits or None}
+                     "gbps": nbytes / (us * 1e-6) / 1e9,
+                     "form": "direct" if ws.numel() == 0 else "sliced"}
     gbps = res["unfolded"]["gbps"]
     print(json.dumps({
         "mode": "outproj", "metric": "output projection after decode, HBM GB/s (% of peak)",
@@ -301,7 +302,7 @@ def bench_outproj(args, mla, datagen):
         "unfolded": res["unfolded"], "folded": res["folded"], "fold_weights_ms": fold_ms,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS,
-                     "kernel": "rowproj_bf16_kernel + rowproj_reduce_kernel (unfolded W_O)"}}),
+                     "kernel": "rowproj_direct_bf16_kernel (unfolded W_O)"}}),
         flush=True)
     return 0
 

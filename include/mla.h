@@ -293,11 +293,13 @@ typedef struct mla_proj_params {
     int32_t dtype;         /* mla_dtype of x and w                               */
     int32_t out_dtype;     /* mla_dtype of y                                     */
     int32_t num_splits;    /* slices of K summed in a fixed order; 0 -> by size */
+                           /* (bf16 with N >= 2048: the direct form, below)    */
     int32_t reserved;      /* must be 0                                          */
 } mla_proj_params;
 
-/* Bytes of device workspace mla_output_proj needs (host; 0 if invalid):
- * the fp32 partial sums of every K slice. */
+/* Bytes of device workspace mla_output_proj needs (host): the fp32 partial
+ * sums of every K slice.  0 when the call needs none (the direct form) or
+ * when p is invalid; mla_output_proj validates p itself before any launch. */
 size_t mla_output_proj_workspace_bytes(const mla_proj_params *p);
 
 /*
@@ -311,7 +313,11 @@ size_t mla_output_proj_workspace_bytes(const mla_proj_params *p);
  *   x [B][K], w [N][K] dtype; y [B][N] out_dtype, written.
  * Dot products accumulate in fp32 over slices of K whose partial sums are
  * added in ascending slice order: bitwise reproducible for a fixed split
- * count.  workspace >= mla_output_proj_workspace_bytes(p), 256-byte aligned.
+ * count.  workspace >= mla_output_proj_workspace_bytes(p), 256-byte aligned
+ * (may be NULL when that is 0).
+ * Direct form (bf16, num_splits = 0, N >= 2048): each workgroup takes R =
+ * min(32, ceil(N / 256)) rows over all of K, its 8 waves' eighths of K added
+ * in a fixed order: one launch, no workspace, bitwise reproducible.
  */
 mla_status mla_output_proj(const mla_proj_params *p, const void *x, const void *w, void *y,
                            void *workspace, size_t workspace_bytes, void *stream);

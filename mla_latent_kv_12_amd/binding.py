@@ -306,13 +306,14 @@ def output_proj(x, w, *, out=None, workspace=None, out_dtype=None, num_splits=0,
     if out is None:
         odt = torch.float32 if params.out_dtype == MLA_F32 else torch.bfloat16
         out = torch.empty((params.batch, params.out_features), dtype=odt, device=x.device)
+    # 0 bytes: the direct form needs none, or params are invalid (the call
+    # itself then reports why, before any launch)
     need = output_proj_workspace_bytes(params)
-    if need == 0:
-        _check(lib().mla_output_proj(ctypes.byref(params), None, None, None, None, 0, None))
-    if workspace is None:
+    if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
     _check(lib().mla_output_proj(ctypes.byref(params), _ptr(x), _ptr(w), _ptr(out),
-                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+                                 _ptr(workspace) if ws_bytes else None, ws_bytes, _stream(stream)))
     return out
 
 

@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "mla.h"
@@ -35,6 +36,7 @@ mla_status ok()
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kProjDirectGroups = 256;  // workgroups of the direct projection: one per CU
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 bool debug_checks()
@@ -687,8 +689,18 @@ mla::ProjShape make_proj_shape(const mla_proj_params *p)
     s.N = (int)p->out_features;
     s.bf16 = p->dtype == MLA_BF16;
     s.out_bf16 = p->out_dtype == MLA_BF16;
-    // Slices of about 1024 input features: enough workgroups to stream the
-    // weight from every CU (e.g. 112 row blocks x 16 slices for 7168 x 16384).
+    s.R = 0;
+    // bf16 weights with at least 8 rows per CU, split count left to the
+    // library: the direct form, one group of R <= 32 rows per workgroup over
+    // all of K, the groups covering the 256 CUs of an MI355X once
+    // (R = 28 for 7168 rows).
+    if (s.bf16 && p->num_splits == 0 && p->out_features >= 8 * kProjDirectGroups) {
+        s.S = 1;
+        s.R = (int)std::min<int64_t>(32, (p->out_features + kProjDirectGroups - 1) / kProjDirectGroups);
+        return s;
+    }
+    // Otherwise slices of about 1024 input features: enough workgroups to
+    // stream the weight from every CU.
     int64_t S = p->num_splits > 0 ? p->num_splits : (p->in_features + 1023) / 1024;
     if (S < 1) S = 1;
     if (S > mla::kMaxSplits) S = mla::kMaxSplits;
@@ -698,6 +710,7 @@ mla::ProjShape make_proj_shape(const mla_proj_params *p)
 
 size_t proj_workspace(const mla::ProjShape &s)
 {
+    if (s.R > 0) return 0;  // the direct form keeps its partial sums in LDS
     return round_up((size_t)s.S * (size_t)s.B * (size_t)s.N * 4, kAlign);
 }
 
@@ -723,7 +736,7 @@ mla_status mla_output_proj(const mla_proj_params *p, const void *x, const void *
         return fail(MLA_ERR_INVALID_ARG, "x and w must be %d-byte aligned", bf16 ? 16 : 4);
     mla::ProjShape s = make_proj_shape(p);
     const size_t need = proj_workspace(s);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign))
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)))
         return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu)",
                     need, workspace_bytes);
     hipError_t e = mla::launch_output_proj(s, x, w, y, static_cast<float *>(workspace),

@@ -108,13 +108,15 @@ hipError_t launch_prefill_bf16(const PrefillShape &s, const void *q_nope, const 
                                const void *kpe, const int32_t *seqlens, void *out, void *kbuf,
                                void *vbuf, hipStream_t st);
 
-// Output projection y[B][N] = x[B][K] w[N][K]^T, K cut into S slices.
+// Output projection y[B][N] = x[B][K] w[N][K]^T, K cut into S slices, or
+// (R > 0, bf16 only) the direct form: R rows per workgroup over all of K.
 struct ProjShape {
     int B, K, N, S;
+    int R;          // > 0: direct form with R <= 32 rows per workgroup (S = 1, no partials)
     bool bf16;      // x and w bf16 (MFMA path; K % 64 == 0), else fp32
     int out_bf16;
 };
-// part: S * B * N fp32 of workspace.
+// part: S * B * N fp32 of workspace (none for the direct form).
 hipError_t launch_output_proj(const ProjShape &p, const void *x, const void *w, void *y,
                               float *part, hipStream_t st);
 hipError_t launch_fold_value_output(int N, int H, int dv, int dc, bool bf16, const void *w_o,

@@ -119,6 +119,80 @@ __global__ __launch_bounds__(64 * kPWaves) void rowproj_bf16_kernel(
     }
 }
 
+// Direct form for weights with many rows: workgroup g takes rows
+// [g R, g R + R) (R <= 32: one MFMA tile, rows past R or N clamped on load
+// and not stored) over the whole of K, its 8 waves splitting K into eighths
+// of whole 16-element steps; the waves' sums are added in LDS in wave order
+// and stored in the output type.  No slice partials and no second launch;
+// R is chosen so that the row groups cover every CU once.
+// Grid (ceil(N / R), ceil(B / 32)).
+constexpr int kDWaves = 8;   // waves per workgroup, splitting K
+constexpr int kDUnroll = 4;  // K steps (16 each) of loads in flight per lane
+__global__ __launch_bounds__(64 * kDWaves) void rowproj_direct_bf16_kernel(
+    int B, int K, int N, int R, const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
+    void *__restrict__ y, int out_bf16)
+{
+    __shared__ f32x4 red[kDWaves][4][64];  // per wave: 16 values per lane
+    const int n0 = blockIdx.x * R, b0 = blockIdx.y * kPBatch;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int half = lane >> 5, l32 = lane & 31;
+    const int steps = K / 16;
+    const int st0 = (steps * wv) / kDWaves, st1 = (steps * (wv + 1)) / kDWaves;
+
+    // A operand: weight row n0 + min(l32, R - 1) (inside the weight);
+    // B operand: batch row b0 + l32 (zeros past the batch); elements
+    // 8 half .. 8 half + 7 of each step.
+    const u32x4 *wrow = reinterpret_cast<const u32x4 *>(
+                            w + static_cast<int64_t>(min(n0 + min(l32, R - 1), N - 1)) * K) + half;
+    const bool xv = b0 + l32 < B;
+    const u32x4 *xrow = reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(xv ? b0 + l32 : 0) * K) + half;
+
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    int st = st0;
+    for (; st + kDUnroll <= st1; st += kDUnroll) {
+        u32x4 wa[kDUnroll], xb[kDUnroll];
+#pragma unroll
+        for (int u = 0; u < kDUnroll; ++u) {
+            wa[u] = wrow[2 * (st + u)];
+            xb[u] = xrow[2 * (st + u)];
+        }
+#pragma unroll
+        for (int u = 0; u < kDUnroll; ++u) acc = mfma32(wa[u], xv ? xb[u] : zero, acc);
+    }
+    for (; st < st1; ++st) {
+        const u32x4 wq = wrow[2 * st], xq = xrow[2 * st];
+        acc = mfma32(wq, xv ? xq : zero, acc);
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+        red[wv][g][lane] = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+    __syncthreads();
+    // thread -> (group g, lane) of the wave-0 layout: 4 x 64 = 256 entries
+    if (tid < 4 * 64) {
+        const int g = tid >> 6, ln = tid & 63;
+        f32x4 v = red[0][g][ln];
+#pragma unroll
+        for (int q = 1; q < kDWaves; ++q) v += red[q][g][ln];
+        // lane ln holds batch column ln % 32, rows 8 g + 4 (ln / 32) + 0..3 of the tile
+        const int b = b0 + (ln & 31), r = 8 * g + 4 * (ln >> 5);
+        if (b < B) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = n0 + r + i;
+                if (r + i >= R || n >= N) continue;
+                const int64_t o = static_cast<int64_t>(b) * N + n;
+                if (out_bf16)
+                    reinterpret_cast<__bf16 *>(y)[o] = static_cast<__bf16>(v[i]);
+                else
+                    reinterpret_cast<float *>(y)[o] = v[i];
+            }
+        }
+    }
+}
+
 // y[b][n] = sum_{s ascending} part[s][b][n], rounded to the output type.
 __global__ __launch_bounds__(256) void rowproj_reduce_kernel(int B, int N, int S,
                                                              const float *__restrict__ part,
@@ -231,6 +305,13 @@ __global__ __launch_bounds__(256) void fold_value_output_kernel(int N, int H, in
 hipError_t launch_output_proj(const ProjShape &p, const void *x, const void *w, void *y,
                               float *part, hipStream_t st)
 {
+    if (p.R > 0) {
+        dim3 grid((p.N + p.R - 1) / p.R, (p.B + kPBatch - 1) / kPBatch);
+        rowproj_direct_bf16_kernel<<<grid, 64 * kDWaves, 0, st>>>(
+            p.B, p.K, p.N, p.R, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w),
+            y, p.out_bf16);
+        return hipGetLastError();
+    }
     if (p.bf16) {
         dim3 grid((p.N + kPRows - 1) / kPRows, p.S, (p.B + kPBatch - 1) / kPBatch);
         rowproj_bf16_kernel<<<grid, 64 * kPWaves, 0, st>>>(p.B, p.K, p.N, p.S,

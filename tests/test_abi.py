@@ -250,9 +250,13 @@ def _proj_params(**kw):
 
 def test_output_proj_workspace_and_validation():
     assert ctypes.sizeof(binding.ProjParams) == 3 * 8 + 4 * 4
-    # auto: slices of ~1024 input features, fp32 partials of every slice
-    assert mla.output_proj_workspace_bytes(_proj_params()) == 16 * 8 * 7168 * 4
-    assert mla.output_proj_workspace_bytes(_proj_params(in_features=65536)) == 64 * 8 * 7168 * 4
+    # auto, bf16, >= 2048 rows: the direct form, no workspace
+    assert mla.output_proj_workspace_bytes(_proj_params()) == 0
+    assert mla.output_proj_workspace_bytes(_proj_params(in_features=65536)) == 0
+    # auto with fewer rows, or fp32: slices of ~1024 input features, fp32 partials of every slice
+    assert mla.output_proj_workspace_bytes(_proj_params(out_features=2047)) == 16 * 8 * 2047 * 4
+    assert mla.output_proj_workspace_bytes(_proj_params(dtype=mla.MLA_F32)) == 16 * 8 * 7168 * 4
+    # an explicit split count always takes the sliced form
     assert mla.output_proj_workspace_bytes(_proj_params(num_splits=3)) == 3 * 8 * 7168 * 4
     assert mla.output_proj_workspace_bytes(_proj_params(in_features=100)) == 0   # bf16: K % 64
     assert mla.output_proj_workspace_bytes(_proj_params(in_features=100, dtype=mla.MLA_F32)) > 0
@@ -268,8 +272,11 @@ def test_output_proj_workspace_and_validation():
     pp = _proj_params()
     assert lib.mla_output_proj(ctypes.byref(pp), vp(0x1008), vp(0x2000), vp(0x3000),
                                vp(0x100000), 1 << 40, None) == mla.MLA_ERR_INVALID_ARG  # x % 16
+    pp = _proj_params(num_splits=3)   # the sliced form, whose partials need a workspace
     assert lib.mla_output_proj(ctypes.byref(pp), vp(0x1000), vp(0x2000), vp(0x3000),
                                vp(0x100000), 100, None) == mla.MLA_ERR_WORKSPACE
+    assert lib.mla_output_proj(ctypes.byref(pp), vp(0x1000), vp(0x2000), vp(0x3000),
+                               None, 1 << 40, None) == mla.MLA_ERR_WORKSPACE
 
 
 def test_fold_and_decode_latent_reject_before_launch():

@@ -68,6 +68,30 @@ def test_output_proj_shapes_and_slices(dtype, B, K, N, S):
     assert np.array_equal(y, again)
 
 
+@pytest.mark.parametrize("B,K,N", [
+    (40, 192, 2500),    # 10 rows per workgroup, two batch groups
+    (3, 4096, 2048),    # 8 rows per workgroup
+    (1, 64, 9000),      # 32 rows per workgroup, a partial last group; waves with no K steps
+])
+def test_output_proj_direct_form(B, K, N):
+    """bf16 with >= 2048 rows and the split count left to the library: one
+    group of rows per workgroup over all of K, no workspace."""
+    say(f"output projection direct form bf16 B={B} K={K} N={N}")
+    rng = np.random.default_rng(4250 + B + K + N)
+    x = normals(rng, (B, K), 1.0, "bf16")
+    w = normals(rng, (N, K), 1.0 / math.sqrt(K), "bf16")
+    params = mla.proj_params(to_device(x, "bf16"), to_device(w, "bf16"), out_dtype=torch.float32)
+    assert mla.output_proj_workspace_bytes(params) == 0
+    y = run_proj(x, w, "bf16")
+    m = metrics(y, oracle.output_proj(x, w))
+    say(f"  parity all outputs: {m}")
+    assert m["finite"] and m["max_abs"] <= 1e-4
+    assert np.array_equal(y, run_proj(x, w, "bf16"))                      # bitwise repeatable
+    assert np.max(np.abs(y - run_proj(x, w, "bf16", num_splits=3))) <= 1e-4  # the sliced form
+    y16 = run_proj(x, w, "bf16", out_dtype="bf16")
+    assert np.array_equal(y16, torch.from_numpy(y).to(torch.bfloat16).double().numpy())
+
+
 @pytest.mark.parametrize("splits", [1, 3])
 @pytest.mark.parametrize("dtype,dims,H,L", [("bf16", V3, 128, [300, 77]),
                                             ("f32", TINY, 4, [128, 9])])
