@@ -8,9 +8,10 @@
 //
 // A matrix-vector product per sequence: HBM-bound on the weights (d_c + d_r
 // rows of d_model values, 8.3 MB at the V3 shape), which every workgroup
-// reads once for a group of 8 sequences.  Workgroup = 4 waves = 4 output rows;
-// a wave streams its row in 16-byte pieces, lane-strided, dotting it with up to
-// 8 hidden states at once, then reduces across the wave.  Rows d_c + 2i and
+// reads once for a group of 8 sequences.  Workgroup = 4 waves and 4 output
+// rows; wave w streams the w-th quarter of all four rows in 16-byte pieces,
+// lane-strided, so that each hidden-state piece it loads serves four rows,
+// then the workgroup's 256 lanes are summed in LDS in a fixed order.  Rows d_c + 2i and
 // d_c + 2i + 1 (one rotation pair) always fall in the same workgroup (row
 // groups start at multiples of 4 and d_c is even), which rotates the pair and
 // writes both.
@@ -25,9 +26,12 @@ namespace {
 
 using namespace cdna4;
 
-constexpr int kAppendRows = 4;     // output rows (waves) per workgroup
-constexpr int kAppendGroup = 8;    // sequences per pass over a weight row
-constexpr int kAppendUnroll = 4;   // 16-byte pieces per lane in flight per pass
+constexpr int kAppendRows = 4;     // output rows per workgroup
+constexpr int kAppendWaves = 4;    // waves per workgroup: contiguous quarters of d_model
+constexpr int kAppendGroup = 8;    // sequences per pass over the weight rows
+constexpr int kAppendUnroll = 2;   // 16-byte pieces per lane and row in flight per pass
+constexpr int kAppendVals = kAppendRows * kAppendGroup;  // dot products per workgroup and pass
+static_assert(64 * kAppendWaves == 8 * kAppendVals, "the lane sum runs as 8 chunks x 32 values");
 
 template <bool BF16>
 __device__ __forceinline__ void piece_to_f32(const u32x4 &v, float *f)
@@ -45,68 +49,94 @@ __device__ __forceinline__ void piece_to_f32(const u32x4 &v, float *f)
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(64 * kAppendRows) void cache_append_kernel(
+__global__ __launch_bounds__(64 * kAppendWaves) void cache_append_kernel(
     int B, int d_model, int dc, int dr, int64_t n_max, const u32x4 *__restrict__ h,
     const u32x4 *__restrict__ w_dkv, const u32x4 *__restrict__ w_kr,
     const int32_t *__restrict__ positions, double base, void *__restrict__ ckv, int64_t ckv_sb,
     int64_t ckv_sn, void *__restrict__ kpe, int64_t kpe_sb, int64_t kpe_sn)
 {
     constexpr int kVec = BF16 ? 8 : 4;  // elements per 16-byte piece
+    __shared__ float part[64 * kAppendWaves][kAppendVals + 1];  // per lane, padded rows
+    __shared__ float part2[8][kAppendVals];
     __shared__ float res[kAppendRows][kAppendGroup];
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     const int row0 = blockIdx.x * kAppendRows;
-    const int row = row0 + wv;                  // this wave's output row
-    const bool live = row < dc + dr;
     const int pieces = d_model / kVec;          // 16-byte pieces per row
-    const u32x4 *wrow = !live ? w_dkv : row < dc ? w_dkv + static_cast<int64_t>(row) * pieces
-                                                 : w_kr + static_cast<int64_t>(row - dc) * pieces;
+    // this wave's quarter of every row, and the workgroup's rows (rows past
+    // d_c + d_r read row 0 of W_DKV; their sums are never stored)
+    const int p_begin = (pieces * wv) / kAppendWaves, p_end = (pieces * (wv + 1)) / kAppendWaves;
+    const u32x4 *wrow[kAppendRows];
+#pragma unroll
+    for (int r = 0; r < kAppendRows; ++r) {
+        const int row = row0 + r;
+        wrow[r] = row >= dc + dr ? w_dkv
+                : row < dc       ? w_dkv + static_cast<int64_t>(row) * pieces
+                                 : w_kr + static_cast<int64_t>(row - dc) * pieces;
+    }
 
     for (int b0 = 0; b0 < B; b0 += kAppendGroup) {
         const int nb = min(kAppendGroup, B - b0);
-        float acc[kAppendGroup];
+        float acc[kAppendRows][kAppendGroup];
 #pragma unroll
-        for (int g = 0; g < kAppendGroup; ++g) acc[g] = 0.f;
-        if (live) {
-            // kAppendUnroll pieces per lane per pass, every load of a pass issued
-            // before any is used (indices past the row or the group are clamped to
-            // valid ones and their products dropped)
-            for (int p0 = lane; p0 < pieces; p0 += 64 * kAppendUnroll) {
-                u32x4 wq[kAppendUnroll], hq[kAppendUnroll][kAppendGroup];
+        for (int r = 0; r < kAppendRows; ++r)
 #pragma unroll
-                for (int u = 0; u < kAppendUnroll; ++u) {
-                    const int p = min(p0 + 64 * u, pieces - 1);
-                    wq[u] = wrow[p];
+            for (int g = 0; g < kAppendGroup; ++g) acc[r][g] = 0.f;
+        // kAppendUnroll pieces per lane per pass, every load of a pass issued
+        // before any is used (indices past the quarter or the group are
+        // clamped to valid ones and their products dropped); each
+        // hidden-state piece serves all four rows
+        for (int p0 = p_begin + lane; p0 < p_end; p0 += 64 * kAppendUnroll) {
+            u32x4 wq[kAppendUnroll][kAppendRows], hq[kAppendUnroll][kAppendGroup];
+#pragma unroll
+            for (int u = 0; u < kAppendUnroll; ++u) {
+                const int p = min(p0 + 64 * u, p_end - 1);
+#pragma unroll
+                for (int r = 0; r < kAppendRows; ++r) wq[u][r] = wrow[r][p];
+#pragma unroll
+                for (int g = 0; g < kAppendGroup; ++g)
+                    hq[u][g] = h[static_cast<int64_t>(b0 + min(g, nb - 1)) * pieces + p];
+            }
+#pragma unroll
+            for (int u = 0; u < kAppendUnroll; ++u) {
+                if (p0 + 64 * u >= p_end) break;
+                float hf[kAppendGroup][kVec];
+#pragma unroll
+                for (int g = 0; g < kAppendGroup; ++g) piece_to_f32<BF16>(hq[u][g], hf[g]);
+#pragma unroll
+                for (int r = 0; r < kAppendRows; ++r) {
+                    float wf[kVec];
+                    piece_to_f32<BF16>(wq[u][r], wf);
 #pragma unroll
                     for (int g = 0; g < kAppendGroup; ++g)
-                        hq[u][g] = h[static_cast<int64_t>(b0 + min(g, nb - 1)) * pieces + p];
-                }
 #pragma unroll
-                for (int u = 0; u < kAppendUnroll; ++u) {
-                    if (p0 + 64 * u >= pieces) break;
-                    float wf[kVec];
-                    piece_to_f32<BF16>(wq[u], wf);
-#pragma unroll
-                    for (int g = 0; g < kAppendGroup; ++g) {
-                        float hf[kVec];
-                        piece_to_f32<BF16>(hq[u][g], hf);
-#pragma unroll
-                        for (int e = 0; e < kVec; ++e) acc[g] = fmaf(wf[e], hf[e], acc[g]);
-                    }
+                        for (int e = 0; e < kVec; ++e) acc[r][g] = fmaf(wf[e], hf[g][e], acc[r][g]);
                 }
             }
         }
+        // fixed-order sum over the workgroup's 256 lanes: 8 chunks of 32
+        // lanes, each in ascending lane order, then the chunks in order
 #pragma unroll
-        for (int g = 0; g < kAppendGroup; ++g)
+        for (int r = 0; r < kAppendRows; ++r)
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) acc[g] += __shfl_xor(acc[g], o);
-        if (lane == 0) {
+            for (int g = 0; g < kAppendGroup; ++g) part[tid][r * kAppendGroup + g] = acc[r][g];
+        __syncthreads();
+        {
+            const int v = tid % kAppendVals, c = tid / kAppendVals;
+            float sum = 0.f;
+            for (int l = 32 * c; l < 32 * c + 32; ++l) sum += part[l][v];
+            part2[c][v] = sum;
+        }
+        __syncthreads();
+        if (tid < kAppendVals) {
+            float sum = 0.f;
 #pragma unroll
-            for (int g = 0; g < kAppendGroup; ++g) res[wv][g] = acc[g];
+            for (int c = 0; c < 8; ++c) sum += part2[c][tid];
+            res[tid / kAppendGroup][tid % kAppendGroup] = sum;
         }
         __syncthreads();
         // one thread per (row, sequence): rotate RoPE pairs, round, store
-        if (tid < kAppendRows * kAppendGroup) {
+        if (tid < kAppendVals) {
             const int r = tid / kAppendGroup, g = tid % kAppendGroup;
             const int j = row0 + r, b = b0 + g;
             if (g < nb && j < dc + dr) {
@@ -147,12 +177,12 @@ hipError_t launch_cache_append(const AppendShape &s, const void *h, const void *
     const int rows = s.dc + s.dr;
     const unsigned grid = static_cast<unsigned>((rows + kAppendRows - 1) / kAppendRows);
     if (s.bf16)
-        cache_append_kernel<true><<<grid, 64 * kAppendRows, 0, st>>>(
+        cache_append_kernel<true><<<grid, 64 * kAppendWaves, 0, st>>>(
             s.B, s.d_model, s.dc, s.dr, s.n_max, static_cast<const u32x4 *>(h),
             static_cast<const u32x4 *>(w_dkv), static_cast<const u32x4 *>(w_kr), positions,
             s.rope_base, ckv, s.ckv_sb, s.ckv_sn, kpe, s.kpe_sb, s.kpe_sn);
     else
-        cache_append_kernel<false><<<grid, 64 * kAppendRows, 0, st>>>(
+        cache_append_kernel<false><<<grid, 64 * kAppendWaves, 0, st>>>(
             s.B, s.d_model, s.dc, s.dr, s.n_max, static_cast<const u32x4 *>(h),
             static_cast<const u32x4 *>(w_dkv), static_cast<const u32x4 *>(w_kr), positions,
             s.rope_base, ckv, s.ckv_sb, s.ckv_sn, kpe, s.kpe_sb, s.kpe_sn);
