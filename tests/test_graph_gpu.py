@@ -1,0 +1,111 @@
+"""The library's calls captured in a HIP graph (torch.cuda.CUDAGraph): a
+serving loop replays one decode layer step (absorbed decode, then the output
+projection) without host launch work.  Every replay is checked bitwise
+against an eager call on the same inputs, with eager work and
+synchronisations between the replays and the inputs changed in place
+between them."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_latent_kv_12_amd as mla
+from gpu_util import say
+from mla_latent_kv_12_amd import datagen
+from mla_latent_kv_12_amd.tensors import decode_tensors, to_device
+
+pytestmark = pytest.mark.gpu
+
+V3 = dict(dc=512, dr=64, dn=128, dv=128)
+
+
+def test_decode_step_graph_replays_match_eager():
+    say("decode + output projection captured in a HIP graph, 3 replays")
+    case = datagen.make_decode_case(B=2, H=128, n_max=640, dtype="bf16", seed=4700,
+                                    seqlens=[600, 77], **V3)
+    t = decode_tensors(case)
+    rng = np.random.default_rng(4701)
+    d_model = 2048
+    w_o = to_device(datagen.bf16_bits(rng.standard_normal((d_model, 128 * 128), dtype=np.float32)
+                                      / np.float32(math.sqrt(128 * 128))), "bf16")
+    args = (t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv_cache"], t["kpe_cache"],
+            t["seqlens"])
+    dp = mla.decode_params(*args[:6], softmax_scale=case.scale)
+    ws = torch.empty(mla.decode_workspace_bytes(dp), dtype=torch.uint8, device="cuda")
+    out = torch.empty((2, 128, 128), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((2, d_model), dtype=torch.bfloat16, device="cuda")
+    pp = mla.proj_params(out.view(2, -1), w_o)
+    pws_bytes = mla.output_proj_workspace_bytes(pp)
+    pws = torch.empty(pws_bytes, dtype=torch.uint8, device="cuda") if pws_bytes else None
+
+    def step():
+        mla.decode(*args, out=out, workspace=ws, params=dp)
+        mla.output_proj(out.view(2, -1), w_o, out=y, workspace=pws, params=pp)
+
+    def eager():
+        o = mla.decode(*args, softmax_scale=case.scale)
+        return o, mla.output_proj(o.reshape(2, -1), w_o)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+
+    gen = torch.Generator(device="cuda").manual_seed(4702)
+    for rep in range(3):
+        if rep:   # new queries and one new cache row, written in place
+            t["q_nope"].copy_(torch.randn(t["q_nope"].shape, generator=gen, device="cuda"))
+            t["ckv_cache"][0, 599].copy_(torch.randn(512, generator=gen, device="cuda"))
+        out.zero_()
+        y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_out, ref_y = eager()
+        torch.cuda.synchronize()
+        say(f"  replay {rep}: decode equal {torch.equal(out, ref_out)}, projection equal "
+            f"{torch.equal(y, ref_y)}")
+        assert torch.equal(out, ref_out)
+        assert torch.equal(y, ref_y)
+        assert torch.isfinite(y.float()).all()
+
+
+def test_naive_prefill_graph_replays_match_eager():
+    say("naive prefill captured in a HIP graph, 2 replays")
+    case = datagen.make_prefill_case(B=1, T=300, H=8, d_model=64, dtype="bf16", seed=4710, **V3)
+    dt = case.dtype
+    cache = to_device(case.cache, dt)
+    qn, qr = to_device(case.q_nope, dt), to_device(case.q_rope, dt)
+    wuk, wuv = to_device(case.w_uk, dt), to_device(case.w_uv, dt)
+    seq = torch.tensor(case.seqlens.astype(np.int32), device="cuda")
+    args = (qn, qr, wuk, wuv, cache[:, :, :512], cache[:, :, 512:], seq)
+    pp = mla.prefill_params(*args[:6], softmax_scale=case.scale)
+    ws = torch.empty(mla.prefill_workspace_bytes(pp), dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, 300, 8, 128), dtype=torch.bfloat16, device="cuda")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mla.prefill_naive(*args, out=out, workspace=ws, params=pp)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mla.prefill_naive(*args, out=out, workspace=ws, params=pp)
+
+    gen = torch.Generator(device="cuda").manual_seed(4711)
+    for rep in range(2):
+        if rep:
+            qn.copy_(torch.randn(qn.shape, generator=gen, device="cuda"))
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = mla.prefill_naive(*args, softmax_scale=case.scale)
+        torch.cuda.synchronize()
+        say(f"  replay {rep}: equal {torch.equal(out, ref)}")
+        assert torch.equal(out, ref)
