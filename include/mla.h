@@ -32,7 +32,11 @@
  *    step 2; eyestech-mla quickstart, where the returned cache grows by one
  *    row).  Values are clamped to [0, n_max] on the device; a sequence with
  *    length 0 gets an all-zero output row.  Rows at or beyond the length are
- *    never read, so they may hold anything, NaN included.
+ *    never read, so they may hold anything, NaN included.  With the
+ *    environment variable MLA_DEBUG_CHECKS=1 the calls that take seqlens
+ *    first copy it to the host (a synchronisation of the stream) and return
+ *    MLA_ERR_INVALID_ARG for a value outside [1, n_max] ([tokens, n_max] for
+ *    the prefills); without it no call ever waits on the device.
  *  - Functions return an mla_status.  All argument checks run on the host
  *    before any launch; a rejected call enqueues nothing.  MLA_ERR_HIP means
  *    a launch failed to enqueue; faults inside kernels surface at the
