@@ -256,3 +256,28 @@ def test_bf16_several_head_groups(H, seqlens, splits):
                                     dtype="bf16", H=H, dc=512, dr=64, dn=128, dv=128)
     out = to_host_f64(run_decode(case, num_splits=splits, out_dtype="f32"))
     assert_close(out, oracle_decode(case), "bf16", f"H={H} vs absorbed oracle")
+
+
+def test_debug_checks_reject_lengths_outside_range(monkeypatch):
+    """MLA_DEBUG_CHECKS=1: seqlens is read back before any launch and values
+    outside [1, n_max] are refused; without it the same call is accepted
+    (lengths clamped on the device)."""
+    say("decode with MLA_DEBUG_CHECKS=1: out-of-range lengths refused")
+    case = datagen.make_decode_case(B=2, H=128, n_max=96, dtype="bf16", seed=4800,
+                                    seqlens=[96, 5], dc=512, dr=64, dn=128, dv=128)
+    t = decode_tensors(case)
+    args = [t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv_cache"], t["kpe_cache"]]
+    monkeypatch.setenv("MLA_DEBUG_CHECKS", "1")
+    good = mla.decode(*args, t["seqlens"], softmax_scale=case.scale)
+    torch.cuda.synchronize()
+    for bad in ([96, 0], [97, 5], [-3, 5]):
+        with pytest.raises(mla.MLAError) as err:
+            mla.decode(*args, torch.tensor(bad, dtype=torch.int32, device="cuda"),
+                       softmax_scale=case.scale)
+        assert err.value.status == mla.MLA_ERR_INVALID_ARG, bad
+    monkeypatch.delenv("MLA_DEBUG_CHECKS")
+    again = mla.decode(*args, t["seqlens"], softmax_scale=case.scale)
+    clamped = mla.decode(*args, torch.tensor([97, 5], dtype=torch.int32, device="cuda"),
+                         softmax_scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(good, again) and torch.equal(good, clamped)
