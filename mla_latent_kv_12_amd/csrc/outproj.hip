@@ -300,6 +300,87 @@ __global__ __launch_bounds__(256) void fold_value_output_kernel(int N, int H, in
     }
 }
 
+// MFMA form of the fold for bf16 with d_v = 128 and d_c a multiple of 128:
+// workgroup (head h, column block jb, row part z) computes
+// W_OV[n][h dc + 128 jb + j] for the rows n of its part, as
+// D^T[j][n] = sum_i W_UV[h][i][128 jb + j] W_O[n][h dv + i].
+// A = W_UV[h]'s column block, transposed once into LDS and then held in
+// registers (wave w: columns 32 w .. 32 w + 31, all 8 K steps of 16);
+// B = W_O rows straight from global memory, 64 rows per pass.  All heads'
+// workgroups of one column block share an XCD with h % 8 (blockIdx.x = h),
+// so the 4 column blocks of a head find its W_O columns in one L2.
+// Grid (H, dc / 128, parts), 256 threads; `rows` (a multiple of 64) per part.
+constexpr int kFoldDv = 128;
+__global__ __launch_bounds__(256) void fold_value_output_mfma_kernel(int N, int H, int dc, int rows,
+                                                                     const uint16_t *__restrict__ w_o,
+                                                                     const uint16_t *__restrict__ w_uv,
+                                                                     uint16_t *__restrict__ w_ov)
+{
+    constexpr int kRow = kFoldDv + 8;            // padded LDS row of the transposed block (bf16)
+    __shared__ __attribute__((aligned(16))) uint16_t wt[128 * kRow];  // [j][i]
+    const int h = blockIdx.x, jb = blockIdx.y;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int half = lane >> 5, l32 = lane & 31;
+
+    // W_UV[h][i][128 jb + 8 c .. + 7] -> wt[8 c + e][i]
+    const uint16_t *src = w_uv + static_cast<int64_t>(h) * kFoldDv * dc + 128 * jb;
+    for (int e = tid; e < kFoldDv * 16; e += 256) {
+        const int i = e >> 4, c = e & 15;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(src + static_cast<int64_t>(i) * dc + 8 * c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            wt[(8 * c + 2 * q) * kRow + i] = static_cast<uint16_t>(v[q] & 0xffffu);
+            wt[(8 * c + 2 * q + 1) * kRow + i] = static_cast<uint16_t>(v[q] >> 16);
+        }
+    }
+    __syncthreads();
+    u32x4 a[kFoldDv / 16];  // A: column 32 wv + l32, K elements 16 s + 8 half .. + 7
+#pragma unroll
+    for (int s = 0; s < kFoldDv / 16; ++s)
+        a[s] = *reinterpret_cast<const u32x4 *>(&wt[(32 * wv + l32) * kRow + 16 * s + 8 * half]);
+
+    const int64_t ld = static_cast<int64_t>(H) * kFoldDv;       // W_O row length
+    const int64_t ldo = static_cast<int64_t>(H) * dc;           // W_OV row length
+    const int n_end = min(N, (static_cast<int>(blockIdx.z) + 1) * rows);
+    // The transposed block now lives in registers; its LDS holds each pass's
+    // 64 x 128 output tile as bf16 rows (stride kRow), written out as whole
+    // 256-byte row segments.
+    for (int n0 = blockIdx.z * rows; n0 < n_end; n0 += 64) {
+        u32x4 b[2][kFoldDv / 16];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int n = min(n0 + 32 * t + l32, N - 1);
+            const u32x4 *row = reinterpret_cast<const u32x4 *>(w_o + n * ld + static_cast<int64_t>(h) * kFoldDv) + half;
+#pragma unroll
+            for (int s = 0; s < kFoldDv / 16; ++s) b[t][s] = row[2 * s];
+        }
+        __syncthreads();  // the previous pass's tile has been written out
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f32x16 acc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < kFoldDv / 16; ++s) acc = mfma32(a[s], b[t][s], acc);
+            // acc[r]: column j = 32 wv + 8 (r / 4) + 4 half + r % 4 of row n0 + 32 t + l32
+            uint16_t *trow = &wt[(32 * t + l32) * kRow + 32 * wv + 4 * half];
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<u32x2 *>(trow + 8 * g) =
+                    u32x2{pack_bf16(acc[4 * g], acc[4 * g + 1]), pack_bf16(acc[4 * g + 2], acc[4 * g + 3])};
+        }
+        __syncthreads();
+        // 64 rows x 16 pieces of 16 bytes, 4 per thread
+#pragma unroll
+        for (int e = tid; e < 64 * 16; e += 256) {
+            const int r = e >> 4, c = e & 15, n = n0 + r;
+            if (n < n_end)
+                *reinterpret_cast<u32x4 *>(w_ov + n * ldo + static_cast<int64_t>(h) * dc + 128 * jb + 8 * c) =
+                    *reinterpret_cast<const u32x4 *>(&wt[r * kRow + 8 * c]);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_output_proj(const ProjShape &p, const void *x, const void *w, void *y,
@@ -333,6 +414,16 @@ hipError_t launch_output_proj(const ProjShape &p, const void *x, const void *w, 
 hipError_t launch_fold_value_output(int N, int H, int dv, int dc, bool bf16, const void *w_o,
                                     const void *w_uv, void *w_ov, hipStream_t st)
 {
+    const auto al = [](const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; };
+    if (bf16 && dv == kFoldDv && dc % 128 == 0 && al(w_o, 16) && al(w_uv, 16) && al(w_ov, 16)) {
+        // up to 4 row parts, so that enough waves stream W_O at once
+        const int chunks = (N + 63) / 64, parts = chunks < 4 ? chunks : 4;
+        const int rows = 64 * ((chunks + parts - 1) / parts);
+        fold_value_output_mfma_kernel<<<dim3(H, dc / 128, (N + rows - 1) / rows), 256, 0, st>>>(
+            N, H, dc, rows, static_cast<const uint16_t *>(w_o), static_cast<const uint16_t *>(w_uv),
+            static_cast<uint16_t *>(w_ov));
+        return hipGetLastError();
+    }
     dim3 grid((N + 63) / 64, (dc + 63) / 64, H);
     if (bf16)
         fold_value_output_kernel<true><<<grid, 256, 0, st>>>(N, H, dv, dc, w_o, w_uv, w_ov);

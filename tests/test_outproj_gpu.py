@@ -122,6 +122,8 @@ def test_decode_latent_matches_oracle(dtype, dims, H, L, splits):
 
 
 @pytest.mark.parametrize("dtype,d_model,H,dv,dc", [("bf16", 192, 128, 128, 512),
+                                                   ("bf16", 70, 3, 128, 256),   # MFMA form, partial row pass
+                                                   ("bf16", 33, 2, 64, 96),     # scalar form (d_v != 128)
                                                    ("f32", 70, 3, 20, 50)])
 def test_fold_value_output_matches_oracle(dtype, d_model, H, dv, dc):
     say(f"fold W_UV into W_O {dtype} d_model={d_model} H={H} dv={dv} dc={dc}")
