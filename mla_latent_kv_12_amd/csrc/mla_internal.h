@@ -38,12 +38,13 @@ struct DecodeWorkspace {
     float *o_lat;     // bf16 path with many query rows: [rows][H][dc] merged latents
 };
 
-// With many (query row, head) pairs (an absorbed prefill) the bf16 path
-// merges into fp32 latents and up-projects them with one batched product per
-// head, instead of re-reading W_UV[h] for every query row.
+// With many (query row, head) pairs (a decode batch of 8 or more at 128
+// heads, an absorbed prefill) the bf16 path merges into fp32 latents and
+// up-projects them with one batched product per head, instead of re-reading
+// W_UV[h] for every query row.
 inline bool batched_upproj(const DecodeShape &s, bool bf16)
 {
-    return bf16 && static_cast<int64_t>(s.B) * s.T * s.H >= 8192;
+    return bf16 && static_cast<int64_t>(s.B) * s.T * s.H >= 1024;
 }
 
 size_t decode_workspace_layout(const DecodeShape &s, bool bf16, DecodeWorkspace *ws_or_null,

@@ -75,8 +75,12 @@ def test_decode_workspace_size():
     q = 8 * 128 * 576 * 2
     o = 8 * 32 * 128 * 512 * 4
     ml = 8 * 32 * 128 * 2 * 4
+    lat = 8 * 128 * 512 * 4        # merged latents for the batched up-projection (B*H >= 1024)
     rnd = lambda x: (x + 255) // 256 * 256
-    assert ws == rnd(q) + rnd(o) + rnd(ml)
+    assert ws == rnd(q) + rnd(o) + rnd(ml) + rnd(lat)
+    # batch 4 (B*H = 512) keeps the fused merge + up-projection: no latent buffer
+    assert mla.decode_workspace_bytes(_v3_params(batch=4, num_splits=32)) == \
+        rnd(q // 2) + rnd(o // 2) + rnd(ml // 2)
     # the bf16 path rotates q_rope while placing it beside q~ (no extra room);
     # the fp32 path keeps a rotated copy
     assert mla.decode_workspace_bytes(_v3_params(num_splits=32, q_rope_base=10000.0)) == ws
@@ -195,8 +199,10 @@ def test_prefill_absorbed_workspace_and_splits():
     rows = T * 128
     rnd = lambda x: (x + 255) // 256 * 256
     assert mla.prefill_absorbed_num_splits(p) == 4
+    # q~ | q_rope, partials and (m, l) of 4 splits, and the merged latents of
+    # the batched up-projection (query rows x heads = 2048 >= 1024)
     assert mla.prefill_absorbed_workspace_bytes(p) == \
-        rnd(rows * 576 * 2) + rnd(rows * 4 * 512 * 4) + rnd(rows * 4 * 2 * 4)
+        rnd(rows * 576 * 2) + rnd(rows * 4 * 512 * 4) + rnd(rows * 4 * 2 * 4) + rnd(rows * 512 * 4)
     # auto split count: enough (query row, split) blocks for the chip
     auto = _prefill_params(tokens=T, n_max=131072, ckv_stride_b=131072 * 576,
                            kpe_stride_b=131072 * 576)
