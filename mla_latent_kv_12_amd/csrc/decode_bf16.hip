@@ -675,19 +675,21 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
 }
 
 // Batched up-projection for many query rows: out[v][h][i] = W_UV[h][i] . o[v][h]
-// for 32 query rows per workgroup and the 128 output features of head h
-// (wave w: features 32 w .. 32 w + 31), on MFMA.  A = W_UV rows straight from
-// global memory; B = the fp32 latents, each split into a bf16 high part and
-// a bf16 remainder (x = hi + lo to about 2^-17 relative), two MFMAs per K
-// step, so the product keeps the latent's fp32 precision.  W_UV[h] is read
-// once per 32 query rows.  Grid (H, ceil(rows / 32)), 256 threads.
-__global__ __launch_bounds__(256) void upproj_bf16_kernel(int H, int rows,
-                                                          const float *__restrict__ o_lat,
-                                                          const uint16_t *__restrict__ w_uv,
-                                                          void *__restrict__ out, int out_bf16)
+// for 32 query rows and 32 output features of head h per workgroup of one
+// wave (features 32 w .. 32 w + 31, w = blockIdx.x % 4), on MFMA; four
+// workgroups per head spread W_UV over four times as many CUs.  A = W_UV
+// rows straight from global memory; B = the fp32 latents, each split into a
+// bf16 high part and a bf16 remainder (x = hi + lo to about 2^-17
+// relative), two MFMAs per K step, so the product keeps the latent's fp32
+// precision.  W_UV[h] is read once per 32 query rows.
+// Grid (4 H, ceil(rows / 32)), 64 threads.
+__global__ __launch_bounds__(64) void upproj_bf16_kernel(int H, int rows,
+                                                         const float *__restrict__ o_lat,
+                                                         const uint16_t *__restrict__ w_uv,
+                                                         void *__restrict__ out, int out_bf16)
 {
-    const int h = blockIdx.x, v0 = blockIdx.y * 32;
-    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    const int h = blockIdx.x >> 2, wv = blockIdx.x & 3, v0 = blockIdx.y * 32;
+    const int lane = threadIdx.x;
     const int half = lane >> 5, l32 = lane & 31;
     // A: W_UV[h] row 32 wv + l32, elements 16 s + 8 half .. + 7 of step s
     const u32x4 *wrow = reinterpret_cast<const u32x4 *>(w_uv + (static_cast<int64_t>(h) * DV + 32 * wv + l32) * DC) + half;
@@ -780,8 +782,8 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
                                                               nullptr, ws.o_lat, 0, cv);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        dim3 ugrid(s.H, (rows + 31) / 32);
-        upproj_bf16_kernel<<<ugrid, 256, 0, st>>>(s.H, rows, ws.o_lat,
+        dim3 ugrid(4 * s.H, (rows + 31) / 32);
+        upproj_bf16_kernel<<<ugrid, 64, 0, st>>>(s.H, rows, ws.o_lat,
                                                   static_cast<const uint16_t *>(w_uv), out, s.out_bf16);
     } else if (w_uv) {
         merge_upproj_bf16_kernel<true><<<grid, 256, 0, st>>>(
