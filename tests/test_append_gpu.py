@@ -85,3 +85,21 @@ def test_append_f32_separate_caches(base):
     for b, pos in enumerate(positions):
         mask[b, pos] = False
     assert torch.equal(ckv[mask], b_ckv[mask]) and torch.equal(kpe[mask], b_kpe[mask])
+
+
+@pytest.mark.parametrize("B,d_model,dc,dr", [
+    (11, 7168, 512, 64),   # two sequence groups (8 + 3) over the V3 weights
+    (3, 72, 16, 6),        # quarters of 9 pieces, 22 rows: a partial row group of the workgroup
+    (2, 8, 4, 2),          # one 16-byte piece per row: three of the four waves have no share
+])
+def test_append_bf16_groups_and_small_shapes(B, d_model, dc, dr):
+    case = datagen.make_append_case(B=B, d_model=d_model, dc=dc, dr=dr, dtype="bf16", seed=79 + B)
+    n_max = 40
+    positions = [(7 * b + 3) % n_max for b in range(B)]
+    say(f"append bf16 B={B} d_model={d_model} dc={dc} dr={dr} positions={positions}")
+    g = torch.Generator(device="cuda").manual_seed(6)
+    cache = torch.randn((B, n_max, dc + dr), generator=g, device="cuda").to(torch.bfloat16)
+    before = cache.clone()
+    run_append(case, cache[:, :, :dc], cache[:, :, dc:], positions)
+    check_rows(case, cache[:, :, :dc], cache[:, :, dc:], before[:, :, :dc], before[:, :, dc:],
+               positions, n_max, "bf16")
