@@ -161,10 +161,12 @@ constexpr int kThreadsDec = 256;                // 4 waves x 32 heads
 constexpr int kLoadsPerWave = 9;                // 8 latent rows + 1/4 of the RoPE rows
 constexpr int kQRopeStride = kRopeRow + 16;     // 144 B per head row (bank stagger)
 constexpr int kQRopeBytes = 32 * kQRopeStride;  // one wave's 32 heads
+constexpr int kStageRow = 256 + 4;              // floats per staged partial row (bank stagger)
 static_assert(kTile == 4 * 8, "each wave loads 8 latent rows per tile");
 static_assert(kTile * kRopeRow == 4 * 64 * 16, "each wave loads one quarter of the RoPE rows");
 static_assert(kTile == kSplitGranule, "split boundaries must align to tiles");
 static_assert(3 * kTileBytes + 4 * kQRopeBytes <= 160 * 1024, "LDS budget");
+static_assert(128 * kStageRow * 4 <= 3 * kTileBytes, "the partial rows are staged in the tile buffers");
 
 // Byte offset of latent row r inside a tile.  Each row starts 16 B times a
 // stagger in 0..15 into its slot: 4 (r mod 4) + (r div 4 mod 4).  Rows that
@@ -394,16 +396,33 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     }
 
     // ---- write the split partial: un-normalised O, reference max, mass ----
-    // Accumulator q, element r is latent column 32 q + 8 (r/4) + 4 half + r%4.
+    // The workgroup's 128 heads are 128 consecutive 2-KiB rows of part_o.
+    // Accumulator q, element r is latent column 32 q + 8 (r/4) + 4 half + r%4
+    // of this lane's head; each lane's 16-byte pieces would land in 32
+    // different rows per store, so the rows are staged in the (now idle) tile
+    // buffers, half of the columns at a time, and written as whole 1-KiB row
+    // segments.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    float *orow = part_o + prow * DC;
+    float *stage = reinterpret_cast<float *>(tiles);  // [128 heads][kStageRow]
+    float *obase = part_o + ((static_cast<int64_t>(v) * S + sp) * H + hg * 128) * DC;
+    __syncthreads();  // every wave is done with the last tile
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
+    for (int p = 0; p < 2; ++p) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 v4 = {oacc[q][4 * m], oacc[q][4 * m + 1], oacc[q][4 * m + 2], oacc[q][4 * m + 3]};
-            *reinterpret_cast<f32x4 *>(orow + 32 * q + 8 * m + 4 * half) = v4;
+        for (int q = 8 * p; q < 8 * p + 8; ++q)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                *reinterpret_cast<f32x4 *>(stage + (32 * w + l32) * kStageRow + 32 * (q - 8 * p) + 8 * m + 4 * half) =
+                    f32x4{oacc[q][4 * m], oacc[q][4 * m + 1], oacc[q][4 * m + 2], oacc[q][4 * m + 3]};
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 128 * 64 / kThreadsDec; ++e) {
+            const int idx = tid + kThreadsDec * e, head = idx >> 6, piece = idx & 63;
+            *reinterpret_cast<f32x4 *>(obase + head * DC + 256 * p + 4 * piece) =
+                *reinterpret_cast<const f32x4 *>(stage + head * kStageRow + 4 * piece);
         }
+        __syncthreads();
+    }
     if (half == 0) {
         // NaN marks a head whose weights could overflow: the merge kernel
         // recomputes that (split, head) with the split's true maximum.
