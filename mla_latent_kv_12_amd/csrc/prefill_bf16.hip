@@ -253,6 +253,8 @@ constexpr int kVOff = kKrOff + kAT * DR * 2;            // 24 KiB
 constexpr int kATile = kVOff + kAT * DV * 2;            // 40 KiB
 constexpr int kADmaPerWave = kATile / 1024 / kAW;       // 5
 constexpr float kRescaleThreshold = 8.0f;
+constexpr int kAOutRow = DV * 2 + 16;                   // 272 B staged bf16 output row
+static_assert(kAW * 32 * kAOutRow <= 3 * kATile, "output rows are staged in the tile buffers");
 
 static_assert(kADmaPerWave * 1024 * kAW == kATile, "whole loads per wave");
 static_assert(kKrOff / 1024 == 2 * kAW && (kVOff - kKrOff) / 1024 == kAW &&
@@ -487,10 +489,36 @@ __global__ __launch_bounds__(kAThreads, 1) void prefill_attn_bf16_kernel(
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (t >= T) return;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int64_t orow = ((static_cast<int64_t>(b) * T + t) * H + h) * DV;
     // oacc[q][r] is value dim 32 q + 8 (r / 4) + 4 half + r % 4 of query t.
+    if (out_bf16) {
+        // The wave's 32 query rows are staged as bf16 in the idle tile
+        // buffers and written as whole 256-byte rows (a store straight from
+        // the accumulators would touch 32 rows per instruction).
+        __syncthreads();  // every wave is done with the last tile
+        unsigned char *wstage = tiles + w * (32 * kAOutRow);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d = 32 * q + 8 * g + 4 * half;
+                *reinterpret_cast<u32x2 *>(wstage + l32 * kAOutRow + 2 * d) =
+                    u32x2{pack_bf16(oacc[q][4 * g] * inv, oacc[q][4 * g + 1] * inv),
+                          pack_bf16(oacc[q][4 * g + 2] * inv, oacc[q][4 * g + 3] * inv)};
+            }
+        __syncthreads();
+        uint16_t *obase = reinterpret_cast<uint16_t *>(out) + ((static_cast<int64_t>(b) * T + q0) * H + h) * DV;
+#pragma unroll
+        for (int e = 0; e < 32 * 16 / 64; ++e) {
+            const int idx = lane + 64 * e, r = idx >> 4, pc = idx & 15;
+            if (q0 + r < T)
+                *reinterpret_cast<u32x4 *>(obase + static_cast<int64_t>(r) * H * DV + 8 * pc) =
+                    *reinterpret_cast<const u32x4 *>(wstage + r * kAOutRow + 16 * pc);
+        }
+        return;
+    }
+    if (t >= T) return;
+    const int64_t orow = ((static_cast<int64_t>(b) * T + t) * H + h) * DV;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
