@@ -173,6 +173,67 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+_TORCH_DTYPE = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16}
+
+
+def _need(t, what: str, shape, dtype) -> None:
+    """The library reads and writes plain pointers: every tensor must be a
+    contiguous GPU tensor of exactly the shape and dtype the call implies."""
+    if not isinstance(t, torch.Tensor):
+        raise MLAError(MLA_ERR_INVALID_ARG, f"{what} must be a tensor")
+    if t.device.type != "cuda":
+        raise MLAError(MLA_ERR_INVALID_ARG, f"{what} must be on the GPU (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise MLAError(MLA_ERR_INVALID_ARG, f"{what} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(int(d) for d in shape):
+        raise MLAError(MLA_ERR_INVALID_ARG,
+                       f"{what} must have shape {tuple(int(d) for d in shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise MLAError(MLA_ERR_INVALID_ARG, f"{what} must be contiguous")
+
+
+def _need_cache(t, what: str, batch: int, n_max: int, width: int, dtype, stride_b: int,
+                stride_n: int) -> None:
+    """A cache view: [batch, n_max, width] with unit element stride and the
+    sequence and row strides the parameters carry."""
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise MLAError(MLA_ERR_INVALID_ARG, f"{what} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise MLAError(MLA_ERR_INVALID_ARG, f"{what} must be {dtype} (got {t.dtype})")
+    if (t.dim() != 3 or tuple(t.shape) != (batch, n_max, width) or t.stride(2) != 1 or
+            (batch > 1 and t.stride(0) != stride_b) or t.stride(1) != stride_n):
+        raise MLAError(MLA_ERR_INVALID_ARG,
+                       f"{what} must be a [{batch}, {n_max}, {width}] view with unit element "
+                       f"stride and strides ({stride_b}, {stride_n}) (got shape "
+                       f"{tuple(t.shape)}, strides {tuple(t.stride())})")
+
+
+def _need_workspace(ws) -> None:
+    if ws is not None and (not isinstance(ws, torch.Tensor) or ws.device.type != "cuda" or
+                           ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous()):
+        raise MLAError(MLA_ERR_INVALID_ARG, "workspace must be a contiguous 1-D uint8 GPU tensor")
+
+
+def _check_attention_tensors(p, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, out,
+                             workspace, *, rows, out_width) -> None:
+    """rows: the leading query dimensions ((B,) for decode, (B, T) for prefill)."""
+    dt, odt = _TORCH_DTYPE[p.dtype], _TORCH_DTYPE[p.out_dtype]
+    _need(q_nope, "q_nope", rows + (p.heads, p.d_n), dt)
+    if p.d_r > 0:
+        _need(q_rope, "q_rope", rows + (p.heads, p.d_r), dt)
+    _need(w_uk, "w_uk", (p.heads, p.d_n, p.d_c), dt)
+    if w_uv is not None:
+        _need(w_uv, "w_uv", (p.heads, p.d_v, p.d_c), dt)
+    _need_cache(ckv_cache, "ckv_cache", p.batch, p.n_max, p.d_c, dt, p.ckv_stride_b,
+                p.ckv_stride_n)
+    if p.d_r > 0:
+        _need_cache(kpe_cache, "kpe_cache", p.batch, p.n_max, p.d_r, dt, p.kpe_stride_b,
+                    p.kpe_stride_n)
+    _need(seqlens, "seqlens", (p.batch,), torch.int32)
+    _need(out, "out", rows + (p.heads, out_width), odt)
+    _need_workspace(workspace)
+
+
 def _cache_strides(cache: torch.Tensor, width: int, what: str):
     if cache.dim() != 3 or cache.shape[2] != width or cache.stride(2) != 1:
         raise MLAError(MLA_ERR_INVALID_ARG, f"{what} must be a [B, N, {width}] view with unit "
@@ -213,6 +274,9 @@ def absorb_q(q_nope: torch.Tensor, w_uk: torch.Tensor, out: torch.Tensor | None 
     dc = w_uk.shape[2]
     if out is None:
         out = torch.empty((B, H, dc), dtype=torch.float32, device=q_nope.device)
+    _need(q_nope, "q_nope", (B, H, dn), q_nope.dtype)
+    _need(w_uk, "w_uk", (H, dn, dc), q_nope.dtype)
+    _need(out, "out", (B, H, dc), torch.float32)
     p = DecodeParams(batch=B, heads=H, d_c=dc, d_r=0, d_n=dn, d_v=1, n_max=1,
                      dtype=_dtype_code(q_nope.dtype), out_dtype=MLA_F32)
     qn, wk = q_nope.contiguous(), w_uk.contiguous()
@@ -241,6 +305,8 @@ def decode(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, out=Non
     if need == 0:
         _check(lib().mla_decode(ctypes.byref(params), None, None, None, None, None, None, None,
                                 None, None, 0, None))
+    _check_attention_tensors(params, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens,
+                             out, workspace, rows=(params.batch,), out_width=params.d_v)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
     if events is None:
@@ -278,6 +344,8 @@ def decode_latent(q_nope, q_rope, w_uk, ckv_cache, kpe_cache, seqlens, *, out=No
     if need == 0:
         _check(lib().mla_decode_latent(ctypes.byref(params), None, None, None, None, None, None,
                                        None, None, 0, None))
+    _check_attention_tensors(params, q_nope, q_rope, w_uk, None, ckv_cache, kpe_cache, seqlens,
+                             out, workspace, rows=(params.batch,), out_width=params.d_c)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
     _check(lib().mla_decode_latent(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
@@ -306,6 +374,11 @@ def output_proj(x, w, *, out=None, workspace=None, out_dtype=None, num_splits=0,
     if out is None:
         odt = torch.float32 if params.out_dtype == MLA_F32 else torch.bfloat16
         out = torch.empty((params.batch, params.out_features), dtype=odt, device=x.device)
+    dt, odt = _TORCH_DTYPE.get(params.dtype), _TORCH_DTYPE.get(params.out_dtype)
+    _need(x, "x", (params.batch, params.in_features), dt)
+    _need(w, "w", (params.out_features, params.in_features), dt)
+    _need(out, "out", (params.batch, params.out_features), odt)
+    _need_workspace(workspace)
     # 0 bytes: the direct form needs none, or params are invalid (the call
     # itself then reports why, before any launch)
     need = output_proj_workspace_bytes(params)
@@ -324,6 +397,10 @@ def fold_value_output(w_o, w_uv, *, out=None, stream=None):
     d_model = w_o.shape[0]
     if out is None:
         out = torch.empty((d_model, H * dc), dtype=w_o.dtype, device=w_o.device)
+    _dtype_code(w_o.dtype)
+    _need(w_o, "w_o", (d_model, H * dv), w_o.dtype)
+    _need(w_uv, "w_uv", (H, dv, dc), w_o.dtype)
+    _need(out, "out", (d_model, H * dc), w_o.dtype)
     _check(lib().mla_fold_value_output(d_model, H, dv, dc, _dtype_code(w_o.dtype), _ptr(w_o),
                                        _ptr(w_uv), _ptr(out), _stream(stream)))
     return out
@@ -367,6 +444,9 @@ def prefill_naive(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, 
     if need == 0:
         _check(lib().mla_prefill_naive(ctypes.byref(params), None, None, None, None, None, None,
                                        None, None, None, 0, None))
+    _check_attention_tensors(params, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens,
+                             out, workspace, rows=(params.batch, params.tokens),
+                             out_width=params.d_v)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
     _check(lib().mla_prefill_naive(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
@@ -401,6 +481,9 @@ def prefill_absorbed(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, 
     if need == 0:
         _check(lib().mla_prefill_absorbed(ctypes.byref(params), None, None, None, None, None,
                                           None, None, None, None, 0, None))
+    _check_attention_tensors(params, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens,
+                             out, workspace, rows=(params.batch, params.tokens),
+                             out_width=params.d_v)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
     _check(lib().mla_prefill_absorbed(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope),
@@ -425,6 +508,15 @@ def cache_append(h, w_dkv, w_kr, positions, ckv_cache, kpe_cache, *, rope_base=N
                      ckv_stride_b=csb, ckv_stride_n=csn, kpe_stride_b=ksb, kpe_stride_n=ksn,
                      rope_base=0.0 if rope_base is None else float(rope_base),
                      dtype=_dtype_code(h.dtype), reserved=0)
+    dt = h.dtype
+    _need(h, "h", (B, d_model), dt)
+    _need(w_dkv, "w_dkv", (dc, d_model), dt)
+    if dr > 0:
+        _need(w_kr, "w_kr", (dr, d_model), dt)
+    _need(positions, "positions", (B,), torch.int32)
+    _need_cache(ckv_cache, "ckv_cache", B, p.n_max, dc, dt, csb, csn)
+    if dr > 0:
+        _need_cache(kpe_cache, "kpe_cache", B, p.n_max, dr, dt, ksb, ksn)
     _check(lib().mla_cache_append(ctypes.byref(p), _ptr(h), _ptr(w_dkv), _ptr(w_kr),
                                   _ptr(positions), _ptr(ckv_cache),
                                   _ptr(kpe_cache) if dr > 0 else None, _stream(stream)))

@@ -8,6 +8,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import mla_latent_kv_12_amd as mla
 from mla_latent_kv_12_amd import binding, datagen
@@ -379,3 +380,26 @@ def test_datagen_is_seeded_and_shaped():
     # weights have std 1/sqrt(d_c)
     w = datagen.bf16_to_f32(c.w_uk)
     assert abs(w.std() * np.sqrt(512) - 1) < 0.02
+
+
+def test_binding_refuses_host_tensors_before_any_launch():
+    """The binding passes plain pointers, so it checks every tensor first: host
+    tensors are refused with MLA_ERR_INVALID_ARG and nothing reaches the GPU."""
+    B, H, N = 2, 128, 64
+    bf = torch.bfloat16
+    cache = torch.zeros((B, N, 576), dtype=bf)
+    args = (torch.zeros((B, H, 128), dtype=bf), torch.zeros((B, H, 64), dtype=bf),
+            torch.zeros((H, 128, 512), dtype=bf), torch.zeros((H, 128, 512), dtype=bf),
+            cache[:, :, :512], cache[:, :, 512:], torch.full((B,), N, dtype=torch.int32))
+    with pytest.raises(mla.MLAError) as err:
+        mla.decode(*args, workspace=None, out=torch.zeros((B, H, 128), dtype=bf))
+    assert err.value.status == mla.MLA_ERR_INVALID_ARG and "GPU" in str(err.value)
+    with pytest.raises(mla.MLAError) as err:
+        mla.output_proj(torch.zeros((8, 16384), dtype=bf), torch.zeros((7168, 16384), dtype=bf),
+                        out=torch.zeros((8, 7168), dtype=bf))
+    assert err.value.status == mla.MLA_ERR_INVALID_ARG
+    with pytest.raises(mla.MLAError) as err:
+        mla.cache_append(torch.zeros((B, 7168), dtype=bf), torch.zeros((512, 7168), dtype=bf),
+                         torch.zeros((64, 7168), dtype=bf), torch.zeros((B,), dtype=torch.int32),
+                         cache[:, :, :512], cache[:, :, 512:])
+    assert err.value.status == mla.MLA_ERR_INVALID_ARG

@@ -109,3 +109,28 @@ def test_naive_prefill_graph_replays_match_eager():
         torch.cuda.synchronize()
         say(f"  replay {rep}: equal {torch.equal(out, ref)}")
         assert torch.equal(out, ref)
+
+
+def test_binding_refuses_mismatched_tensors():
+    """Wrong shape, dtype or layout of a GPU tensor is refused before launch."""
+    case = datagen.make_decode_case(B=2, H=128, n_max=64, dtype="bf16", seed=4720,
+                                    seqlens=[64, 9], **V3)
+    t = decode_tensors(case)
+    args = [t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv_cache"], t["kpe_cache"],
+            t["seqlens"]]
+    bad_cases = [
+        (6, dict(), torch.zeros(2, dtype=torch.int64, device="cuda")),        # seqlens int64
+        (0, dict(), t["q_nope"].transpose(0, 1).contiguous().transpose(0, 1)),  # not contiguous
+    ]
+    for i, kw, bad in bad_cases:
+        a = list(args)
+        a[i] = bad
+        with pytest.raises(mla.MLAError) as err:
+            mla.decode(*a, softmax_scale=case.scale)
+        assert err.value.status == mla.MLA_ERR_INVALID_ARG
+    with pytest.raises(mla.MLAError):
+        mla.decode(*args, softmax_scale=case.scale,
+                   out=torch.empty((2, 128, 64), dtype=torch.bfloat16, device="cuda"))
+    ok = mla.decode(*args, softmax_scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(ok.float()).all()
