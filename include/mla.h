@@ -79,6 +79,9 @@ typedef enum mla_dtype {
  *    workgroup holds 128 heads).  n_max * row stride * 2 bytes of each
  *    cache must stay below 4 GiB per sequence.
  *    Cache pointers must be 16-byte aligned and row strides multiples of 8.
+ *  - any dtype: each cache's extent, (batch - 1) * stride_b + n_max *
+ *    stride_n elements, stays below 2^60 elements (so that every offset fits
+ *    in 64 bits; the same holds for the prefill and cache-append calls).
  * Anything else returns MLA_ERR_UNSUPPORTED: the library refuses a shape it
  * does not implement rather than computing something else (the
  * "mla-from-scratch" README's absorbed model likewise refuses to build from

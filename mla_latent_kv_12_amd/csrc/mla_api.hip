@@ -39,6 +39,15 @@ constexpr size_t kAlign = 256;
 constexpr int64_t kProjDirectGroups = 256;  // workgroups of the direct projection: one per CU
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// A cache's extent, (batch - 1) * stride_b + n_max * stride_n elements of
+// `elt` bytes, stays below 2^62 bytes: every later product of sizes and
+// strides (host checks and the kernels' 64-bit offsets) then fits in int64.
+bool cache_span_ok(int64_t batch, int64_t n_max, int64_t stride_b, int64_t stride_n, int64_t elt)
+{
+    const __int128 span = (__int128)(batch - 1) * stride_b + (__int128)n_max * stride_n;
+    return span * elt < ((__int128)1 << 62);
+}
+
 bool debug_checks()
 {
     const char *e = getenv("MLA_DEBUG_CHECKS");
@@ -114,14 +123,17 @@ mla_status check_decode_params(const mla_decode_params *p)
                     (long long)p->heads);
     if (p->ckv_stride_n < p->d_c || (p->d_r > 0 && p->kpe_stride_n < p->d_r))
         return fail(MLA_ERR_INVALID_ARG, "cache row stride smaller than the row width");
+    if (p->ckv_stride_b < 0 || p->kpe_stride_b < 0)
+        return fail(MLA_ERR_INVALID_ARG, "negative cache stride");
+    if (!cache_span_ok(p->batch, p->n_max, p->ckv_stride_b, p->ckv_stride_n, 4) ||
+        !cache_span_ok(p->batch, p->n_max, p->kpe_stride_b, p->kpe_stride_n, 4))
+        return fail(MLA_ERR_UNSUPPORTED, "cache strides span beyond the addressable range");
     if (p->dtype == MLA_BF16 && (p->n_max * p->ckv_stride_n * 2 >= ((int64_t)1 << 32) ||
                                  p->n_max * p->kpe_stride_n * 2 >= ((int64_t)1 << 32)))
         return fail(MLA_ERR_UNSUPPORTED, "bf16 decode addresses one sequence's cache with 32-bit offsets");
     if (p->batch > 1 && (p->ckv_stride_b < p->n_max * p->ckv_stride_n ||
                          (p->d_r > 0 && p->kpe_stride_b < p->n_max * p->kpe_stride_n)))
         return fail(MLA_ERR_INVALID_ARG, "cache sequence stride smaller than n_max rows");
-    if (p->ckv_stride_b < 0 || p->kpe_stride_b < 0)
-        return fail(MLA_ERR_INVALID_ARG, "negative cache stride");
     if (p->num_splits < 0 || p->num_splits > mla::kMaxSplits)
         return fail(MLA_ERR_INVALID_ARG, "num_splits must be in [0, %d]", mla::kMaxSplits);
     if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
@@ -370,6 +382,11 @@ mla_status check_prefill_params(const mla_prefill_params *p)
         return fail(MLA_ERR_UNSUPPORTED, "bf16 prefill supports d_c=512, d_r=64, d_n=d_v=128");
     if (p->ckv_stride_n < p->d_c || (p->d_r > 0 && p->kpe_stride_n < p->d_r))
         return fail(MLA_ERR_INVALID_ARG, "cache row stride smaller than the row width");
+    if (p->ckv_stride_b < 0 || p->kpe_stride_b < 0)
+        return fail(MLA_ERR_INVALID_ARG, "negative cache stride");
+    if (!cache_span_ok(p->batch, p->n_max + 256, p->ckv_stride_b, p->ckv_stride_n, 4) ||
+        !cache_span_ok(p->batch, p->n_max, p->kpe_stride_b, p->kpe_stride_n, 4))
+        return fail(MLA_ERR_UNSUPPORTED, "cache strides span beyond the addressable range");
     if (p->dtype == MLA_BF16 &&
         ((uint64_t)(p->n_max + 256) * (uint64_t)p->ckv_stride_n * 2 >= (1ull << 32) ||
          (uint64_t)p->n_max * (uint64_t)p->kpe_stride_n * 2 >= (1ull << 32)))
@@ -377,8 +394,6 @@ mla_status check_prefill_params(const mla_prefill_params *p)
     if (p->batch > 1 && (p->ckv_stride_b < p->n_max * p->ckv_stride_n ||
                          (p->d_r > 0 && p->kpe_stride_b < p->n_max * p->kpe_stride_n)))
         return fail(MLA_ERR_INVALID_ARG, "cache sequence stride smaller than n_max rows");
-    if (p->ckv_stride_b < 0 || p->kpe_stride_b < 0)
-        return fail(MLA_ERR_INVALID_ARG, "negative cache stride");
     if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
         return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
     return check_rope_base(p->q_rope_base, p->d_r);
@@ -626,6 +641,9 @@ mla_status mla_cache_append(const mla_append_params *p, const void *h, const voi
     if (p->ckv_stride_n < p->d_c || (p->d_r > 0 && p->kpe_stride_n < p->d_r) ||
         p->ckv_stride_b < 0 || p->kpe_stride_b < 0)
         return fail(MLA_ERR_INVALID_ARG, "cache strides smaller than the row width");
+    if (p->batch > 0 && (!cache_span_ok(p->batch, p->n_max, p->ckv_stride_b, p->ckv_stride_n, 4) ||
+                         !cache_span_ok(p->batch, p->n_max, p->kpe_stride_b, p->kpe_stride_n, 4)))
+        return fail(MLA_ERR_UNSUPPORTED, "cache strides span beyond the addressable range");
     if (p->batch > 1 && (p->ckv_stride_b < p->n_max * p->ckv_stride_n ||
                          (p->d_r > 0 && p->kpe_stride_b < p->n_max * p->kpe_stride_n)))
         return fail(MLA_ERR_INVALID_ARG, "cache sequence stride smaller than n_max rows");

@@ -126,6 +126,10 @@ def _msg():
     (dict(q_rope_base=float("inf")), mla.MLA_ERR_INVALID_ARG),
     (dict(ckv_stride_n=580, kpe_stride_n=580, ckv_stride_b=131072 * 580,
           kpe_stride_b=131072 * 580), mla.MLA_ERR_INVALID_ARG),  # rows not 16-byte aligned
+    # strides whose products with n_max or the batch would overflow 64 bits
+    (dict(ckv_stride_n=1 << 55), mla.MLA_ERR_UNSUPPORTED),
+    (dict(kpe_stride_b=1 << 62), mla.MLA_ERR_UNSUPPORTED),
+    (dict(ckv_stride_b=-576), mla.MLA_ERR_INVALID_ARG),
 ])
 def test_decode_rejects_bad_params_before_launch(kw, status):
     assert _call_decode(_v3_params(**kw)) == status
@@ -222,6 +226,8 @@ def test_prefill_absorbed_workspace_and_splits():
     (dict(num_splits=300), "INVALID_ARG"),
     (dict(q_rope_base=1.0), "INVALID_ARG"),
     (dict(softmax_scale=-1.0), "INVALID_ARG"),
+    (dict(ckv_stride_n=1 << 50), "UNSUPPORTED"),   # n_max * stride beyond 64 bits
+    (dict(kpe_stride_b=-8), "INVALID_ARG"),
 ])
 def test_prefill_absorbed_rejects_bad_params_before_launch(kw, status):
     lib = binding.lib()
@@ -326,6 +332,8 @@ def _append_params(**kw):
     (dict(ckv_stride_b=576), "INVALID_ARG"),
     (dict(rope_base=1.0), "INVALID_ARG"),
     (dict(rope_base=-5.0), "INVALID_ARG"),
+    (dict(ckv_stride_n=1 << 52), "UNSUPPORTED"),   # n_max * stride beyond 64 bits
+    (dict(kpe_stride_b=1 << 61), "UNSUPPORTED"),
 ])
 def test_append_rejects_bad_params_before_launch(kw, status):
     lib = binding.lib()
