@@ -52,20 +52,37 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, int T, i
     __shared__ float qs[kAbsorbBatch][DN];
     __shared__ float red[4][kAbsorbBatch][128];
 
-    for (int e = tid; e < kAbsorbBatch * DN; e += 256) {
-        const int bb = e / DN, i = e % DN;
-        qs[bb][i] = bb < nb ? bf16lo(q_nope[(static_cast<int64_t>(b0 + bb) * H + h) * DN + i]) : 0.f;
-    }
-    __syncthreads();
-
+    // Every global load is issued before the first wait: this wave's 32
+    // weight pieces, then the queries, then (quarter 0) the RoPE channel
+    // pair of this thread, so the kernel costs one memory round trip.
     const int col = qtr * 128 + 2 * lane;
-    float acc[kAbsorbBatch][2];
-#pragma unroll
-    for (int bb = 0; bb < kAbsorbBatch; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
     const uint32_t *wrow = reinterpret_cast<const uint32_t *>(w_uk + (static_cast<int64_t>(h) * DN + 32 * w) * DC + col);
     uint32_t wvals[32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) wvals[i] = wrow[i * (DC / 2)];  // 32 loads in flight
+    for (int i = 0; i < 32; ++i) wvals[i] = wrow[i * (DC / 2)];
+    constexpr int kQPer = kAbsorbBatch * DN / 256;  // query values per thread
+    uint16_t qv[kQPer];
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+        const int e = tid + 256 * k, bb = e / DN, i = e % DN;
+        qv[k] = q_nope[(static_cast<int64_t>(b0 + min(bb, nb - 1)) * H + h) * DN + i];
+    }
+    // one rotation pair per thread: nb * d_r / 2 <= 8 * 32 = 256 threads
+    static_assert(kAbsorbBatch * (DR / 2) <= 256, "one RoPE pair per thread");
+    const bool rope_lane = qtr == 0 && tid < nb * (DR / 2);
+    const int rv = b0 + tid / (DR / 2), ri = tid % (DR / 2);
+    const int64_t rrow = static_cast<int64_t>(rv) * H + h;
+    uint32_t two = rope_lane ? *reinterpret_cast<const uint32_t *>(q_rope + rrow * DR + 2 * ri) : 0u;
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+        const int e = tid + 256 * k, bb = e / DN, i = e % DN;
+        qs[bb][i] = bb < nb ? bf16lo(qv[k]) : 0.f;
+    }
+    __syncthreads();
+
+    float acc[kAbsorbBatch][2];
+#pragma unroll
+    for (int bb = 0; bb < kAbsorbBatch; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const uint32_t wv = wvals[i];
@@ -91,25 +108,20 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, int T, i
         reinterpret_cast<__bf16 *>(qa)[(static_cast<int64_t>(b0 + bb) * H + h) * DQK + qtr * 128 + c] =
             static_cast<__bf16>(v);
     }
-    if (qtr == 0) {  // RoPE query channels, one rotation pair per thread
-        for (int e = tid; e < nb * (DR / 2); e += 256) {
-            const int v = b0 + e / (DR / 2), i = e % (DR / 2);
-            const int64_t row = static_cast<int64_t>(v) * H + h;
-            uint32_t two = *reinterpret_cast<const uint32_t *>(q_rope + row * DR + 2 * i);
-            if (rope_base > 0.0) {
-                const int b = v / T;
-                const int pos = static_cast<int>(min<int64_t>(max(seqlens[b], 0), n_max)) - T + (v - b * T);
-                if (pos > 0) {
-                    const double theta = pow(rope_base, -2.0 * i / DR);
-                    double sn, cs;
-                    sincos(static_cast<double>(pos) * theta, &sn, &cs);
-                    const double x0 = bf16lo(two), x1 = bf16hi(two);
-                    two = pack_bf16(static_cast<float>(x0 * cs - x1 * sn),
-                                    static_cast<float>(x0 * sn + x1 * cs));
-                }
+    if (rope_lane) {  // RoPE query channels beside q~
+        if (rope_base > 0.0) {
+            const int b = rv / T;
+            const int pos = static_cast<int>(min<int64_t>(max(seqlens[b], 0), n_max)) - T + (rv - b * T);
+            if (pos > 0) {
+                const double theta = pow(rope_base, -2.0 * ri / DR);
+                double sn, cs;
+                sincos(static_cast<double>(pos) * theta, &sn, &cs);
+                const double x0 = bf16lo(two), x1 = bf16hi(two);
+                two = pack_bf16(static_cast<float>(x0 * cs - x1 * sn),
+                                static_cast<float>(x0 * sn + x1 * cs));
             }
-            *reinterpret_cast<uint32_t *>(qa + row * DQK + DC + 2 * i) = two;
         }
+        *reinterpret_cast<uint32_t *>(qa + rrow * DQK + DC + 2 * ri) = two;
     }
 }
 
@@ -718,28 +730,41 @@ __global__ __launch_bounds__(64) void upproj_bf16_kernel(int H, int rows,
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    constexpr int kU = 4;
-    for (int s0 = 0; s0 < DC / 16; s0 += kU) {
-        u32x4 a[kU];
-        f32x4 x0[kU], x1[kU];
+    // The 32 K steps in 4 batches of 8, double-buffered: the loads of batch
+    // k + 1 are issued before the MFMAs of batch k, so the call costs about
+    // one memory round trip instead of one per batch.
+    constexpr int kU = 8, kBatches = DC / 16 / kU;
+    u32x4 a[2][kU];
+    f32x4 x0[2][kU], x1[2][kU];
+    auto load = [&](int buf, int s0) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            a[u] = wrow[2 * (s0 + u)];
-            x0[u] = orow[4 * (s0 + u)];
-            x1[u] = orow[4 * (s0 + u) + 1];
+            a[buf][u] = wrow[2 * (s0 + u)];
+            x0[buf][u] = orow[4 * (s0 + u)];
+            x1[buf][u] = orow[4 * (s0 + u) + 1];
         }
+    };
+    // (the scheduling barriers keep the compiler from spreading a batch's
+    // loads between the previous batch's MFMAs)
+    load(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < kBatches; ++k) {
+        const int buf = k & 1;
+        if (k + 1 < kBatches) load(buf ^ 1, (k + 1) * kU);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const float x[8] = {x0[u][0], x0[u][1], x0[u][2], x0[u][3],
-                                x1[u][0], x1[u][1], x1[u][2], x1[u][3]};
+            const float x[8] = {x0[buf][u][0], x0[buf][u][1], x0[buf][u][2], x0[buf][u][3],
+                                x1[buf][u][0], x1[buf][u][1], x1[buf][u][2], x1[buf][u][3]};
             u32x4 hi, lo;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 hi[e] = pack_bf16(x[2 * e], x[2 * e + 1]);
                 lo[e] = pack_bf16(x[2 * e] - bf16lo(hi[e]), x[2 * e + 1] - bf16hi(hi[e]));
             }
-            acc = mfma32(a[u], hi, acc);
-            acc = mfma32(a[u], lo, acc);
+            acc = mfma32(a[buf][u], hi, acc);
+            acc = mfma32(a[buf][u], lo, acc);
         }
     }
     // acc[r] is feature 32 wv + 8 (r / 4) + 4 half + r % 4 of query row v0 + l32
