@@ -121,6 +121,35 @@ def cpu_baseline(case, seconds: float):
             "sample": f"{what}, {reps} pass(es), {ts:.1f} s in total, {t_step:.1f} s per step"}
 
 
+def cpu_baseline_sampled(run, units, seconds: float, value_of_time, unit: str, label: str):
+    """fp64 oracle on an evenly spaced sample of the call's independent units
+    (query rows, sequences), all host threads: about `seconds` of host work
+    (at least one unit; the whole call, repeated, when it is cheaper), scaled
+    to the whole call and reported as value_of_time(seconds per call)."""
+    import oracle  # test infrastructure, used here only for the CPU baseline leg
+    threads = oracle.max_threads()
+    n_all = len(units)
+
+    def pick(n):
+        return [units[int((i + 0.5) * n_all / n)] for i in range(n)]
+
+    t = time.perf_counter()
+    run(pick(1))
+    t1 = time.perf_counter() - t
+    n = int(min(n_all, max(1, round(seconds / max(t1, 1e-3)))))
+    reps, ts = 0, 0.0
+    while reps == 0 or (n == n_all and ts < 0.8 * seconds):
+        t = time.perf_counter()
+        run(pick(n))
+        ts += time.perf_counter() - t
+        reps += 1
+    t_call = ts / reps * n_all / n
+    what = (f"{n} of {n_all} {label}, evenly spaced" if n < n_all
+            else f"the whole call ({n_all} {label})")
+    return {"value": value_of_time(t_call), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{what}, {reps} pass(es), {ts:.1f} s in total, {t_call:.3g} s per call"}
+
+
 def bench_prefill(args, mla, datagen):
     """Naive causal prefill (decompress K/V for every cached row, then causal
     attention) on the V3 shape, batch 1, 4096 tokens; one JSON line with the
@@ -165,7 +194,7 @@ def bench_prefill(args, mla, datagen):
     f_attn = 2 * pairs * case.H * (case.dn + case.dr + case.dv)
     flops = f_decomp + f_attn
     tflops = flops / (ms * 1e-3) / 1e12
-    print(json.dumps({
+    line = {
         "mode": "prefill", "metric": "naive causal prefill bf16 MFMA TFLOP/s (% of dense peak)",
         "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "bf16",
@@ -176,8 +205,16 @@ def bench_prefill(args, mla, datagen):
                      "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                      "algorithmic_flops_per_call": flops, "decompress_flops": f_decomp,
                      "attention_flops": f_attn},
-        "ms_p10_p90": [float(np.percentile(per, 10)), float(np.percentile(per, 90))]}),
-        flush=True)
+        "ms_p10_p90": [float(np.percentile(per, 10)), float(np.percentile(per, 90))]}
+    if not args.no_cpu_baseline:
+        import oracle
+        line["cpu_baseline"] = cpu_baseline_sampled(
+            lambda rr: oracle.prefill_naive(case.q_nope, case.q_rope, case.w_uk, case.w_uv,
+                                            case.cache[:, :, :case.dc], case.cache[:, :, case.dc:],
+                                            case.seqlens, case.scale, rr),
+            [(b, t) for b in range(case.B) for t in range(case.T)], args.cpu_seconds,
+            lambda t_call: flops / t_call / 1e12, "TFLOP/s", "query rows (all heads)")
+    print(json.dumps(line), flush=True)
     return 0
 
 
@@ -228,7 +265,7 @@ def bench_chunk(args, mla, datagen):
     f_up = 2 * rows * case.H * case.dv * case.dc
     flops = f_absorb + f_attn + f_up
     tflops = flops / (ms * 1e-3) / 1e12
-    print(json.dumps({
+    line = {
         "mode": "chunk", "metric": "absorbed causal prefill bf16 MFMA TFLOP/s (% of dense peak)",
         "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "dtype": "bf16",
@@ -242,8 +279,17 @@ def bench_chunk(args, mla, datagen):
                      "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                      "algorithmic_flops_per_call": flops, "attention_flops": f_attn,
                      "absorb_and_upproj_flops": f_absorb + f_up},
-        "ms_p10_p90": [float(np.percentile(per, 10)), float(np.percentile(per, 90))]}),
-        flush=True)
+        "ms_p10_p90": [float(np.percentile(per, 10)), float(np.percentile(per, 90))]}
+    if not args.no_cpu_baseline:
+        import oracle
+        line["cpu_baseline"] = cpu_baseline_sampled(
+            lambda rr: oracle.prefill_absorbed(case.q_nope, case.q_rope, case.w_uk, case.w_uv,
+                                               case.cache[:, :, :case.dc],
+                                               case.cache[:, :, case.dc:], case.seqlens,
+                                               case.scale, rr),
+            [(b, t) for b in range(case.B) for t in range(case.T)], args.cpu_seconds,
+            lambda t_call: flops / t_call / 1e12, "TFLOP/s", "query rows (all heads)")
+    print(json.dumps(line), flush=True)
     return 0
 
 
@@ -297,7 +343,7 @@ def bench_outproj(args, mla, datagen):
                      "gbps": nbytes / (us * 1e-6) / 1e9,
                      "form": "direct" if ws.numel() == 0 else "sliced"}
     gbps = res["unfolded"]["gbps"]
-    print(json.dumps({
+    line = {
         "mode": "outproj", "metric": "output projection after decode, HBM GB/s (% of peak)",
         "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic (seeded normals)",
@@ -306,8 +352,19 @@ def bench_outproj(args, mla, datagen):
         "unfolded": res["unfolded"], "folded": res["folded"], "fold_weights_ms": fold_ms,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS,
-                     "kernel": "rowproj_direct_bf16_kernel (unfolded W_O)"}}),
-        flush=True)
+                     "kernel": "rowproj_direct_bf16_kernel (unfolded W_O)"}}
+    if not args.no_cpu_baseline:
+        import oracle
+
+        def bits(t):  # bf16 storage bits on the host, as the oracle takes them
+            return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+        xh, wh = bits(x_unf), bits(w_o)
+        nbytes = (w_o.numel() + x_unf.numel() + B * d_model) * 2
+        line["cpu_baseline"] = cpu_baseline_sampled(
+            lambda rr: oracle.output_proj(xh[rr], wh), list(range(B)), args.cpu_seconds,
+            lambda t_call: nbytes / t_call / 1e9, "GB/s", "rows of the unfolded projection")
+    print(json.dumps(line), flush=True)
     return 0
 
 
@@ -372,7 +429,7 @@ def bench_append(args, mla, datagen):
     nbytes = ((case.dc + case.dr) * case.d_model + case.B * case.d_model
               + case.B * (case.dc + case.dr)) * 2
     gbps = nbytes / (us * 1e-6) / 1e9
-    print(json.dumps({
+    line = {
         "mode": "append", "metric": "cache-row producer HBM GB/s (% of peak)", "value": gbps,
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "us_per_step": us, "us_per_call_eager": us_eager,
@@ -384,8 +441,15 @@ def bench_append(args, mla, datagen):
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_call": nbytes},
         "eager_us_p10_p90": [1e3 * float(np.percentile(per, 10)),
-                             1e3 * float(np.percentile(per, 90))]}),
-        flush=True)
+                             1e3 * float(np.percentile(per, 90))]}
+    if not args.no_cpu_baseline:
+        import oracle
+        pos_h = pos.cpu().numpy()
+        line["cpu_baseline"] = cpu_baseline_sampled(
+            lambda rr: oracle.cache_rows(case.h[rr], case.w_dkv, case.w_kr, pos_h[rr]),
+            list(range(case.B)), args.cpu_seconds, lambda t_call: nbytes / t_call / 1e9, "GB/s",
+            "sequences")
+    print(json.dumps(line), flush=True)
     return 0
 
 

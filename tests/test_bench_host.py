@@ -51,3 +51,26 @@ def test_traffic_record_is_consistent():
     fetch = float(kv["fetch_kib_per_dispatch"]) * fs * 1024
     write = float(kv["write_kib_per_dispatch"]) * ws * 1024
     assert abs(fetch + write - float(kv["traffic_bytes_per_launch"])) <= 1e-6 * (fetch + write)
+
+
+def test_sampled_oracle_baseline_scales_to_the_whole_call():
+    """The sampled baseline times evenly spaced units and scales by the
+    fraction sampled; when the whole call fits the budget it is repeated."""
+    seen = []
+
+    def run(units):   # a stand-in workload: 10 ms per unit
+        seen.append(list(units))
+        import time
+        time.sleep(0.01 * len(units))
+
+    r = bench.cpu_baseline_sampled(run, list(range(1000)), 0.1, lambda t: 1.0 / t, "calls/s",
+                                   "units")
+    assert seen[0] == [500]                            # calibration: the middle unit
+    n = len(seen[1])
+    assert 5 <= n <= 20 and seen[1] == sorted(set(seen[1]))
+    assert 0.05 < r["value"] <= 0.101                   # whole call ~ 1000 x 10 ms (sleep never short)
+    assert r["kind"] == "oracle" and f"{n} of 1000 units" in r["sample"]
+    seen.clear()
+    r = bench.cpu_baseline_sampled(run, [0, 1], 0.2, lambda t: t, "s", "units")
+    assert all(s == [0, 1] for s in seen[1:]) and len(seen) >= 3
+    assert "the whole call (2 units)" in r["sample"] and 0.0199 <= r["value"] < 0.04
