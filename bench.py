@@ -27,25 +27,36 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published peak
 METRIC = "decode tokens/s and achieved HBM GB/s (% of peak), MLA V3 shape @128k ctx"
 
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
+
+
 class HipEvents:
-    """hipEvent_t handles created through the HIP runtime that torch loaded."""
+    """hipEvent_t handles created through the HIP runtime that torch loaded,
+    for timing only: without the system-scope fence (an L2 write-back and
+    invalidate) that a default event performs when it is recorded, which
+    leaves the GPU idle for about 6 us between the kernels it separates."""
 
     def __init__(self, n):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self.ev.append(e)
 
     def group(self, i, k):
         arr = (ctypes.c_void_p * k)(*[self.ev[i + j].value for j in range(k)])
         return arr
+
+    def around_attention(self, i):
+        """mla_decode_profiled's four slots with events i, i + 1 around the
+        split-KV kernel only (NULL slots are not recorded)."""
+        return (ctypes.c_void_p * 4)(None, self.ev[i].value, self.ev[i + 1].value, None)
 
     def ms(self, a, b):
         out = ctypes.c_float()
@@ -121,6 +132,22 @@ def cpu_baseline(case, seconds: float):
             "sample": f"{what}, {reps} pass(es), {ts:.1f} s in total, {t_step:.1f} s per step"}
 
 
+def timed_back_to_back(step, steps: int) -> float:
+    """Mean ms per call of `steps` calls launched back to back between one
+    event pair (an event recorded between two launches idles the GPU for
+    about 6 us while its timestamp is written)."""
+    import torch
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
 def cpu_baseline_sampled(run, units, seconds: float, value_of_time, unit: str, label: str):
     """fp64 oracle on an evenly spaced sample of the call's independent units
     (query rows, sequences), all host threads: about `seconds` of host work
@@ -178,14 +205,7 @@ def bench_prefill(args, mla, datagen):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    evs[0].record()
-    for i in range(args.steps):
-        step()
-        evs[i + 1].record()
-    torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
-    ms = float(np.mean(per))
+    ms = timed_back_to_back(step, args.steps)
     L = case.seqlens.astype(np.int64)
     rows = int(L.sum())
     # causal (query, key) pairs: query t at position L - T + t sees keys 0..pos
@@ -205,7 +225,7 @@ def bench_prefill(args, mla, datagen):
                      "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                      "algorithmic_flops_per_call": flops, "decompress_flops": f_decomp,
                      "attention_flops": f_attn},
-        "ms_p10_p90": [float(np.percentile(per, 10)), float(np.percentile(per, 90))]}
+        "timing": "the K calls back to back between one event pair"}
     if not args.no_cpu_baseline:
         import oracle
         line["cpu_baseline"] = cpu_baseline_sampled(
@@ -249,14 +269,7 @@ def bench_chunk(args, mla, datagen):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    evs[0].record()
-    for i in range(args.steps):
-        step()
-        evs[i + 1].record()
-    torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
-    ms = float(np.mean(per))
+    ms = timed_back_to_back(step, args.steps)
     L = case.seqlens.astype(np.int64)
     rows = case.B * case.T
     pairs = int(sum(int(l) * case.T - case.T * (case.T - 1) // 2 for l in L))
@@ -279,7 +292,7 @@ def bench_chunk(args, mla, datagen):
                      "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                      "algorithmic_flops_per_call": flops, "attention_flops": f_attn,
                      "absorb_and_upproj_flops": f_absorb + f_up},
-        "ms_p10_p90": [float(np.percentile(per, 10)), float(np.percentile(per, 90))]}
+        "timing": "the K calls back to back between one event pair"}
     if not args.no_cpu_baseline:
         import oracle
         line["cpu_baseline"] = cpu_baseline_sampled(
@@ -328,19 +341,44 @@ def bench_outproj(args, mla, datagen):
         ws = torch.empty(mla.output_proj_workspace_bytes(params), dtype=torch.uint8,
                          device="cuda")
         y = torch.empty((B, d_model), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            mla.output_proj(x, w, out=y, workspace=ws, params=params)
+
         for _ in range(args.warmup):
-            mla.output_proj(x, w, out=y, workspace=ws, params=params)
+            step()
         torch.cuda.synchronize()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-        evs[0].record()
-        for i in range(args.steps):
-            mla.output_proj(x, w, out=y, workspace=ws, params=params)
-            evs[i + 1].record()
-        torch.cuda.synchronize()
-        us = 1e3 * float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]))
+        ref = y.clone()
+        # eager calls back to back: the host's launch path (argument checks
+        # and marshalling, 40-65 us) is slower than the kernel, so this
+        # measures the host
+        us_eager = 1e3 * timed_back_to_back(step, args.steps)
+        # device time: the steps captured back to back in one HIP graph,
+        # median of 3 replays, each checked against the eager result
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                step()
+        reps = []
+        for _ in range(3):
+            y.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            if not torch.equal(y, ref):
+                raise RuntimeError("graph replay of the projection differs from the eager call")
+            reps.append(1e3 * e0.elapsed_time(e1) / args.steps)
+        us = float(np.median(reps))
         nbytes = (w.numel() + x.numel() + y.numel()) * 2
-        res[name] = {"us_per_call": us, "weight_bytes": w.numel() * 2,
-                     "gbps": nbytes / (us * 1e-6) / 1e9,
+        res[name] = {"us_per_call": us, "us_per_call_eager": us_eager,
+                     "weight_bytes": w.numel() * 2, "gbps": nbytes / (us * 1e-6) / 1e9,
                      "form": "direct" if ws.numel() == 0 else "sliced"}
     gbps = res["unfolded"]["gbps"]
     line = {
@@ -349,6 +387,7 @@ def bench_outproj(args, mla, datagen):
         "higher_is_better": True, "dtype": "bf16", "data": "synthetic (seeded normals)",
         "config": {"workload": "V3 output projection batch 8, d_model 7168", "batch": B,
                    "heads": H, "d_v": dv, "d_c": dc, "d_model": d_model},
+        "timing": "HIP graph of the steps, median of 3 replays (eager: the host's launch rate)",
         "unfolded": res["unfolded"], "folded": res["folded"], "fold_weights_ms": fold_ms,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS,
@@ -546,21 +585,23 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = HipEvents(4 * K)
+    # The K timed calls, each with two fence-free HIP events recorded on the
+    # launch stream around its split-KV kernel (the roofline's kernel
+    # duration; each record idles the GPU for about 5 us, so no others are
+    # taken), between one event pair for the whole region.
+    ev = HipEvents(2 * K)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
     for i in range(K):
-        step(i, events=ev.group(4 * i, 4))
+        step(i, events=ev.around_attention(2 * i))
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
-    absorb = [ev.ms(4 * i, 4 * i + 1) for i in range(K)]
-    attn = [ev.ms(4 * i + 1, 4 * i + 2) for i in range(K)]
-    merge = [ev.ms(4 * i + 2, 4 * i + 3) for i in range(K)]
+    attn = [ev.ms(2 * i, 2 * i + 1) for i in range(K)]
     ev.close()
 
     ms_per_step = total_ms / K
@@ -598,9 +639,10 @@ def main(argv=None):
         "context_rows_per_s": rows / (ms_per_step * 1e-3),
         "mfma_tflops_call": flops / (ms_per_step * 1e-3) / 1e12,
         "wall_s_timed": wall,
-        "stages_us": {"absorb": 1e3 * float(np.mean(absorb)),
-                      "splitkv_attention": 1e3 * attn_ms,
-                      "merge_upproj": 1e3 * float(np.mean(merge)),
+        "timing": ("value: the K calls between one event pair; stages_us and roofline: "
+                   "hipEvents without the system fence around the split-KV kernel of the same "
+                   "calls"),
+        "stages_us": {"splitkv_attention": 1e3 * attn_ms,
                       "splitkv_p10_p90": [1e3 * float(np.percentile(attn, 10)),
                                           1e3 * float(np.percentile(attn, 90))]},
         "roofline": {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -183,7 +183,10 @@ mla_status mla_decode(const mla_decode_params *p, const void *q_nope, const void
  * NULL for none) on `stream`: events[0] before the absorb kernel, events[1]
  * between absorb and the split-KV attention kernel, events[2] between that
  * kernel and the merge/up-projection kernel, events[3] after the last
- * kernel.  For benchmarks that time the attention kernel on its own.
+ * kernel; a NULL entry skips that record.  For benchmarks that time the
+ * attention kernel on its own (each record between two kernels idles the
+ * GPU for a few microseconds, so a benchmark records only the events it
+ * reads).
  */
 mla_status mla_decode_profiled(const mla_decode_params *p, const void *q_nope,
                                const void *q_rope, const void *w_uk, const void *w_uv,

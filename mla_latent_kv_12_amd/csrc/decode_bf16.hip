@@ -794,7 +794,7 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
     // w_uv == nullptr: write the merged latent instead of W_UV[h] o_lat.
     uint16_t *qa = static_cast<uint16_t *>(ws.q);
     const int rows = s.B * s.T;  // query rows
-    if (events) (void)hipEventRecord(events[0], st);
+    if (events && events[0]) (void)hipEventRecord(events[0], st);
     {
         dim3 grid(4, s.H, (rows + kAbsorbBatch - 1) / kAbsorbBatch);
         absorb_bf16_kernel<<<grid, 256, 0, st>>>(rows, s.H, s.T, s.n_max, seqlens, s.q_rope_base,
@@ -804,7 +804,7 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (events) (void)hipEventRecord(events[1], st);
+    if (events && events[1]) (void)hipEventRecord(events[1], st);
     {
         dim3 grid(s.S, s.H / 128, rows);
         decode_splitkv_bf16_kernel<<<grid, kThreadsDec, 0, st>>>(
@@ -814,7 +814,7 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (events) (void)hipEventRecord(events[2], st);
+    if (events && events[2]) (void)hipEventRecord(events[2], st);
     dim3 grid(s.H, rows);
     CacheView cv{s.T, s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb, s.ckv_sn,
                  static_cast<const uint16_t *>(kpe), s.kpe_sb, s.kpe_sn, seqlens, qa,
@@ -837,7 +837,7 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
             s.H, s.S, ws.part_o, ws.part_ml, nullptr, out, s.out_bf16, cv);
     }
     e = hipGetLastError();
-    if (events) (void)hipEventRecord(events[3], st);
+    if (events && events[3]) (void)hipEventRecord(events[3], st);
     return e;
 }
 

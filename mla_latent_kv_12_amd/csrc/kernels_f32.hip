@@ -257,7 +257,7 @@ hipError_t launch_decode_f32(const DecodeShape &s, const float *q_nope, const fl
 {
     float *qabs = static_cast<float *>(ws.q);
     const int rows = s.B * s.T;  // query rows
-    if (events) (void)hipEventRecord(events[0], st);
+    if (events && events[0]) (void)hipEventRecord(events[0], st);
     hipError_t e;
     if (s.q_rope_base > 0.0 && s.dr > 0) {  // rotate the queries' RoPE channels at their positions
         e = launch_rope_q(s.B, s.T, s.H, s.dr, s.n_max, s.q_rope_base, false, seqlens, q_rope,
@@ -267,7 +267,7 @@ hipError_t launch_decode_f32(const DecodeShape &s, const float *q_nope, const fl
     }
     e = launch_absorb_f32(rows, s.H, s.dn, s.dc, false, q_nope, w_uk, qabs, st);
     if (e != hipSuccess) return e;
-    if (events) (void)hipEventRecord(events[1], st);
+    if (events && events[1]) (void)hipEventRecord(events[1], st);
     {
         dim3 grid(s.S, s.H, rows);
         size_t shm = sizeof(float) * (s.dc + s.dr + kThreads + kThreads / 64);
@@ -276,9 +276,9 @@ hipError_t launch_decode_f32(const DecodeShape &s, const float *q_nope, const fl
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (events) (void)hipEventRecord(events[2], st);
+    if (events && events[2]) (void)hipEventRecord(events[2], st);
     e = launch_merge_upproj_generic(s, ws, w_uv, false, out, st);
-    if (events) (void)hipEventRecord(events[3], st);
+    if (events && events[3]) (void)hipEventRecord(events[3], st);
     return e;
 }
 

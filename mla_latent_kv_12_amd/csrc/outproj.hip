@@ -121,9 +121,9 @@ __global__ __launch_bounds__(64 * kPWaves) void rowproj_bf16_kernel(
 
 // Direct form for weights with many rows: workgroup g takes rows
 // [g R, g R + R) (R <= 32: one MFMA tile, rows past R or N clamped on load
-// and not stored) over the whole of K, its 8 waves splitting K into eighths
-// of whole 16-element steps; the waves' sums are added in LDS in wave order
-// and stored in the output type.  No slice partials and no second launch;
+// and not stored) over the whole of K, its 8 waves taking interleaved
+// blocks of 4 16-element steps; the waves' sums are added in LDS in wave
+// order and stored in the output type.  No slice partials and no second launch;
 // R is chosen so that the row groups cover every CU once.
 // Grid (ceil(N / R), ceil(B / 32)).
 constexpr int kDWaves = 8;   // waves per workgroup, splitting K
@@ -136,8 +136,7 @@ __global__ __launch_bounds__(64 * kDWaves) void rowproj_direct_bf16_kernel(
     const int n0 = blockIdx.x * R, b0 = blockIdx.y * kPBatch;
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     const int half = lane >> 5, l32 = lane & 31;
-    const int steps = K / 16;
-    const int st0 = (steps * wv) / kDWaves, st1 = (steps * (wv + 1)) / kDWaves;
+    const int steps = K / 16;  // a multiple of kDUnroll: K % 64 == 0
 
     // A operand: weight row n0 + min(l32, R - 1) (inside the weight);
     // B operand: batch row b0 + l32 (zeros past the batch); elements
@@ -151,8 +150,13 @@ __global__ __launch_bounds__(64 * kDWaves) void rowproj_direct_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    int st = st0;
-    for (; st + kDUnroll <= st1; st += kDUnroll) {
+    // Wave w takes the blocks of kDUnroll steps b = w, w + 8, ...: at any
+    // time the workgroup's 8 waves read neighbouring 128-byte blocks of its
+    // rows, one 1-KiB span per row, rather than 8 spans 1/8 of the row
+    // apart (that form ran 44 or 66 us per call at the V3 width depending on
+    // the process, and 187 us folded, against 44 and 177 us for this one).
+    for (int blk = wv; blk * kDUnroll < steps; blk += kDWaves) {
+        const int st = blk * kDUnroll;
         u32x4 wa[kDUnroll], xb[kDUnroll];
 #pragma unroll
         for (int u = 0; u < kDUnroll; ++u) {
@@ -161,10 +165,6 @@ __global__ __launch_bounds__(64 * kDWaves) void rowproj_direct_bf16_kernel(
         }
 #pragma unroll
         for (int u = 0; u < kDUnroll; ++u) acc = mfma32(wa[u], xv ? xb[u] : zero, acc);
-    }
-    for (; st < st1; ++st) {
-        const u32x4 wq = wrow[2 * st], xq = xrow[2 * st];
-        acc = mfma32(wq, xv ? xq : zero, acc);
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g)

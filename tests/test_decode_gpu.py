@@ -281,3 +281,31 @@ def test_debug_checks_reject_lengths_outside_range(monkeypatch):
                          softmax_scale=case.scale)
     torch.cuda.synchronize()
     assert torch.equal(good, again) and torch.equal(good, clamped)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_profiled_decode_records_its_events_and_matches(dtype):
+    """mla_decode_profiled: the same output bitwise, with all four events or
+    only the two around the attention kernel (NULL slots skipped)."""
+    from bench import HipEvents
+    say(f"{dtype} decode with stage events")
+    if dtype == "bf16":
+        case = v3_case(2, 700, 931, seqlens=[700, 45])
+    else:
+        case = datagen.make_decode_case(B=2, H=4, n_max=200, seed=932, seqlens=[200, 17],
+                                        dtype="f32", dc=64, dr=16, dn=32, dv=32)
+    t = decode_tensors(case)
+    args = (t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv_cache"], t["kpe_cache"],
+            t["seqlens"])
+    ev = HipEvents(6)
+    plain = mla.decode(*args, softmax_scale=case.scale)
+    four = mla.decode(*args, softmax_scale=case.scale, events=ev.group(0, 4))
+    two = mla.decode(*args, softmax_scale=case.scale, events=ev.around_attention(4))
+    torch.cuda.synchronize()
+    try:
+        assert torch.equal(plain, four) and torch.equal(plain, two)
+        spans = [ev.ms(0, 1), ev.ms(1, 2), ev.ms(2, 3), ev.ms(4, 5)]
+        say(f"  stage ms {[round(x, 4) for x in spans]}")
+        assert all(x > 0 for x in spans)
+    finally:
+        ev.close()
