@@ -7,14 +7,18 @@
 // theta_i = base^(-2i/d_r) (RoFormer).
 //
 // A matrix-vector product per sequence: HBM-bound on the weights (d_c + d_r
-// rows of d_model values, 8.3 MB at the V3 shape), which every workgroup
-// reads once for a group of 8 sequences.  Workgroup = 4 waves and 4 output
-// rows; wave w streams the w-th quarter of all four rows in 16-byte pieces,
-// lane-strided, so that each hidden-state piece it loads serves four rows,
-// then the workgroup's 256 lanes are summed in LDS in a fixed order.  Rows d_c + 2i and
+// rows of d_model values, 8.3 MB at the V3 shape), in practice bound by the
+// stream from L2 into each CU, since every workgroup reads the hidden states
+// of its sequences in full.  Workgroup = 4 waves, 6 output rows and 4
+// sequences (grid.y runs over the sequence groups): wave w streams the w-th
+// quarter of the six rows in 16-byte pieces, lane-strided, so that each
+// hidden-state piece it loads serves six rows and each weight piece four
+// sequences; then the workgroup's 256 lanes are summed in LDS in a fixed
+// order.  At the V3 shape that is 96 x 2 workgroups reading 143 KB each,
+// against 144 reading 172 KB with 4 rows and 8 sequences.  Rows d_c + 2i and
 // d_c + 2i + 1 (one rotation pair) always fall in the same workgroup (row
-// groups start at multiples of 4 and d_c is even), which rotates the pair and
-// writes both.
+// groups start at multiples of 6 and d_c is even), which rotates the pair
+// and writes both.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -26,12 +30,15 @@ namespace {
 
 using namespace cdna4;
 
-constexpr int kAppendRows = 4;     // output rows per workgroup
+constexpr int kAppendRows = 6;     // output rows per workgroup (even: a RoPE pair never straddles two)
 constexpr int kAppendWaves = 4;    // waves per workgroup: contiguous quarters of d_model
-constexpr int kAppendGroup = 8;    // sequences per pass over the weight rows
+constexpr int kAppendGroup = 4;    // sequences per workgroup (grid.y runs over the groups)
 constexpr int kAppendUnroll = 2;   // 16-byte pieces per lane and row in flight per pass
-constexpr int kAppendVals = kAppendRows * kAppendGroup;  // dot products per workgroup and pass
-static_assert(64 * kAppendWaves == 8 * kAppendVals, "the lane sum runs as 8 chunks x 32 values");
+constexpr int kAppendVals = kAppendRows * kAppendGroup;  // dot products per workgroup
+constexpr int kAppendChunks = 8;   // the lane sum: 8 chunks of 32 lanes, then the chunks
+static_assert(kAppendChunks * 32 == 64 * kAppendWaves, "chunks of 32 lanes cover the workgroup");
+static_assert(kAppendChunks * kAppendVals <= 64 * kAppendWaves, "one thread per (chunk, value)");
+static_assert(kAppendRows % 2 == 0, "rotation pairs stay inside one workgroup");
 
 template <bool BF16>
 __device__ __forceinline__ void piece_to_f32(const u32x4 &v, float *f)
@@ -57,7 +64,7 @@ __global__ __launch_bounds__(64 * kAppendWaves) void cache_append_kernel(
 {
     constexpr int kVec = BF16 ? 8 : 4;  // elements per 16-byte piece
     __shared__ float part[64 * kAppendWaves][kAppendVals + 1];  // per lane, padded rows
-    __shared__ float part2[8][kAppendVals];
+    __shared__ float part2[kAppendChunks][kAppendVals];
     __shared__ float res[kAppendRows][kAppendGroup];
 
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
@@ -75,7 +82,9 @@ __global__ __launch_bounds__(64 * kAppendWaves) void cache_append_kernel(
                                  : w_kr + static_cast<int64_t>(row - dc) * pieces;
     }
 
-    for (int b0 = 0; b0 < B; b0 += kAppendGroup) {
+    // sequence groups: normally one per workgroup (grid.y = groups), more
+    // when the groups outnumber the grid's y range
+    for (int b0 = blockIdx.y * kAppendGroup; b0 < B; b0 += gridDim.y * kAppendGroup) {
         const int nb = min(kAppendGroup, B - b0);
         float acc[kAppendRows][kAppendGroup];
 #pragma unroll
@@ -85,7 +94,7 @@ __global__ __launch_bounds__(64 * kAppendWaves) void cache_append_kernel(
         // kAppendUnroll pieces per lane per pass, every load of a pass issued
         // before any is used (indices past the quarter or the group are
         // clamped to valid ones and their products dropped); each
-        // hidden-state piece serves all four rows
+        // hidden-state piece serves all the workgroup's rows
         for (int p0 = p_begin + lane; p0 < p_end; p0 += 64 * kAppendUnroll) {
             u32x4 wq[kAppendUnroll][kAppendRows], hq[kAppendUnroll][kAppendGroup];
 #pragma unroll
@@ -121,7 +130,7 @@ __global__ __launch_bounds__(64 * kAppendWaves) void cache_append_kernel(
 #pragma unroll
             for (int g = 0; g < kAppendGroup; ++g) part[tid][r * kAppendGroup + g] = acc[r][g];
         __syncthreads();
-        {
+        if (tid < kAppendChunks * kAppendVals) {
             const int v = tid % kAppendVals, c = tid / kAppendVals;
             float sum = 0.f;
             for (int l = 32 * c; l < 32 * c + 32; ++l) sum += part[l][v];
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(64 * kAppendWaves) void cache_append_kernel(
         if (tid < kAppendVals) {
             float sum = 0.f;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) sum += part2[c][tid];
+            for (int c = 0; c < kAppendChunks; ++c) sum += part2[c][tid];
             res[tid / kAppendGroup][tid % kAppendGroup] = sum;
         }
         __syncthreads();
@@ -175,7 +184,9 @@ hipError_t launch_cache_append(const AppendShape &s, const void *h, const void *
                                hipStream_t st)
 {
     const int rows = s.dc + s.dr;
-    const unsigned grid = static_cast<unsigned>((rows + kAppendRows - 1) / kAppendRows);
+    const int groups = (s.B + kAppendGroup - 1) / kAppendGroup;
+    const dim3 grid(static_cast<unsigned>((rows + kAppendRows - 1) / kAppendRows),
+                    static_cast<unsigned>(min(groups, 65535)));
     if (s.bf16)
         cache_append_kernel<true><<<grid, 64 * kAppendWaves, 0, st>>>(
             s.B, s.d_model, s.dc, s.dr, s.n_max, static_cast<const u32x4 *>(h),
