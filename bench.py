@@ -186,7 +186,14 @@ def bench_prefill(args, mla, datagen):
 
     from mla_latent_kv_12_amd.tensors import to_device
 
-    case = datagen.make_workload("v3-prefill-4k")
+    def latents_fp64(x, w_dkv):
+        # c = W_DKV x: the prefill workload's input latents (an untimed harness
+        # step, accumulated in fp64 and then stored as bf16)
+        xf = datagen.bf16_to_f32(x).astype(np.float64)
+        wf = datagen.bf16_to_f32(w_dkv).astype(np.float64)
+        return xf @ wf.T
+
+    case = datagen.make_workload("v3-prefill-4k", latents=latents_fp64)
     dt = case.dtype
     cache = to_device(case.cache, dt)
     q_nope, q_rope = to_device(case.q_nope, dt), to_device(case.q_rope, dt)

@@ -79,12 +79,13 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char *shared)
 // assembly so that the compiler does not track it: it would otherwise make
 // every later LDS read wait for all loads in flight.  Completion is awaited
 // explicitly (wait_then_barrier) before any wave reads the destination.  M0
-// carries the LDS address; the kernels using this have no other M0 user.
-// The instruction has no register result.
+// carries the LDS address and is declared clobbered, so the compiler never
+// keeps a value of its own in M0 across the load.  The instruction has no
+// register result.
 __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t lds_dst, unsigned voff)
 {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds_dst), "v"(voff), "s"(rsrc) : "memory");
+                 :: "s"(lds_dst), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
 // The same load with the non-temporal cache policy, for data that one call
@@ -93,7 +94,7 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t lds_dst, unsigned
 __device__ __forceinline__ void lds_dma16_stream(i32x4 rsrc, uint32_t lds_dst, unsigned voff)
 {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-                 :: "s"(lds_dst), "v"(voff), "s"(rsrc) : "memory");
+                 :: "s"(lds_dst), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 
 // Transposing LDS read (gfx950): within each group of 16 lanes, lane j gets

@@ -13,9 +13,10 @@ in float32, scaled where a standard deviation is given):
            uniform in [1, Nmax].
   prefill: q_nope [B,T,H,dn], q_rope [B,T,H,dr], W_UK, W_UV, then
            x [B,T,d_model] ~ N(0,1) and W_DKV [dc,d_model] (std
-           1/sqrt(d_model)); the latent rows are c = W_DKV x (accumulated in
-           float64, then stored), and the decoupled RoPE keys k^R [B,T,dr]
-           ~ N(0,1).  Queries' RoPE channels and k^R are taken as already
+           1/sqrt(d_model)); the latent rows c = W_DKV x come from a callable
+           the caller supplies (the tests pass the fp64 oracle's cache-row
+           producer), then are stored; then the decoupled RoPE keys k^R
+           [B,T,dr] ~ N(0,1).  Queries' RoPE channels and k^R are taken as already
            rotated: a rotation maps i.i.d. standard normals to i.i.d. standard
            normals, so the rotated values are drawn directly.
   chunk:   (a chunk of T new queries over a cached context, for the absorbed
@@ -139,8 +140,14 @@ def make_decode_case(*, B, H, dc, dr, dn, dv, n_max, dtype="bf16", seed=SEED_BAS
                       w_uk, w_uv, cache, seqlens)
 
 
-def make_prefill_case(*, B, T, H, dc, dr, dn, dv, d_model, dtype="bf16", seed=SEED_BASE,
-                      scale=None, name="custom"):
+def make_prefill_case(*, B, T, H, dc, dr, dn, dv, d_model, latents, dtype="bf16",
+                      seed=SEED_BASE, scale=None, name="custom"):
+    """Draw one causal-prefill workload.  The latent rows c = W_DKV x are the
+    caller's to compute (this module only draws random numbers):
+    ``latents(x_b, w_dkv)`` returns them in fp64, [T, dc], from sequence b's
+    stored hidden states x_b [T, d_model] and the stored W_DKV [dc, d_model];
+    they are rounded to the storage type here.  Draw order: q_nope, q_rope,
+    W_UK, W_UV, x, W_DKV, then the RoPE keys."""
     rng = np.random.default_rng(seed)
     w_std = 1.0 / math.sqrt(dc)
     q_nope = _store(_normal(rng, (B, T, H, dn)), dtype)
@@ -149,13 +156,12 @@ def make_prefill_case(*, B, T, H, dc, dr, dn, dv, d_model, dtype="bf16", seed=SE
     w_uv = _store(_normal(rng, (H, dv, dc), w_std), dtype)
     x = _store(_normal(rng, (B, T, d_model)), dtype)
     w_dkv = _store(_normal(rng, (dc, d_model), 1.0 / math.sqrt(d_model)), dtype)
-    xf = bf16_to_f32(x) if dtype == "bf16" else x
-    wf = bf16_to_f32(w_dkv) if dtype == "bf16" else w_dkv
     cache = np.empty((B, T, dc + dr), dtype=np.uint16 if dtype == "bf16" else np.float32)
-    wt = wf.astype(np.float64).T
     for b in range(B):
-        lat = (xf[b].astype(np.float64) @ wt).astype(np.float32)
-        cache[b, :, :dc] = _store(lat, dtype)
+        lat = np.asarray(latents(x[b], w_dkv), dtype=np.float64)
+        if lat.shape != (T, dc):
+            raise ValueError(f"latents() returned shape {lat.shape}, expected {(T, dc)}")
+        cache[b, :, :dc] = _store(lat.astype(np.float32), dtype)
     cache[:, :, dc:] = _store(_normal(rng, (B, T, dr)), dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(dn + dr)
@@ -234,7 +240,9 @@ WORKLOADS = {
 }
 
 
-def make_workload(name: str, seed: int | None = None):
+def make_workload(name: str, seed: int | None = None, latents=None):
+    """The named workload; prefill workloads need ``latents`` (see
+    :func:`make_prefill_case`)."""
     kind, offset, kw = WORKLOADS[name]
     seed = SEED_BASE + offset if seed is None else seed
     if kind == "decode":
@@ -243,4 +251,6 @@ def make_workload(name: str, seed: int | None = None):
         return make_append_case(seed=seed, **kw)
     if kind == "chunk":
         return make_chunk_case(seed=seed, **kw)
-    return make_prefill_case(seed=seed, **kw)
+    if latents is None:
+        raise ValueError(f"workload {name} needs latents(x, w_dkv) for c = W_DKV x")
+    return make_prefill_case(seed=seed, latents=latents, **kw)

@@ -62,7 +62,12 @@ def metrics(gpu: np.ndarray, ref: np.ndarray) -> dict:
 
 def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
     m = metrics(gpu, ref)
-    say(f"  parity {what}: {m}")
+    if dtype == "f32":
+        used = f"max-abs at {100 * m['max_abs'] / F32_TOL:.1f}% of its bound"
+    else:
+        used = (f"worst row at {100 * m['max_over_row_rms'] / BF16_REL_RMS:.1f}% of its bound, "
+                f"max-abs at {100 * m['max_abs'] / BF16_ABS:.1f}%")
+    say(f"  parity {what}: {used}; {m}")
     assert m["finite"], f"{what}: non-finite output"
     if dtype == "f32":
         assert m["max_abs"] <= F32_TOL, f"{what}: {m}"
@@ -73,10 +78,18 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
     return m
 
 
+def oracle_latents(x, w_dkv) -> np.ndarray:
+    """c = W_DKV x for the prefill workloads' latent rows, by the oracle's fp64
+    cache-row producer (no RoPE part)."""
+    c, _ = oracle.cache_rows(x, w_dkv, w_dkv[:0], np.zeros(len(x), dtype=np.int64))
+    return c
+
+
 def gather_pairs(out: torch.Tensor, pairs) -> np.ndarray:
     o = to_host_f64(out)
     return np.stack([o[b, h] for b, h in pairs])
 
 
 __all__ = ["say", "run_decode", "oracle_decode", "metrics", "assert_close", "gather_pairs",
+           "oracle_latents",
            "to_device", "to_host_f64", "decode_tensors", "F32_TOL"]

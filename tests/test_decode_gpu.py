@@ -74,36 +74,42 @@ def test_bf16_v3_4k_full():
     case = datagen.make_workload("v3-4k")
     say(f"V3 B=1 L=4096 seed={datagen.SEED_BASE + 1}")
     out = to_host_f64(run_decode(case))
-    assert_close(out, oracle_decode(case), "bf16", "all heads vs absorbed oracle")
-    pairs = [(0, h) for h in (0, 37, 101, 127)]
-    ref = oracle_decode(case, pairs=pairs, naive=True)
-    assert_close(np.stack([out[b, h] for b, h in pairs]), ref, "bf16", "4 heads vs naive oracle")
+    assert_close(out, oracle_decode(case), "bf16", "all 128 heads vs absorbed oracle")
+    # the naive decompress-then-attend definition on every head
+    assert_close(out, oracle_decode(case, naive=True), "bf16", "all 128 heads vs naive oracle")
     # the same workload with an fp32 output
     out32 = to_host_f64(run_decode(case, out_dtype="f32"))
     assert_close(out32, oracle_decode(case), "bf16", "fp32 output")
 
 
 def test_bf16_v3_ragged_full():
+    """Batch 32, lengths uniform in [1, 8192]: every (sequence, head) output
+    against the absorbed oracle, and 8 seeded pairs (the shortest and the
+    longest sequence among them) against the naive definition."""
     case = datagen.make_workload("v3-ragged")
     say(f"V3 B=32 ragged seed={datagen.SEED_BASE + 2} seqlens={case.seqlens.tolist()}")
-    out = run_decode(case)
+    out = to_host_f64(run_decode(case))  # automatic split count, as the benchmark launches it
+    assert_close(out, oracle_decode(case), "bf16", "all 4096 pairs vs absorbed oracle")
     order = np.argsort(case.seqlens)
     rng = np.random.default_rng(1)
-    bs = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
-    pairs = [(b, h) for b in sorted(bs) for h in range(128)]
-    pairs += [(int(rng.integers(32)), int(rng.integers(128))) for _ in range(64)]
-    ref = oracle_decode(case, pairs=pairs)
-    assert_close(gather_pairs(out, pairs), ref, "bf16", f"{len(pairs)} sampled pairs")
+    pairs = [(int(order[0]), 0), (int(order[-1]), 127)]
+    pairs += [(int(rng.integers(32)), int(rng.integers(128))) for _ in range(6)]
+    ref = oracle_decode(case, pairs=pairs, naive=True)
+    assert_close(np.stack([out[b, h] for b, h in pairs]), ref, "bf16", f"{pairs} vs naive oracle")
 
 
 def test_bf16_v3_128k_full():
+    """Batch 8 at 131072 cached rows, in the benchmark's launch configuration:
+    all 1024 (sequence, head) outputs against the absorbed oracle, and 2
+    seeded pairs against the naive definition (17 G multiply-adds each)."""
     case = datagen.make_workload("v3-128k")
     say(f"V3 B=8 L=131072 seed={datagen.SEED_BASE + 3}")
-    out = run_decode(case)  # automatic split count, as the benchmark launches it
+    out = to_host_f64(run_decode(case))  # automatic split count, as the benchmark launches it
+    assert_close(out, oracle_decode(case), "bf16", "all 1024 pairs vs absorbed oracle")
     rng = np.random.default_rng(3)
-    pairs = [(b, int(rng.integers(128))) for b in range(8)] + [(3, 0), (5, 127)]
-    ref = oracle_decode(case, pairs=pairs)
-    assert_close(gather_pairs(out, pairs), ref, "bf16", f"{len(pairs)} sampled pairs")
+    pairs = [(int(rng.integers(8)), int(rng.integers(128))) for _ in range(2)]
+    ref = oracle_decode(case, pairs=pairs, naive=True)
+    assert_close(np.stack([out[b, h] for b, h in pairs]), ref, "bf16", f"{pairs} vs naive oracle")
 
 
 # ---------------------------------------------------------------------------

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import mla_latent_kv_12_amd as mla
-from gpu_util import say
+from gpu_util import oracle_latents, say
 from mla_latent_kv_12_amd import datagen
 from mla_latent_kv_12_amd.tensors import decode_tensors, to_device
 
@@ -77,7 +77,8 @@ def test_decode_step_graph_replays_match_eager():
 
 def test_naive_prefill_graph_replays_match_eager():
     say("naive prefill captured in a HIP graph, 2 replays")
-    case = datagen.make_prefill_case(B=1, T=300, H=8, d_model=64, dtype="bf16", seed=4710, **V3)
+    case = datagen.make_prefill_case(B=1, T=300, H=8, d_model=64, dtype="bf16", seed=4710,
+                                     latents=oracle_latents, **V3)
     dt = case.dtype
     cache = to_device(case.cache, dt)
     qn, qr = to_device(case.q_nope, dt), to_device(case.q_rope, dt)

@@ -5,7 +5,7 @@ import torch
 
 import mla_latent_kv_12_amd as mla
 import oracle
-from gpu_util import assert_close, run_decode, say, to_device, to_host_f64
+from gpu_util import assert_close, oracle_latents, run_decode, say, to_device, to_host_f64
 from mla_latent_kv_12_amd import datagen
 
 pytestmark = pytest.mark.gpu
@@ -33,7 +33,8 @@ def make_case(B, T, L, H, dtype, seed, dims=None):
     """Prefill workload with L_b >= T cached rows (the last T are the queries)."""
     d = dims or dict(dc=512, dr=64, dn=128, dv=128)
     n_max = max(L)
-    base = datagen.make_prefill_case(B=B, T=n_max, H=H, d_model=64, dtype=dtype, seed=seed, **d)
+    base = datagen.make_prefill_case(B=B, T=n_max, H=H, d_model=64, dtype=dtype, seed=seed,
+                                     latents=oracle_latents, **d)
     # keep the first T query rows; seqlens may exceed T (bottom-right alignment)
     base.q_nope = np.ascontiguousarray(base.q_nope[:, :T])
     base.q_rope = np.ascontiguousarray(base.q_rope[:, :T])
@@ -117,7 +118,7 @@ def test_prefill_single_token_equals_decode():
 
 
 def test_prefill_v3_4k_full():
-    case = datagen.make_workload("v3-prefill-4k")
+    case = datagen.make_workload("v3-prefill-4k", latents=oracle_latents)
     say(f"V3 prefill T=4096 H=128 seed={datagen.SEED_BASE + 4}")
     t = prefill_tensors(case)
     out16 = run_prefill(case, t)              # the benchmark's launch: bf16 output
