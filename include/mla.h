@@ -42,8 +42,9 @@
  *    a launch failed to enqueue; faults inside kernels surface at the
  *    caller's next synchronisation.  mla_last_error() gives a per-thread
  *    message for the last failing call.  The library never aborts and no C++
- *    exception crosses this interface.  It holds no mutable global state and
- *    may be called from several threads at once.
+ *    exception crosses this interface.  It may be called from several
+ *    threads at once.  Its only mutable global state is the per-device
+ *    address table of mla_decode_noalloc's scratch array.
  */
 #ifndef MLA_H
 #define MLA_H
@@ -193,6 +194,37 @@ mla_status mla_decode_profiled(const mla_decode_params *p, const void *q_nope,
                                const void *ckv_cache, const void *kpe_cache,
                                const int32_t *seqlens, void *out, void *workspace,
                                size_t workspace_bytes, void *stream, void *const *events);
+
+/*
+ * Largest workspace, in bytes, that mla_decode_noalloc serves (80 MiB: the
+ * DeepSeek-V3 shape at batch 8 and 131072 cached tokens per sequence with
+ * the library's split count needs 67.4 MiB).
+ */
+#define MLA_DECODE_NOALLOC_MAX_BYTES ((size_t)80 << 20)
+
+/*
+ * mla_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without `workspace` / `workspace_bytes`, the same
+ * kernels and bitwise the same results as mla_decode with the same split
+ * count.  The workspace is a device array inside the library, of
+ * MLA_DECODE_NOALLOC_MAX_BYTES, that each GPU the library runs on holds
+ * until the process ends; its address on the current device is looked up
+ * on the first call there (`stream` must belong to the current device).
+ * No call allocates, frees or synchronises.
+ *   Returns MLA_ERR_WORKSPACE, before any launch, when
+ *   mla_decode_workspace_bytes(p) exceeds MLA_DECODE_NOALLOC_MAX_BYTES
+ *   (fewer sequences or context splits fit), and MLA_ERR_HIP when the
+ *   array's address cannot be looked up.
+ *   Every call on one GPU shares that GPU's array, and the kernels need
+ *   nothing of its previous contents: calls that overlap in time on one GPU
+ *   (on different streams, or from several threads) race on it and must be
+ *   ordered by the caller.
+ */
+mla_status mla_decode_noalloc(const mla_decode_params *p, const void *q_nope,
+                              const void *q_rope, const void *w_uk, const void *w_uv,
+                              const void *ckv_cache, const void *kpe_cache,
+                              const int32_t *seqlens, void *out, void *stream);
 
 /*
  * Shape of a naive causal prefill call: T new query tokens per sequence,

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     MLA_ERR_WORKSPACE,
     MLA_F32,
     MLA_OK,
+    NOALLOC_MAX_BYTES,
     AppendParams,
     DecodeParams,
     MLAError,
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     cache_append,
     decode,
     decode_latent,
+    decode_noalloc,
     decode_num_splits,
     decode_params,
     decode_workspace_bytes,

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 
 MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP = range(5)
 MLA_F32, MLA_BF16 = 0, 1
+NOALLOC_MAX_BYTES = 80 << 20  # MLA_DECODE_NOALLOC_MAX_BYTES in include/mla.h
 
 EXPORTS = (
     "mla_absorb_q",
@@ -24,6 +25,7 @@ EXPORTS = (
     "mla_decode_workspace_bytes",
     "mla_decode",
     "mla_decode_profiled",
+    "mla_decode_noalloc",
     "mla_decode_latent",
     "mla_prefill_workspace_bytes",
     "mla_prefill_naive",
@@ -116,6 +118,9 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_profiled.argtypes = [ctypes.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp,
                                           vp, vp, vp, sz, vp, vp]
         L.mla_decode_profiled.restype = ctypes.c_int
+        L.mla_decode_noalloc.argtypes = [ctypes.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp,
+                                         vp, vp, vp]
+        L.mla_decode_noalloc.restype = ctypes.c_int
         L.mla_decode_latent.argtypes = [ctypes.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp, vp,
                                         vp, sz, vp]
         L.mla_decode_latent.restype = ctypes.c_int
@@ -319,6 +324,24 @@ def decode(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, out=Non
                                          _ptr(kpe_cache), _ptr(seqlens), _ptr(out),
                                          _ptr(workspace), workspace.numel(), _stream(stream),
                                          events))
+    return out
+
+
+def decode_noalloc(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, *, out,
+                   softmax_scale=None, out_dtype=None, num_splits=0, q_rope_base=None,
+                   stream=None, params: DecodeParams | None = None):
+    """``mla_decode_noalloc``: mla_decode with the library's own fixed device
+    scratch (NOALLOC_MAX_BYTES) instead of a workspace; ``out`` is the
+    caller's.  Calls that overlap in time on one GPU race on that scratch."""
+    if params is None:
+        params = decode_params(q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache,
+                               softmax_scale=softmax_scale, out_dtype=out_dtype,
+                               num_splits=num_splits, q_rope_base=q_rope_base)
+    _check_attention_tensors(params, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens,
+                             out, None, rows=(params.batch,), out_width=params.d_v)
+    _check(lib().mla_decode_noalloc(ctypes.byref(params), _ptr(q_nope), _ptr(q_rope), _ptr(w_uk),
+                                    _ptr(w_uv), _ptr(ckv_cache), _ptr(kpe_cache), _ptr(seqlens),
+                                    _ptr(out), _stream(stream)))
     return out
 
 

@@ -9,6 +9,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "mla.h"
@@ -244,20 +246,21 @@ mla_status mla_absorb_q(const mla_decode_params *p, const void *q_nope, const vo
     return ok();
 }
 
-mla_status mla_decode_profiled(const mla_decode_params *p, const void *q_nope,
-                               const void *q_rope, const void *w_uk, const void *w_uv,
-                               const void *ckv_cache, const void *kpe_cache,
-                               const int32_t *seqlens, void *out, void *workspace,
-                               size_t workspace_bytes, void *stream, void *const *events)
+}  // extern "C"
+
+namespace {
+
+// Pointer and alignment checks of a decode call (after check_decode_params).
+mla_status check_decode_tensors(const mla_decode_params *p, const void *q_nope,
+                                const void *q_rope, const void *w_uk, const void *w_uv,
+                                const void *ckv_cache, const void *kpe_cache,
+                                const int32_t *seqlens, const void *out)
 {
-    mla_status st = check_decode_params(p);
-    if (st != MLA_OK) return st;
     if (!q_nope || !w_uk || !w_uv || !ckv_cache || !seqlens || !out)
         return fail(MLA_ERR_INVALID_ARG, "NULL tensor pointer");
     if (p->d_r > 0 && (!q_rope || !kpe_cache))
         return fail(MLA_ERR_INVALID_ARG, "NULL q_rope or kpe_cache with d_r > 0");
-    const bool bf16 = p->dtype == MLA_BF16;
-    if (bf16) {
+    if (p->dtype == MLA_BF16) {
         if (!aligned(ckv_cache, 16) || !aligned(kpe_cache, 16) || p->ckv_stride_n % 8 ||
             p->kpe_stride_n % 8 || p->ckv_stride_b % 8 || p->kpe_stride_b % 8)
             return fail(MLA_ERR_INVALID_ARG,
@@ -271,20 +274,22 @@ mla_status mla_decode_profiled(const mla_decode_params *p, const void *q_nope,
             !aligned(out, 4))
             return fail(MLA_ERR_INVALID_ARG, "fp32 tensors must be 4-byte aligned");
     }
-    mla::DecodeShape s = make_shape(p);
-    mla::DecodeWorkspace ws;
-    const size_t need = mla::decode_workspace_layout(s, bf16, &ws, workspace);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign))
-        return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu at %p)",
-                    need, workspace_bytes, workspace);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return MLA_OK;
+}
+
+// The launches of a checked decode call on workspace `ws` (laid out for s).
+mla_status launch_decode(const mla_decode_params *p, const mla::DecodeShape &s,
+                         const mla::DecodeWorkspace &ws, const void *q_nope, const void *q_rope,
+                         const void *w_uk, const void *w_uv, const void *ckv_cache,
+                         const void *kpe_cache, const int32_t *seqlens, void *out,
+                         hipStream_t hs, hipEvent_t const *ev)
+{
     if (debug_checks()) {
-        st = check_seqlens_debug(seqlens, p->batch, p->n_max, hs, 1);
+        mla_status st = check_seqlens_debug(seqlens, p->batch, p->n_max, hs, 1);
         if (st != MLA_OK) return st;
     }
     hipError_t e;
-    hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(events);
-    if (bf16)
+    if (p->dtype == MLA_BF16)
         e = mla::launch_decode_bf16(s, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens,
                                     out, ws, hs, ev);
     else
@@ -294,6 +299,94 @@ mla_status mla_decode_profiled(const mla_decode_params *p, const void *q_nope,
                                    static_cast<const float *>(kpe_cache), seqlens, out, ws, hs, ev);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace: the workspace lives in `scratch`, a
+// device array of fixed size that every GPU the library runs on holds once
+// (it is part of the library's code object).  In host code the array's name
+// is only a stand-in: its device address on the current GPU is looked up
+// once per device with hipGetSymbolAddress and kept in scratch_addr[].
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = MLA_DECODE_NOALLOC_MAX_BYTES;
+static_assert(kScratchBytes % kAlign == 0, "scratch size is a multiple of the region alignment");
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void *> scratch_addr[kMaxDevices];
+std::mutex scratch_mu;
+
+mla_status scratch_on_current_device(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MLA_ERR_UNSUPPORTED, "device %d beyond the %d devices the scratch table holds",
+                    dev, kMaxDevices);
+    void *ptr = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        ptr = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!ptr) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !ptr)
+                return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                            hipGetErrorString(e));
+            scratch_addr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_profiled(const mla_decode_params *p, const void *q_nope,
+                               const void *q_rope, const void *w_uk, const void *w_uv,
+                               const void *ckv_cache, const void *kpe_cache,
+                               const int32_t *seqlens, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream, void *const *events)
+{
+    mla_status st = check_decode_params(p);
+    if (st != MLA_OK) return st;
+    st = check_decode_tensors(p, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, out);
+    if (st != MLA_OK) return st;
+    mla::DecodeShape s = make_shape(p);
+    mla::DecodeWorkspace ws;
+    const size_t need = mla::decode_workspace_layout(s, p->dtype == MLA_BF16, &ws, workspace);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign))
+        return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes at 256-byte alignment (got %zu at %p)",
+                    need, workspace_bytes, workspace);
+    return launch_decode(p, s, ws, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, out,
+                         static_cast<hipStream_t>(stream),
+                         reinterpret_cast<hipEvent_t const *>(events));
+}
+
+mla_status mla_decode_noalloc(const mla_decode_params *p, const void *q_nope, const void *q_rope,
+                              const void *w_uk, const void *w_uv, const void *ckv_cache,
+                              const void *kpe_cache, const int32_t *seqlens, void *out,
+                              void *stream)
+{
+    mla_status st = check_decode_params(p);
+    if (st != MLA_OK) return st;
+    st = check_decode_tensors(p, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, out);
+    if (st != MLA_OK) return st;
+    mla::DecodeShape s = make_shape(p);
+    const size_t need = mla::decode_workspace_layout(s, p->dtype == MLA_BF16, nullptr, nullptr);
+    if (need > kScratchBytes)
+        return fail(MLA_ERR_WORKSPACE,
+                    "mla_decode_noalloc: this call needs %zu bytes of scratch, beyond the library's "
+                    "fixed %zu (fewer sequences or splits fit; mla_decode takes a caller workspace)",
+                    need, kScratchBytes);
+    void *base = nullptr;
+    st = scratch_on_current_device(&base);
+    if (st != MLA_OK) return st;
+    mla::DecodeWorkspace ws;
+    mla::decode_workspace_layout(s, p->dtype == MLA_BF16, &ws, base);
+    return launch_decode(p, s, ws, q_nope, q_rope, w_uk, w_uv, ckv_cache, kpe_cache, seqlens, out,
+                         static_cast<hipStream_t>(stream), nullptr);
 }
 
 mla_status mla_decode_latent(const mla_decode_params *p, const void *q_nope, const void *q_rope,

@@ -156,6 +156,33 @@ def test_decode_rejects_bad_workspace():
     assert str(need) in _msg()
 
 
+def test_noalloc_decode_refuses_before_any_launch():
+    """mla_decode_noalloc checks its arguments and the size of its fixed
+    scratch on the host first: a call that would need more than
+    MLA_DECODE_NOALLOC_MAX_BYTES, or with bad arguments, returns before any
+    device call (so this runs without a GPU)."""
+    lib = binding.lib()
+    vp = ctypes.c_void_p
+    ptrs = [vp(x) for x in (0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x5400, 0x6000, 0x7000)]
+
+    def call(p, args=ptrs):
+        return lib.mla_decode_noalloc(ctypes.byref(p), *args, None)
+
+    # the V3 128k decode at batch 8 fits with the library's split count; 64 splits do not
+    assert mla.decode_workspace_bytes(_v3_params()) <= mla.NOALLOC_MAX_BYTES
+    big = _v3_params(num_splits=64)
+    need = mla.decode_workspace_bytes(big)
+    assert need > mla.NOALLOC_MAX_BYTES
+    assert call(big) == mla.MLA_ERR_WORKSPACE
+    assert str(need) in _msg() and str(mla.NOALLOC_MAX_BYTES) in _msg()
+    assert call(_v3_params(num_splits=-1)) == mla.MLA_ERR_INVALID_ARG
+    assert call(_v3_params(d_c=256)) == mla.MLA_ERR_UNSUPPORTED
+    assert call(_v3_params(), [vp(0)] + ptrs[1:]) == mla.MLA_ERR_INVALID_ARG
+    header = open(HEADER).read()
+    assert re.search(r"#define MLA_DECODE_NOALLOC_MAX_BYTES \(\(size_t\)80 << 20\)", header)
+    assert mla.NOALLOC_MAX_BYTES == 80 << 20
+
+
 def test_absorb_rejects_bad_args():
     lib = binding.lib()
     vp = ctypes.c_void_p
