@@ -1,5 +1,5 @@
 // cdna4.h -- small gfx950 (CDNA4) device helpers shared by the bf16 kernels:
-// bf16 packing, the 32x32x16 bf16 MFMA, buffer descriptors, direct-to-LDS
+// bf16 packing, the 32x32x16 and 16x16x32 bf16 MFMAs, buffer descriptors, direct-to-LDS
 // buffer loads, the transposing LDS read and the wait + barrier hand-off.
 #pragma once
 
@@ -79,13 +79,17 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char *shared)
 // assembly so that the compiler does not track it: it would otherwise make
 // every later LDS read wait for all loads in flight.  Completion is awaited
 // explicitly (wait_then_barrier) before any wave reads the destination.  M0
-// carries the LDS address and is declared clobbered, so the compiler never
-// keeps a value of its own in M0 across the load.  The instruction has no
+// carries the LDS address; M0 is a register the compiler reserves for itself
+// (a clobber declaration of it is not honoured), so the sequence saves M0 in
+// a scratch SGPR and restores it after the load has issued (the load reads
+// M0 at issue), leaving M0 as the compiler left it.  The instruction has no
 // register result.
 __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t lds_dst, unsigned voff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :: "s"(lds_dst), "v"(voff), "s"(rsrc) : "memory", "m0");
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds_dst), "v"(voff), "s"(rsrc) : "memory");
 }
 
 // The same load with the non-temporal cache policy, for data that one call
@@ -93,8 +97,19 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t lds_dst, unsigned
 // kept in the caches for reuse.
 __device__ __forceinline__ void lds_dma16_stream(i32x4 rsrc, uint32_t lds_dst, unsigned voff)
 {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
-                 :: "s"(lds_dst), "v"(voff), "s"(rsrc) : "memory", "m0");
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds_dst), "v"(voff), "s"(rsrc) : "memory");
+}
+
+// D = A B + C on v_mfma_f32_16x16x32_bf16.  Lane l supplies row (A) or
+// column (B) l % 16 and K elements 8 (l / 16) .. 8 (l / 16) + 7; the result
+// lane l holds column l % 16, rows 4 (l / 16) + r, r = 0..3.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
 // Transposing LDS read (gfx950): within each group of 16 lanes, lane j gets

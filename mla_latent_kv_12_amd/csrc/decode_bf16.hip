@@ -128,32 +128,46 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, int T, i
 // ---------------------------------------------------------------------------
 // 2. split-KV flash-decode
 //
-// Workgroup = 4 waves = 128 heads of one sequence over one context split.
-// Cache tiles of 32 rows x 576 bf16 (36 KiB) are copied HBM -> LDS with
-// direct-to-LDS 16-byte buffer loads (buffer_load_dwordx4 ... lds, with the
-// non-temporal policy: a decode call reads each row once) into three LDS
-// buffers, so two tiles are in flight while one is consumed.  The buffer
-// descriptor's range ends at the split's last row: rows past it arrive as
-// zeros (weight zero, and they can never inject NaN/Inf).  The cross-wave
-// hand-off is an explicit "wait for my tile loads, then s_barrier".
+// Workgroup = 8 waves = 128 heads of one query row over one context split,
+// two waves per SIMD.  Cache tiles of 32 rows x 576 bf16 (36 KiB) are copied
+// HBM -> LDS with direct-to-LDS 16-byte buffer loads (non-temporal: a decode
+// call reads each row once) into four tile buffers; the buffer descriptor's
+// range ends at the split's last row, so rows past it arrive as zeros.
 //
-// LDS tile layout: latent row r (one 1-KiB load each, so its placement is
-// free) sits at r * 1280 + 16 * f(r), f(r) = 4 (r & 3) + ((r >> 2) & 3) < 16:
-// 1280-byte slots keep the staggered rows from overlapping and leave the bank
-// phase to f alone.  The stagger keeps both access patterns free of bank
-// conflicts: the score MFMA's lanes read 16 consecutive rows at one column
-// (f distinct over any 16 consecutive rows), and each 16-lane group of a
-// transposing read takes 32 bytes from 4 consecutive rows r = 4m..4m+3
-// (f = 4k + const, so their windows start 64 bytes apart).  Then come 32
-// RoPE-key rows of 128 bytes, 16-byte chunks XOR-swizzled by (row >> 1) & 7.
-// Every read address is a per-lane base plus an immediate.
+// The waves come in four pairs; pair p owns heads 32p .. 32p + 31 of the
+// workgroup's 128, and the two waves of a pair split the work of those heads:
+//   score   S[head][token] = Qa . C^T over the 576-wide row, for the 16 heads
+//           of the wave's half of the pair (v_mfma_f32_16x16x32_bf16, A = the
+//           absorbed query held in VGPRs, B = cache rows from LDS);
+//   softmax weights of those 16 heads, written to LDS as bf16 [token][head];
+//   latent  O^T[col][head] += C^T . P^T for all 32 heads of the pair and the
+//           wave's half of the 512 latent columns (v_mfma_f32_32x32x16_bf16,
+//           A = cache columns, B = the pair's softmax weights, both through
+//           the transposing LDS read), 128 accumulator registers.
+// A wave therefore needs 128 accumulator + 72 query registers and fits two to
+// a SIMD, so one wave's softmax and waits run under the other's MFMAs.  Each
+// LDS read of the cache tile serves 16 heads (score) or 32 heads (latent).
 //
-// Score  S^T[token][head] = C . Qa^T  (A = cache rows, B = absorbed query)
-// Accum  O^T[col][head] += C^T . P^T  (A = cache columns, read with the
-//        transposing ds_read_b64_tr_b16, B = softmax weights from registers)
-// both on v_mfma_f32_32x32x16_bf16.  The absorbed query's 512 latent channels
-// stay in VGPRs (128 per lane), its 64 RoPE channels in LDS; the 512 x 32 fp32
-// accumulator of the wave's heads fills the 256 AGPRs.
+// Pipeline, one workgroup barrier per tile: iteration i (after the barrier
+// that publishes tile i + 1 and the weights P(i)) issues the loads of tile
+// i + 3, computes the scores of tile i + 1 and writes their weights P(i + 1),
+// then the latent products of tile i.  Tiles i .. i + 3 occupy the four
+// buffers; P is double-buffered.  The two waves of a SIMD drift apart within
+// an iteration, so one's softmax overlaps the other's MFMAs.
+//
+// LDS tile layout: latent row r at r * 1024, its 16-byte chunk c stored at
+// chunk c ^ phase(r), phase(r) = 4 (r mod 4) + (r div 4 mod 4) (an
+// involution).  The 32 RoPE-key rows of 128 bytes follow, chunk c of row r
+// at c ^ rphase(r), rphase(r) = (r div 4 mod 4) + 4 (r div 2 mod 2).  The
+// loads place the chunks by gathering each lane's source chunk accordingly.
+// Bank behaviour measured on gfx950 (LDS bank-conflict counter): a 16-byte
+// read is conflict-free when, in each group of four consecutive lanes, the
+// lanes hit the four chunks of one 64-byte block of the 256-byte bank
+// window; a transposing read when the 32 lanes of each half hit 32 distinct
+// 8-byte slots.  The score read therefore takes the 16 tokens of a block in
+// the order phase(i) (lane i reads row phase(i), whose chunk 4 s + g then
+// sits at (4 s + g) ^ i), and the transposing reads take 4 consecutive rows;
+// both are conflict-free on this layout, and so are the weight reads.
 //
 // Softmax: scores are kept in log2 units (scale * log2(e) folded in).  The
 // reference maximum m_ref of each head is fixed by the split's first tile;
@@ -165,54 +179,33 @@ __global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, int T, i
 // ---------------------------------------------------------------------------
 constexpr int kTile = 32;                       // tokens per LDS tile (== split granule)
 constexpr int kLatRow = DC * 2;                 // 1024 B per latent row
-constexpr int kLatSlot = kLatRow + 256;         // 1280 B LDS slot per latent row
 constexpr int kRopeRow = DR * 2;                // 128 B
-constexpr int kRopeBase = kTile * kLatSlot;     // 40960: RoPE rows follow the latent slots
-constexpr int kTileBytes = kRopeBase + kTile * kRopeRow;  // 45056
-constexpr int kThreadsDec = 256;                // 4 waves x 32 heads
-constexpr int kLoadsPerWave = 9;                // 8 latent rows + 1/4 of the RoPE rows
-constexpr int kQRopeStride = kRopeRow + 16;     // 144 B per head row (bank stagger)
-constexpr int kQRopeBytes = 32 * kQRopeStride;  // one wave's 32 heads
+constexpr int kRopeOff = kTile * kLatRow;       // 32768: RoPE rows follow the latent rows
+constexpr int kTileBytes = kRopeOff + kTile * kRopeRow;  // 36864
+constexpr int kTileBufs = 4;
+constexpr int kPBytes = 128 * kTile * 2;        // softmax weights, 128 heads x 32 tokens (bf16)
+constexpr int kThreadsDec = 512;                // 8 waves, two per SIMD
 constexpr int kStageRow = 256 + 4;              // floats per staged partial row (bank stagger)
-static_assert(kTile == 4 * 8, "each wave loads 8 latent rows per tile");
-static_assert(kTile * kRopeRow == 4 * 64 * 16, "each wave loads one quarter of the RoPE rows");
 static_assert(kTile == kSplitGranule, "split boundaries must align to tiles");
-static_assert(3 * kTileBytes + 4 * kQRopeBytes <= 160 * 1024, "LDS budget");
-static_assert(128 * kStageRow * 4 <= 3 * kTileBytes, "the partial rows are staged in the tile buffers");
-
-// Byte offset of latent row r inside a tile.  Each row starts 16 B times a
-// stagger in 0..15 into its slot: 4 (r mod 4) + (r div 4 mod 4).  Rows that
-// one score read touches together (consecutive r) then start in distinct
-// 16-byte bank groups, and so do the rows of one transposing read.
-__host__ __device__ constexpr int lat_slot(int r)
-{
-    return r * kLatSlot + 16 * (4 * (r & 3) + ((r >> 2) & 3));
-}
-static_assert(lat_slot(kTile - 1) + kLatRow <= kRopeBase, "staggered rows fit before the RoPE rows");
-static_assert(16 * 15 + kLatRow <= kLatSlot, "a staggered row stays inside its slot");
-// Rows 16 ks + 8 + j and 16 ks + j differ by 8 * 1280 plus this stagger delta,
-// the same for every j in 0..7 and every ks, so the second transposing read
-// of a K step is the first one's address plus an immediate.
-// The loads address row 8 w + k of a tile through this closed form of lat_slot.
-__host__ __device__ constexpr int lat_slot_wk(int w, int k)
-{
-    return (8 * w + k) * kLatSlot + 16 * (4 * (k & 3) + ((2 * w + (k >> 2)) & 3));
-}
-static_assert(lat_slot_wk(0, 0) == lat_slot(0) && lat_slot_wk(1, 5) == lat_slot(13) &&
-              lat_slot_wk(2, 7) == lat_slot(23) && lat_slot_wk(3, 6) == lat_slot(30) &&
-              lat_slot_wk(3, 3) == lat_slot(27), "closed form of the load slots");
-constexpr int kTrHiStagger = lat_slot(8) - 8 * kLatSlot;
-static_assert(kTrHiStagger == lat_slot(9) - lat_slot(1) - 8 * kLatSlot &&
-              kTrHiStagger == lat_slot(15) - lat_slot(7) - 8 * kLatSlot &&
-              kTrHiStagger == lat_slot(31) - lat_slot(23) - 8 * kLatSlot,
-              "uniform stagger delta between the two halves of a K step");
+static_assert(kTileBufs * kTileBytes + 2 * kPBytes <= 160 * 1024, "LDS budget");
+static_assert(128 * kStageRow * 4 <= kTileBufs * kTileBytes, "partial rows are staged in the tile buffers");
 constexpr float kRefSlack = 64.0f;              // log2 headroom above the reference maximum
-// LDS operand reads kept in flight ahead of the MFMA that consumes them: with
-// one wave per SIMD, this depth is what covers the LDS latency.
-#ifndef MLA_DECODE_LOOKAHEAD
-#define MLA_DECODE_LOOKAHEAD 8
-#endif
-constexpr int kLook = MLA_DECODE_LOOKAHEAD;
+constexpr int kLookS = 4;                       // score operand reads in flight
+constexpr int kLookP = 2;                       // latent-product operand reads in flight
+
+// 16-byte chunk phase of latent row r (XOR applied to the chunk index); an
+// involution on 0..15: lat_phase(lat_phase(r)) = r for r < 16.
+__host__ __device__ constexpr int lat_phase(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+// 16-byte chunk phase of RoPE row r (0..7).
+__host__ __device__ constexpr int rope_phase(int r) { return ((r >> 2) & 3) + 4 * ((r >> 1) & 1); }
+static_assert(lat_phase(lat_phase(13)) == 13 && lat_phase(lat_phase(6)) == 6, "phase is an involution");
+
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     int T, int H, int S, int64_t n_max, const uint16_t *__restrict__ ckv, int64_t ckv_sb, int ckv_rowb,
@@ -220,26 +213,30 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ qa, float c2,
     float *__restrict__ part_o, float *__restrict__ part_ml)
 {
-    __shared__ __attribute__((aligned(1024))) unsigned char tiles[3 * kTileBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char qrope_lds[4 * kQRopeBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char tiles[kTileBufs * kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char pbuf[2 * kPBytes];
 
     // Query row v = b * T + t: query t of sequence b (T = 1 for decode)
     // attends to the causal prefix of its sequence's cache.
     const int sp = blockIdx.x, hg = blockIdx.y, v = blockIdx.z;
     const int b = v / T, tq = v - b * T;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int half = lane >> 5, l32 = lane & 31;
-    const int hq = hg * 128 + w * 32 + l32;  // this lane's head (score column)
+    const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, known uniform
+    const int pr = wu & 3, role = wu >> 2;      // pair, and this wave's half of it
+    const int l16 = lane & 15, g = lane >> 4;   // 16x16x32 layout: row/column, K slice
+    const int l32 = lane & 31, hh = lane >> 5;  // 32x32x16 layout: row/column, K half
+    const int hs0 = hg * 128 + 32 * pr + 16 * role;       // first of this wave's 16 score heads
+    const int hs = hs0 + l16;                              // query row of this lane (score A operand)
 
     const int L = query_len(seqlens[b], n_max, T, tq);
     const int ntiles_seq = (L + kTile - 1) / kTile;
     const int tps = (ntiles_seq + S - 1) / S;
     const int start = sp * tps * kTile;
     const int end = min(L, start + tps * kTile);
-    const int64_t prow = (static_cast<int64_t>(v) * S + sp) * H + hq;
 
     if (start >= end) {  // empty split: weight zero in the merge, O never read
-        if (half == 0) {
+        if (g == 0) {
+            const int64_t prow = (static_cast<int64_t>(v) * S + sp) * H + hs;
             part_ml[prow * 2 + 0] = -INFINITY;
             part_ml[prow * 2 + 1] = 0.f;
         }
@@ -247,199 +244,299 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     }
     const int ntiles = (end - start + kTile - 1) / kTile;
 
-    // Absorbed query of this lane's head as the score MFMA's B operand:
-    // B[k][j = head], lane holds k = 16 s + 8 half + 0..7.  Latent channels
-    // (s < 32) in registers; RoPE channels (s = 32..35) in this wave's LDS
-    // slice (head row l32 at a 144-byte stride).
-    const uint16_t *qrow = qa + (static_cast<int64_t>(v) * H + hq) * DQK + 8 * half;
-    u32x4 qreg[DC / 16];
-#pragma unroll
-    for (int s = 0; s < DC / 16; ++s) qreg[s] = *reinterpret_cast<const u32x4 *>(qrow + 16 * s);
-    const unsigned char *qr = qrope_lds + w * kQRopeBytes + l32 * kQRopeStride + 16 * half;
-#pragma unroll
-    for (int s = 0; s < DR / 16; ++s)
-        *reinterpret_cast<u32x4 *>(const_cast<unsigned char *>(qr) + 32 * s) =
-            *reinterpret_cast<const u32x4 *>(qrow + DC + 16 * s);
-    // Let the query loads land here, once: the compiler then knows they are
-    // complete and puts no wait on them inside the tile loop (where any
-    // vector-memory wait would also wait for the tile loads in flight).
-    __builtin_amdgcn_s_waitcnt(0);
-
-    // Buffer descriptors covering rows [0, end) of this sequence.
-    const i32x4 rs_lat =
-        make_rsrc(ckv + static_cast<int64_t>(b) * ckv_sb, static_cast<uint32_t>(end) * ckv_rowb);
-    const i32x4 rs_rope =
-        make_rsrc(kpe + static_cast<int64_t>(b) * kpe_sb, static_cast<uint32_t>(end) * kpe_rowb);
-
-    // This wave's nine loads of the tile starting at token n0: latent rows
-    // 8 w .. 8 w + 7 (one 1-KiB load each), and RoPE rows 8 w .. 8 w + 7 in
-    // one load (lane -> row 8 w + lane / 8, LDS chunk lane % 8 holding source
-    // chunk (lane % 8) ^ (row & 7)).
-    const unsigned lat_src = static_cast<unsigned>(8 * w * ckv_rowb + 16 * lane);
-    const int rr = 8 * w + (lane >> 3);
-    const unsigned rope_src = static_cast<unsigned>(rr * kpe_rowb + 16 * ((lane & 7) ^ ((rr >> 1) & 7)));
-    // LDS addresses of this wave's rows (wave-uniform, scalar arithmetic).
-    const int wu = __builtin_amdgcn_readfirstlane(w);
+    // ---- loads: wave w places latent rows 4w .. 4w + 3 of each tile, and
+    // waves 0..3 also RoPE rows 8w .. 8w + 7 (one 1-KiB load).  Each tile's
+    // buffer descriptors start at its first row and end at the split's last
+    // row, so rows past the end read as zeros and never reach memory. ----
+    const unsigned char *lat_seq =
+        reinterpret_cast<const unsigned char *>(ckv + static_cast<int64_t>(b) * ckv_sb);
+    const unsigned char *rope_seq =
+        reinterpret_cast<const unsigned char *>(kpe + static_cast<int64_t>(b) * kpe_sb);
     const uint32_t tiles_lds = lds_addr(tiles);
-    auto issue_tile = [&](int n0, int dst_buf) {
-        const unsigned lat_base = static_cast<unsigned>(n0) * static_cast<unsigned>(ckv_rowb);
-        const uint32_t dst = tiles_lds + static_cast<uint32_t>(dst_buf) * kTileBytes;
+    auto issue_tile = [&](int t) {
+        const int n0 = start + t * kTile;
+        const uint32_t dst = tiles_lds + static_cast<uint32_t>(t & 3) * kTileBytes;
+        const i32x4 rs_lat = make_rsrc(lat_seq + static_cast<int64_t>(n0) * ckv_rowb,
+                                       static_cast<uint32_t>(end - n0) * ckv_rowb);
+        // The per-lane source offsets are rebuilt for every tile from a lane
+        // index the compiler cannot see through, so that they are not kept
+        // live (the loop's registers are all taken).
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            lds_dma16_stream(rs_lat, dst + lat_slot_wk(wu, k),
-                         lat_src + lat_base + static_cast<unsigned>(k * ckv_rowb));
-        lds_dma16_stream(rs_rope, dst + kRopeBase + wu * 8 * kRopeRow,
-                     rope_src + static_cast<unsigned>(n0) * static_cast<unsigned>(kpe_rowb));
+        for (int k = 0; k < 4; ++k)   // row 4w + k: LDS chunk ln holds source chunk ln ^ phase
+            lds_dma16_stream(rs_lat, dst + (4 * wu + k) * kLatRow,
+                             static_cast<unsigned>((4 * wu + k) * ckv_rowb + 16 * (ln ^ lat_phase(4 * wu + k))));
+        if (wu < 4) {  // RoPE rows 8w + ln / 8, LDS chunk ln % 8 holding source chunk (ln % 8) ^ rphase
+            const i32x4 rs_rope = make_rsrc(rope_seq + static_cast<int64_t>(n0) * kpe_rowb,
+                                            static_cast<uint32_t>(end - n0) * kpe_rowb);
+            const int rq = 8 * wu + (ln >> 3);
+            lds_dma16_stream(rs_rope, dst + kRopeOff + wu * 8 * kRopeRow,
+                             static_cast<unsigned>(rq * kpe_rowb + 16 * ((ln & 7) ^ rope_phase(rq))));
+        }
+    };
+    // Wait until this wave's loads of tile t have landed, given whether the
+    // next tile's loads were issued after them (5 loads per tile on waves
+    // 0..3, 4 on waves 4..7), then meet the other waves.
+    auto wait_tile_then_barrier = [&](bool next_in_flight) {
+        if (wu < 4) {
+            if (next_in_flight) vm_wait<5>(); else vm_wait<0>();
+        } else {
+            if (next_in_flight) vm_wait<4>(); else vm_wait<0>();
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
-    // Per-lane LDS offsets within a tile (immediates are added per access).
-    // Score A operand, latent step s: row l32, byte 32 s + 16 half.
-    const int s_lat = lat_slot(l32) + 16 * half;
-    // P.C A operand via the transposing read, K step ks, j-block q, read r:
-    // source lane 4 k + c of each 16-lane group g addresses token (row)
-    // 16 ks + 8 r + 4 (g >> 1) + k, latent columns 32 q + 16 (g & 1) + 4 c.
-    // lat_slot of that row = its lane part lat_slot(4 (g >> 1) + k) plus
-    // (16 ks + 8 r) * 1280 + r * kTrHiStagger, an immediate.
-    const int g16 = lane >> 4, k4 = (lane >> 2) & 3, c4 = lane & 3;
-    const int pv_base = lat_slot(4 * (g16 >> 1) + k4) + 2 * (16 * (g16 & 1) + 4 * c4);
+    issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
 
-    f32x16 oacc[16];
+    // Absorbed query of head l16 of the wave's 16 as the 16x16x32 A operand:
+    // K step s holds channels 32 s + 8 g .. + 7 (s < 16 latent, s = 16, 17 RoPE).
+    const uint16_t *qrow = qa + (static_cast<int64_t>(v) * H + hs) * DQK + 8 * g;
+    u32x4 qreg[DQK / 32];
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
+    for (int s = 0; s < DQK / 32; ++s) qreg[s] = *reinterpret_cast<const u32x4 *>(qrow + 32 * s);
+    // Let the query loads land here, once (they also retire tiles 0 and 1):
+    // the compiler then puts no wait on them inside the tile loop.
+    __builtin_amdgcn_s_waitcnt(0);
+    if (ntiles > 2) issue_tile(2);
+    // From here on this wave's vector-memory operations are tile loads only,
+    // issued in tile order, so "tile t landed" is a count of loads in flight.
+
+    // ---- per-lane LDS offsets within a tile (immediates added per access) ----
+    // Only one base per access pattern stays live through the loop; the
+    // variants that differ from it by an XOR of a few address bits are formed
+    // at the start of each phase (from an opaque copy, so that the compiler
+    // does not hoist them out of the loop: its registers are all taken).
+    //
+    // Score B operand, token block tb, K step s < 16: MFMA column l16 is row
+    // 16 tb + phase(l16) (its token), logical chunk 4 s + g, stored at chunk
+    // (4 s + g) ^ l16: byte (sc0 ^ 64 (s & 3)) + 16384 tb + 256 (s >> 2).
+    const unsigned sc0 = lat_phase(l16) * kLatRow + 64 * (l16 >> 2) + 16 * (g ^ (l16 & 3));
+    // RoPE steps s = 16 + s2: logical chunk 4 s2 + g of RoPE row 16 tb +
+    // phase(l16), at chunk (4 s2 + g) ^ rphase(row): byte (rp0 ^ 64 s2) + 2048 tb.
+    const unsigned rp0 = kRopeOff + lat_phase(l16) * kRopeRow + 64 * ((l16 >> 3) & 1) + 16 * (g ^ (l16 & 3));
+    // Latent-product A operand through the transposing read: column block q
+    // (32 columns of this wave's half), K step ks, read ri.  Source lane
+    // 4 k + c of 16-lane group G addresses token 16 ks + 8 (G >> 1) + 4 ri + k,
+    // columns 256 role + 32 q + 16 (G & 1) + 4 c; the lane then holds column
+    // 32 q + (lane & 31), tokens 16 ks + 8 (lane >> 5) + 4 ri + 0..3.  With
+    // ri = 0 the byte offset is (pv0 ^ 64 (q & 3)) + 16384 ks + 256 (q >> 2);
+    // ri = 1 (4 rows on, chunk bit 0 flipped) adds 4096 to that with bit 4
+    // flipped.
+    const unsigned pv0 = [&] {
+        const int kk = l16 >> 2, cc = l16 & 3, G = lane >> 4, h2 = G >> 1;
+        const int a = 2 * (G & 1) + (cc >> 1);
+        return static_cast<unsigned>((8 * h2 + kk) * kLatRow + 512 * role + 64 * kk +
+                                     16 * (a ^ ((2 * h2) & 3)) + 8 * (cc & 1));
+    }();
+    // Softmax weights in LDS: [pair][32 tokens][32 heads] bf16 (64-byte rows),
+    // the 16-byte chunk c of token row t at c ^ (t div 4 mod 4).  This lane
+    // writes heads 16 role + 4 g .. + 3 of token 16 tb + phase(l16).  The
+    // latent product reads them back as its B operand through the
+    // transposing read: source lane 4 k + c of group G addresses token
+    // 16 ks + 8 (G >> 1) + 4 ri + k, heads 16 (G & 1) + 4 c .. + 3, so the
+    // lane holds head lane & 31, tokens 16 ks + 8 hh + 4 ri + 0..3 (the same
+    // tokens as its A operand).  ri = 1 is 4 rows on with chunk bit 0 flipped.
+    const uint32_t pw_off = pr * 2048 + lat_phase(l16) * 64 + 16 * ((2 * role + (g >> 1)) ^ (l16 & 3)) + 8 * (g & 1);
+    const uint32_t pr_off = [&] {
+        const int kk = l16 >> 2, cc = l16 & 3, G = lane >> 4;
+        return static_cast<uint32_t>(pr * 2048 + (8 * (G >> 1) + kk) * 64 +
+                                     16 * ((2 * (G & 1) + (cc >> 1)) ^ ((2 * (G >> 1)) & 3)) + 8 * (cc & 1));
+    }();
+
+    f32x16 oacc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[q][r] = 0.f;
-    float m_ref = -INFINITY;  // per head (lane column): the first tile's maximum
-    float l_run = 0.f;
-    bool over = false;        // a later score exceeded m_ref + 64 for this head
+    // Softmax state of this lane's 4 score heads 4 g + r (r = 0..3).
+    float m_ref[4];           // the split's first tile's maximum, per head
+    float l_run[4];           // this lane's share of each head's softmax mass
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { m_ref[r] = -INFINITY; l_run[r] = 0.f; }
+    int over = 0;             // bit r: a later score of head 4 g + r exceeded its m_ref + 64
 
-    // One tile: wait for it, hand the next-but-one tile's loads to the
-    // hardware, then scores, softmax weights and the latent accumulation.
-    auto tile_step = [&](int t, const unsigned char *tb, int next_buf) {
-        const int n0 = start + t * kTile;
-        if (t + 1 < ntiles)
-            wait_then_barrier<kLoadsPerWave>();
-        else
-            wait_then_barrier<0>();
-        if (t + 2 < ntiles) issue_tile(n0 + 2 * kTile, next_buf);
-
-        // ---- scores: S^T[token i][head j] = sum_k C[i][k] Qa[j][k] ----
-        const unsigned char *sa = tb + s_lat;
-        const unsigned char *sr = tb + kRopeBase + l32 * kRopeRow;
-        auto a_at = [&](int s) -> u32x4 {
-            if (s < DC / 16) return *reinterpret_cast<const u32x4 *>(sa + 32 * s);
-            return *reinterpret_cast<const u32x4 *>(sr + 16 * ((2 * (s - DC / 16) + half) ^ ((l32 >> 1) & 7)));
+    // Scores of tile t (buffer t & 3) for this wave's 16 heads: sacc[tb][r] is
+    // head 4 g + r, token 16 tb + phase(l16).
+    auto scores = [&](int t, f32x4 (&sacc)[2]) {
+        const unsigned char *tb = tiles + (t & 3) * kTileBytes;
+        unsigned sb = sc0, rb = rp0;
+        asm volatile("" : "+v"(sb), "+v"(rb));
+        const unsigned sc_base[4] = {sb, sb ^ 64u, sb ^ 128u, sb ^ 192u};
+        const unsigned rp_base[2] = {rb, rb ^ 64u};
+        auto a_at = [&](int i) -> u32x4 {  // i = 2 s + token block
+            const int s = i >> 1, blk = i & 1;
+            if (s < DC / 32)
+                return *reinterpret_cast<const u32x4 *>(tb + sc_base[s & 3] + 16384 * blk + 256 * (s >> 2));
+            return *reinterpret_cast<const u32x4 *>(tb + rp_base[s - DC / 32] + 2048 * blk);
         };
-        f32x16 sacc;
+        sacc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x4 abuf[kLookS];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-        u32x4 abuf[kLook];
+        for (int i = 0; i < kLookS; ++i) abuf[i] = a_at(i);
 #pragma unroll
-        for (int s = 0; s < kLook; ++s) abuf[s] = a_at(s);
-#pragma unroll
-        for (int s = 0; s < DQK / 16; ++s) {
-            const u32x4 bq = s < DC / 16 ? qreg[s]
-                                         : *reinterpret_cast<const u32x4 *>(qr + 32 * (s - DC / 16));
-            sacc = mfma32(abuf[s % kLook], bq, sacc);
-            if (s + kLook < DQK / 16) abuf[s % kLook] = a_at(s + kLook);
+        for (int i = 0; i < 2 * (DQK / 32); ++i) {
+            sacc[i & 1] = mfma16(qreg[i >> 1], abuf[i % kLookS], sacc[i & 1]);
+            if (i + kLookS < 2 * (DQK / 32)) abuf[i % kLookS] = a_at(i + kLookS);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // sacc[r] is token 8 (r/4) + 4 half + r%4 of the tile, head l32.
-        float tmax = -INFINITY;
+    };
+    // Softmax weights of tile t from its scores, written to P buffer t & 1.
+    auto softmax = [&](int t, f32x4 (&sacc)[2]) {
+        const int n0 = start + t * kTile;
+        const int tok0 = n0 + lat_phase(l16);  // this lane's token of block 0
+        float lmax[4];
         if (n0 + kTile <= end) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sacc[r] *= c2;
-                tmax = fmaxf(tmax, sacc[r]);
+            for (int r = 0; r < 4; ++r) {
+                sacc[0][r] *= c2;
+                sacc[1][r] *= c2;
+                lmax[r] = fmaxf(sacc[0][r], sacc[1][r]);
             }
         } else {  // the split's last, partial tile
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int tok = n0 + 8 * (r >> 2) + 4 * half + (r & 3);
-                sacc[r] = tok < end ? sacc[r] * c2 : -INFINITY;
-                tmax = fmaxf(tmax, sacc[r]);
+            for (int r = 0; r < 4; ++r) {
+                sacc[0][r] = tok0 < end ? sacc[0][r] * c2 : -INFINITY;
+                sacc[1][r] = tok0 + 16 < end ? sacc[1][r] * c2 : -INFINITY;
+                lmax[r] = fmaxf(sacc[0][r], sacc[1][r]);
             }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        if (t == 0) m_ref = tmax;
-        over |= tmax > m_ref + kRefSlack;
-
-        u32x4 pk[2];
-        float psum = 0.f;
+        if (t == 0) {  // each head's maximum over the first tile: its 16 lanes
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const float p0 = __builtin_amdgcn_exp2f(sacc[8 * ks + 2 * p] - m_ref);
-                const float p1 = __builtin_amdgcn_exp2f(sacc[8 * ks + 2 * p + 1] - m_ref);
-                psum += p0 + p1;
-                pk[ks][p] = pack_bf16(p0, p1);
+            for (int r = 0; r < 4; ++r) {
+                float m = lmax[r];
+                m = fmaxf(m, __shfl_xor(m, 1));
+                m = fmaxf(m, __shfl_xor(m, 2));
+                m = fmaxf(m, __shfl_xor(m, 4));
+                m = fmaxf(m, __shfl_xor(m, 8));
+                m_ref[r] = m;
             }
-        l_run += psum;
-
-        // ---- O^T[col][head] += C^T[col][token] P^T[token][head] ----
-        // K step ks covers tokens 16 ks + 8 (e / 4) + 4 half + e % 4 (e = 0..7
-        // across the two transposing reads), where the score accumulator left
-        // them; j-block q holds latent columns 32 q .. 32 q + 31.
-        const unsigned char *pv = tb + pv_base;
-        auto a_tr = [&](int ks, int q) -> u32x4 {
-            const u32x2 lo = lds_read_tr4(pv + (16 * ks) * kLatSlot + 64 * q);
-            const u32x2 hi = lds_read_tr4(pv + (16 * ks + 8) * kLatSlot + kTrHiStagger + 64 * q);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) over |= static_cast<int>(lmax[r] > m_ref[r] + kRefSlack) << r;
+        unsigned char *pw = pbuf + (t & 1) * kPBytes + pw_off;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[r] = __builtin_amdgcn_exp2f(sacc[tb][r] - m_ref[r]);
+                l_run[r] += p[r];
+            }
+            *reinterpret_cast<u32x2 *>(pw + 1024 * tb) = u32x2{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3])};
+        }
+    };
+    // Latent products of tile t with the pair's weights from P buffer t & 1.
+    auto latent = [&](int t) {
+        const unsigned char *tb = tiles + (t & 3) * kTileBytes;
+        unsigned pq = (t & 1) * kPBytes + pr_off;
+        asm volatile("" : "+v"(pq));
+        auto p_tr = [&](int ks) -> u32x4 {
+            const u32x2 lo = lds_read_tr4(pbuf + pq + 1024 * ks);
+            const u32x2 hi = lds_read_tr4(pbuf + (pq ^ 16u) + 256 + 1024 * ks);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
         };
-        u32x4 av[kLook];
+        const u32x4 pk0 = p_tr(0);
+        const u32x4 pk1 = p_tr(1);
+        unsigned pb = pv0;
+        asm volatile("" : "+v"(pb));
+        const unsigned pv_base[4][2] = {{pb, (pb ^ 16u) + 4096u},
+                                        {pb ^ 64u, (pb ^ 80u) + 4096u},
+                                        {pb ^ 128u, (pb ^ 144u) + 4096u},
+                                        {pb ^ 192u, (pb ^ 208u) + 4096u}};
+        auto a_tr = [&](int i) -> u32x4 {  // i = 8 ks + q
+            const int ks = i >> 3, q = i & 7;
+            const u32x2 lo = lds_read_tr4(tb + pv_base[q & 3][0] + 16384 * ks + 256 * (q >> 2));
+            const u32x2 hi = lds_read_tr4(tb + pv_base[q & 3][1] + 16384 * ks + 256 * (q >> 2));
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        u32x4 av[kLookP];
 #pragma unroll
-        for (int i = 0; i < kLook; ++i) av[i] = a_tr(0, i);
+        for (int i = 0; i < kLookP; ++i) av[i] = a_tr(i);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {  // i = 16 ks + q
-            const int ks = i >> 4, q = i & 15;
-            oacc[q] = mfma32(av[i % kLook], pk[ks], oacc[q]);
-            if (i + kLook < 32) av[i % kLook] = a_tr((i + kLook) >> 4, (i + kLook) & 15);
+        for (int i = 0; i < 16; ++i) {
+            oacc[i & 7] = mfma32(av[i % kLookP], (i >> 3) ? pk1 : pk0, oacc[i & 7]);
+            if (i + kLookP < 16) av[i % kLookP] = a_tr(i + kLookP);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    issue_tile(start, 0);
-    if (ntiles > 1) issue_tile(start + kTile, 1);
-    int buf = 0;  // tile t lives in buffer t % 3
-    for (int t = 0; t < ntiles; ++t) {
-        const int nxt = buf == 0 ? 2 : buf - 1;  // (t + 2) % 3
-        tile_step(t, tiles + buf * kTileBytes, nxt);
-        buf = buf == 2 ? 0 : buf + 1;
+    // Prologue: tile 0's scores and weights.
+    wait_tile_then_barrier(ntiles > 2);   // tiles 0 and 1 landed above; tile 0 visible to all
+    {
+        f32x4 sacc[2];
+        scores(0, sacc);
+        softmax(0, sacc);
+    }
+    for (int i = 0; i < ntiles; ++i) {
+        // Tile i + 1 landed (tile i + 2 may still be in flight), P(i)
+        // written, and every wave is done with tile i - 1's buffer.
+        wait_tile_then_barrier(i + 2 < ntiles);
+        if (i + 3 < ntiles) issue_tile(i + 3);
+        if (i + 1 < ntiles) {
+            f32x4 sacc[2];
+            scores(i + 1, sacc);
+            softmax(i + 1, sacc);
+        }
+        latent(i);
     }
 
     // ---- write the split partial: un-normalised O, reference max, mass ----
-    // The workgroup's 128 heads are 128 consecutive 2-KiB rows of part_o.
-    // Accumulator q, element r is latent column 32 q + 8 (r/4) + 4 half + r%4
-    // of this lane's head; each lane's 16-byte pieces would land in 32
-    // different rows per store, so the rows are staged in the (now idle) tile
-    // buffers, half of the columns at a time, and written as whole 1-KiB row
-    // segments.
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    // Pair p's 32 heads are rows 32 p .. 32 p + 31 of the workgroup's 128
+    // consecutive 2-KiB rows of part_o.  Accumulator q, element r of this
+    // lane is latent column 256 role + 32 q + 8 (r / 4) + 4 hh + r % 4 of
+    // pair head l32.  The rows are staged in the (now idle) tile buffers, one
+    // half of the columns (one role) at a time, and written as whole 1-KiB
+    // row segments.
+    // Each score head's mass and overflow mark over its 16 lanes.
+    float l_tot[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float l = l_run[r];
+        l += __shfl_xor(l, 1);
+        l += __shfl_xor(l, 2);
+        l += __shfl_xor(l, 4);
+        l += __shfl_xor(l, 8);
+        l_tot[r] = l;
+    }
+    int ov = over;
+    ov |= __shfl_xor(ov, 1);
+    ov |= __shfl_xor(ov, 2);
+    ov |= __shfl_xor(ov, 4);
+    ov |= __shfl_xor(ov, 8);
     float *stage = reinterpret_cast<float *>(tiles);  // [128 heads][kStageRow]
     float *obase = part_o + ((static_cast<int64_t>(v) * S + sp) * H + hg * 128) * DC;
     __syncthreads();  // every wave is done with the last tile
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int half = 0; half < 2; ++half) {
+        if (role == half) {
 #pragma unroll
-        for (int q = 8 * p; q < 8 * p + 8; ++q)
+            for (int q = 0; q < 8; ++q)
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                *reinterpret_cast<f32x4 *>(stage + (32 * w + l32) * kStageRow + 32 * (q - 8 * p) + 8 * m + 4 * half) =
-                    f32x4{oacc[q][4 * m], oacc[q][4 * m + 1], oacc[q][4 * m + 2], oacc[q][4 * m + 3]};
+                for (int m = 0; m < 4; ++m)
+                    *reinterpret_cast<f32x4 *>(stage + (32 * pr + l32) * kStageRow + 32 * q + 8 * m + 4 * hh) =
+                        f32x4{oacc[q][4 * m], oacc[q][4 * m + 1], oacc[q][4 * m + 2], oacc[q][4 * m + 3]};
+        }
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < 128 * 64 / kThreadsDec; ++e) {
             const int idx = tid + kThreadsDec * e, head = idx >> 6, piece = idx & 63;
-            *reinterpret_cast<f32x4 *>(obase + head * DC + 256 * p + 4 * piece) =
+            *reinterpret_cast<f32x4 *>(obase + head * DC + 256 * half + 4 * piece) =
                 *reinterpret_cast<const f32x4 *>(stage + head * kStageRow + 4 * piece);
         }
         __syncthreads();
     }
-    if (half == 0) {
-        // NaN marks a head whose weights could overflow: the merge kernel
-        // recomputes that (split, head) with the split's true maximum.
-        part_ml[prow * 2 + 0] = over ? __builtin_nanf("") : m_ref;
-        part_ml[prow * 2 + 1] = l_tot;
+    if (l16 == 0) {
+        // NaN marks a (split, head) whose weights could overflow: the merge
+        // kernel recomputes it with the split's true maximum.
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = (static_cast<int64_t>(v) * S + sp) * H + hs0 + 4 * g + r;
+            part_ml[row * 2 + 0] = ((ov >> r) & 1) ? __builtin_nanf("") : m_ref[r];
+            part_ml[row * 2 + 1] = l_tot[r];
+        }
     }
 }
 
