@@ -103,7 +103,8 @@ typedef struct mla_decode_params {
     float softmax_scale;  /* multiplies the full score; 0 -> 1/sqrt(d_n + d_r) */
     int32_t dtype;        /* mla_dtype of q_nope, q_rope, weights and caches   */
     int32_t out_dtype;    /* mla_dtype of out                                   */
-    int32_t num_splits;   /* context splits per sequence; 0 -> chosen by size  */
+    int32_t num_splits;   /* context splits per sequence; 0 -> chosen by the
+                             library (bf16: from the actual lengths, below)    */
     double q_rope_base;   /* 0: q_rope arrives rotated for its position; > 1:
                              the library rotates it (see below) with this base */
 } mla_decode_params;
@@ -136,9 +137,18 @@ mla_status mla_absorb_q(const mla_decode_params *p, const void *q_nope, const vo
                         float *q_abs, void *stream);
 
 /*
- * Context splits per sequence that mla_decode will use for `p` (host
- * function): p->num_splits if set, else the library's choice from the
- * batch, head count and n_max.  0 if `p` is invalid.
+ * Context splits (host function; 0 if `p` is invalid).  With p->num_splits
+ * set, every sequence is cut into that many equal ranges of 32-row tiles.
+ * With num_splits = 0 the fp32 path picks one count for all sequences from
+ * the batch, head count and n_max; the bf16 path builds a balanced plan on
+ * the device from the seqlens values (its first kernel): every sequence is
+ * cut into ranges of at most C tiles, C the smallest width of at least 4
+ * tiles that keeps the whole call within 256 / (heads / 128) ranges (one
+ * workgroup per compute unit), so long and short sequences share the chip
+ * evenly; sequences are never cut into more than 256 ranges, and when there
+ * are that many sequences or more each is one range.  For that plan this
+ * function returns the ranges a sequence gets when every sequence holds
+ * n_max rows.
  */
 int mla_decode_num_splits(const mla_decode_params *p);
 
@@ -170,8 +180,11 @@ size_t mla_decode_workspace_bytes(const mla_decode_params *p);
  *   out       [B][H][d_v]  out_dtype, written
  *   workspace >= mla_decode_workspace_bytes(p) bytes, 256-byte aligned;
  *             scratch owned by the caller, contents not preserved.
- * Results are bitwise reproducible for a fixed split count (fixed-order
- * reduction, no floating-point atomics).
+ * Results are bitwise reproducible for the same arguments and seqlens
+ * values (fixed-order reduction, no floating-point atomics).  Under the bf16
+ * balanced plan a sequence's cut points depend on the other sequences'
+ * lengths too, so its result can change in the last bits with theirs; a
+ * fixed num_splits makes each sequence's result depend on its own data only.
  */
 mla_status mla_decode(const mla_decode_params *p, const void *q_nope, const void *q_rope,
                       const void *w_uk, const void *w_uv, const void *ckv_cache,
@@ -243,7 +256,8 @@ typedef struct mla_prefill_params {
     int32_t dtype;
     int32_t out_dtype;
     int32_t num_splits;   /* mla_prefill_absorbed: context splits per query row,
-                             0 -> chosen by size; mla_prefill_naive: must be 0 */
+                             0 -> chosen by the library (as for decode, each
+                             query row a sequence); mla_prefill_naive: 0     */
     double q_rope_base;   /* 0: q_rope arrives rotated; > 1: rotated by the
                              library at each query's position (see above)     */
 } mla_prefill_params;
@@ -272,7 +286,8 @@ mla_status mla_prefill_naive(const mla_prefill_params *p, const void *q_nope,
                              size_t workspace_bytes, void *stream);
 
 /* Context splits per query row that mla_prefill_absorbed will use (host;
- * 0 if `p` is invalid). */
+ * 0 if `p` is invalid), as mla_decode_num_splits: for the bf16 plan, those
+ * of a query row when every sequence holds n_max rows. */
 int mla_prefill_absorbed_num_splits(const mla_prefill_params *p);
 
 /* Bytes of device workspace mla_prefill_absorbed needs (host; 0 if invalid).
@@ -297,8 +312,8 @@ size_t mla_prefill_absorbed_workspace_bytes(const mla_prefill_params *p);
  *   workspace >= mla_prefill_absorbed_workspace_bytes(p), 256-byte aligned.
  * Supported: the decode limits (dtype MLA_BF16: the V3 widths and heads a
  * multiple of 128; MLA_F32: the fp32 limits), batch * tokens <= 65535.
- * Results are bitwise reproducible for a fixed split count; a query with
- * pos < 0 gets a zero row.
+ * Results are reproducible as for mla_decode; a query with pos < 0 gets a
+ * zero row.
  */
 mla_status mla_prefill_absorbed(const mla_prefill_params *p, const void *q_nope,
                                 const void *q_rope, const void *w_uk, const void *w_uv,

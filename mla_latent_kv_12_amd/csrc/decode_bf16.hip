@@ -6,8 +6,10 @@
 //   1. absorb:  Qa[b][h] = [ W_UK[h]^T q_nope[b][h] ; q_rope[b][h] ]   (bf16, 576 wide)
 //      ("DeepSeek MLA Architecture: How It Cuts KV Cache by 93%", section 2:
 //      the up-projection is folded into the query, so keys are never built.)
-//   2. split-KV flash-decode: one workgroup per (context split, 128 heads,
-//      sequence).  Cache rows (576 bf16 = 1152 B) are streamed into LDS once
+//   2. split-KV flash-decode: one workgroup per (work item, 128 heads), a
+//      work item being a range of one query row's context (the absorb
+//      launch plans them from the sequence lengths, so long and short
+//      sequences spread evenly over the compute units).  Cache rows (576 bf16 = 1152 B) are streamed into LDS once
 //      and shared by all 128 heads -- the absorbed decode is MQA-shaped.
 //      Scores S^T[token][head] = C . Qa^T and the latent accumulation
 //      O^T[col][head] += C^T . P^T both run on v_mfma_f32_32x32x16_bf16.
@@ -15,8 +17,8 @@
 //      ("mla-from-scratch" README, "Absorption, and why RoPE breaks it":
 //      score = absorbed content term + decoupled positional term; attend
 //      over the latents and up-project once at the end.)
-//   3. merge + up-project: fixed-order (ascending split) combination of the
-//      split partials, then out = W_UV[h] o_lat.
+//   3. merge + up-project: fixed-order (ascending range) combination of a
+//      row's partials, then out = W_UV[h] o_lat.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -31,97 +33,280 @@ using namespace cdna4;
 constexpr int DC = 512, DR = 64, DQK = DC + DR, DN = 128, DV = 128;
 
 // ---------------------------------------------------------------------------
-// 1. absorb: grid (4 column quarters, H, ceil(B/8)), 256 threads, B = query
-//    rows.  Wave w reduces rows i in [32w, 32w+32) of W_UK[h]; lane holds 2
-//    columns.  The quarter-0 workgroups also place the RoPE query channels
-//    beside q~, rotated at the query's position when rope_base > 0 (RoFormer
-//    pairs (2i, 2i+1) turned by pos * rope_base^(-2i/d_r), angle and rotation
-//    in fp64, rounded through fp32 to bf16).
+// 0. work plan, built by one workgroup of the absorb launch: the item table
+//    [items] = (query row or -1 for none, first tile, end tile, 0) that the
+//    split-KV grid walks, and the row table [rows] = (first item, item
+//    count) that the merge walks; a row's items are consecutive and in
+//    ascending tile order.  With a fixed split count S, item v S + sp is
+//    split sp of row v (equal ranges of ceil(nt / S) tiles).  Otherwise the
+//    balanced plan: every active row cut into ranges of C tiles (the last
+//    one shorter), C found by bisection over plan_bounds' interval.
 // ---------------------------------------------------------------------------
-constexpr int kAbsorbBatch = 8;
+struct PlanArgs {
+    int rows, T, fixed_S, capacity, target;
+    int64_t n_max;
+    int4 *items;
+    int2 *row_tab;
+};
+
+__device__ __forceinline__ int tiles_of(int L) { return (L + kSplitGranule - 1) / kSplitGranule; }
+
+// Exclusive prefix sum of x over the workgroup's 256 threads in thread
+// order; *total gets the sum of all.  tmp: 4 ints of LDS.
+__device__ int block_scan256(int x, int *total, int *tmp)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int inc = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(inc, o);
+        if (lane >= o) inc += u;
+    }
+    __syncthreads();  // the previous call's readers of tmp are done
+    if (lane == 63) tmp[w] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = tmp[i];
+        before += i < w ? t : 0;
+        all += t;
+    }
+    *total = all;
+    return before + inc - x;
+}
+
+// Sum (is_max = false) or maximum over the workgroup's 256 threads, returned
+// to all of them.  tmp: 4 values of LDS.
+template <typename V>
+__device__ V block_all256(V x, V *tmp, bool is_max)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const V u = __shfl_xor(x, o);
+        x = is_max ? max(x, u) : x + u;
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = x;
+    __syncthreads();
+    V r = tmp[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) r = is_max ? max(r, tmp[i]) : r + tmp[i];
+    return r;
+}
+
+__device__ void build_plan(const PlanArgs &a, const int32_t *seqlens)
+{
+    __shared__ int s_nt[256], s_row[256], s_off[256];
+    __shared__ int s_tmp[4];
+    __shared__ long long s_sum[4];
+    const int tid = threadIdx.x;
+    auto row_tiles = [&](int v) {
+        const int b = v / a.T;
+        return tiles_of(query_len(seqlens[b], a.n_max, a.T, v - b * a.T));
+    };
+    if (a.fixed_S > 0) {  // capacity == rows * S
+        const int S = a.fixed_S;
+        for (int g = tid; g < a.capacity; g += 256) {
+            const int v = g / S, sp = g - v * S;
+            const int nt = row_tiles(v);
+            const int tps = (nt + S - 1) / S;
+            const int t0 = min(nt, sp * tps);
+            a.items[g] = make_int4(v, t0, min(nt, t0 + tps), 0);
+            if (sp == 0) a.row_tab[v] = make_int2(v * S, S);
+        }
+        return;
+    }
+    // Tile counts: total, maximum, active rows, and the first 256 active
+    // rows (all of them whenever the width is searched) in row order.
+    long long tot = 0;
+    int mx = 0, active = 0;
+    for (int v0 = 0; v0 < a.rows; v0 += 256) {
+        const int v = v0 + tid;
+        const int nt = v < a.rows ? row_tiles(v) : 0;
+        tot += nt;
+        mx = max(mx, nt);
+        int n_act;
+        const int k = active + block_scan256(nt > 0 ? 1 : 0, &n_act, s_tmp);
+        if (nt > 0 && k < 256) {
+            s_nt[k] = nt;
+            s_row[k] = v;
+        }
+        active += n_act;
+    }
+    tot = block_all256<long long>(tot, s_sum, false);
+    mx = block_all256<int>(mx, s_tmp, true);
+    int C = max(mx, 1);  // as many active rows as items or more: one item per row
+    if (active > 0 && active < a.target) {
+        int lo, hi;
+        plan_bounds(tot, active, mx, a.target, &lo, &hi);
+        while (lo < hi) {  // the sums reach every thread: the loop is uniform
+            const int mid = lo + (hi - lo) / 2;
+            const int n = block_all256<int>(tid < active ? (s_nt[tid] + mid - 1) / mid : 0, s_tmp, false);
+            if (n <= a.target) hi = mid; else lo = mid + 1;
+        }
+        C = lo;
+    }
+    // Rows in chunks of 256: item counts, their offsets, the row table; then
+    // the chunk's items, each thread finding its item's row by bisection
+    // over the chunk's offsets (rows without items share the next row's
+    // offset, so the last entry at or below the item is its row).
+    int carry = 0;
+    for (int v0 = 0; v0 < a.rows; v0 += 256) {
+        const int v = v0 + tid;
+        const int nt = v < a.rows ? row_tiles(v) : 0;
+        const int cnt = nt > 0 ? (nt + C - 1) / C : 0;
+        int n_chunk;
+        const int off = carry + block_scan256(cnt, &n_chunk, s_tmp);
+        if (v < a.rows) a.row_tab[v] = make_int2(off, cnt);
+        s_off[tid] = off;
+        s_nt[tid] = nt;
+        s_row[tid] = v;
+        __syncthreads();
+        for (int g = carry + tid; g < carry + n_chunk && g < a.capacity; g += 256) {
+            int lo = 0, hi = 255;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_off[mid] <= g) lo = mid; else hi = mid - 1;
+            }
+            const int k = g - s_off[lo];
+            a.items[g] = make_int4(s_row[lo], k * C, min(s_nt[lo], (k + 1) * C), 0);
+        }
+        carry += n_chunk;
+        __syncthreads();  // before the next chunk overwrites the tables
+    }
+    for (int g = carry + tid; g < a.capacity; g += 256) a.items[g] = make_int4(-1, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// 1. absorb on MFMA: grid (3, H, ceil(rows / 128)), 256 threads.
+//    x = 0, 1: columns 256 x .. 256 x + 255 of q~ = W_UK[h]^T q_nope for
+//    head y and query rows 128 z .. 128 z + 127.  The workgroup copies its
+//    W_UK[h] slice (128 x 256 bf16, 64 KiB) into LDS once, then computes
+//    q~^T[col][row] = sum_k W[k][col] q[row][k] on v_mfma_f32_32x32x16_bf16
+//    in blocks of 32 rows: A = W columns through the transposing LDS read,
+//    B = query rows straight from global memory; wave w takes columns
+//    64 w .. 64 w + 63 of the 256.  So W_UK is read from memory once per
+//    128 query rows, and the product costs a few MFMAs per wave.  The x = 0
+//    workgroups also place the RoPE query channels beside q~, rotated at
+//    the query's position when rope_base > 0 (RoFormer pairs (2i, 2i+1)
+//    turned by pos * rope_base^(-2i/d_r), angle and rotation in fp64,
+//    rounded through fp32 to bf16).
+//    x = 2: workgroup (2, 0, 0) builds the work plan; the others exit.
+//
+//    LDS: W row k (512 bytes) at k * 512, its 16-byte chunk c stored at
+//    chunk c ^ 4 (k mod 4).  A transposing read takes 4 consecutive rows x
+//    16 columns per group of 16 lanes, and the two groups of a 32-lane pass
+//    take neighbouring columns of the same rows: with the swizzle their 16
+//    chunks cover the 256-byte bank window once.
+// ---------------------------------------------------------------------------
+constexpr int kAbsorbRows = 128;   // query rows per workgroup (4 MFMA blocks of 32)
+constexpr int kAbsorbCols = 256;   // q~ columns per workgroup
+constexpr int kWRowBytes = kAbsorbCols * 2;
+
+__device__ __forceinline__ unsigned w_swz(int k, int chunk) { return static_cast<unsigned>(chunk ^ (4 * (k & 3))); }
 
 __global__ __launch_bounds__(256) void absorb_bf16_kernel(int B, int H, int T, int64_t n_max,
                                                           const int32_t *seqlens, double rope_base,
                                                           const uint16_t *q_nope,
                                                           const uint16_t *q_rope,
-                                                          const uint16_t *w_uk, uint16_t *qa)
+                                                          const uint16_t *w_uk, uint16_t *qa,
+                                                          PlanArgs plan)
 {
-    const int qtr = blockIdx.x, h = blockIdx.y, b0 = blockIdx.z * kAbsorbBatch;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int nb = min(kAbsorbBatch, B - b0);
-    __shared__ float qs[kAbsorbBatch][DN];
-    __shared__ float red[4][kAbsorbBatch][128];
-
-    // Every global load is issued before the first wait: this wave's 32
-    // weight pieces, then the queries, then (quarter 0) the RoPE channel
-    // pair of this thread, so the kernel costs one memory round trip.
-    const int col = qtr * 128 + 2 * lane;
-    const uint32_t *wrow = reinterpret_cast<const uint32_t *>(w_uk + (static_cast<int64_t>(h) * DN + 32 * w) * DC + col);
-    uint32_t wvals[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) wvals[i] = wrow[i * (DC / 2)];
-    constexpr int kQPer = kAbsorbBatch * DN / 256;  // query values per thread
-    uint16_t qv[kQPer];
-#pragma unroll
-    for (int k = 0; k < kQPer; ++k) {
-        const int e = tid + 256 * k, bb = e / DN, i = e % DN;
-        qv[k] = q_nope[(static_cast<int64_t>(b0 + min(bb, nb - 1)) * H + h) * DN + i];
+    if (blockIdx.x == 2) {
+        if (blockIdx.y == 0 && blockIdx.z == 0) build_plan(plan, seqlens);
+        return;
     }
-    // one rotation pair per thread: nb * d_r / 2 <= 8 * 32 = 256 threads
-    static_assert(kAbsorbBatch * (DR / 2) <= 256, "one RoPE pair per thread");
-    const bool rope_lane = qtr == 0 && tid < nb * (DR / 2);
-    const int rv = b0 + tid / (DR / 2), ri = tid % (DR / 2);
-    const int64_t rrow = static_cast<int64_t>(rv) * H + h;
-    uint32_t two = rope_lane ? *reinterpret_cast<const uint32_t *>(q_rope + rrow * DR + 2 * ri) : 0u;
-#pragma unroll
-    for (int k = 0; k < kQPer; ++k) {
-        const int e = tid + 256 * k, bb = e / DN, i = e % DN;
-        qs[bb][i] = bb < nb ? bf16lo(qv[k]) : 0.f;
-    }
-    __syncthreads();
+    __shared__ __attribute__((aligned(1024))) unsigned char wt[DN * kWRowBytes];
+    const int half = blockIdx.x, h = blockIdx.y, row0 = blockIdx.z * kAbsorbRows;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nrows = min(kAbsorbRows, B - row0);
 
-    float acc[kAbsorbBatch][2];
+    // W_UK[h][k][256 half .. + 255] -> LDS: wave w copies rows 32 w .. 32 w + 31,
+    // two rows (1 KiB) per load; lane i lands at chunk i % 32 of row
+    // 2 j + i / 32 and fetches the source chunk that belongs there.
+    {
+        const i32x4 rs = make_rsrc(w_uk + static_cast<int64_t>(h) * DN * DC, DN * DC * 2);
+        const uint32_t base = lds_addr(wt);
 #pragma unroll
-    for (int bb = 0; bb < kAbsorbBatch; ++bb) acc[bb][0] = acc[bb][1] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const uint32_t wv = wvals[i];
-        const float w0 = bf16lo(wv), w1 = bf16hi(wv);
-#pragma unroll
-        for (int bb = 0; bb < kAbsorbBatch; ++bb) {
-            const float q = qs[bb][32 * w + i];
-            acc[bb][0] = fmaf(w0, q, acc[bb][0]);
-            acc[bb][1] = fmaf(w1, q, acc[bb][1]);
+        for (int j = 0; j < 16; ++j) {
+            const int k = 32 * wu + 2 * j + (lane >> 5), p = lane & 31;
+            lds_dma16(rs, base + (32 * wu + 2 * j) * kWRowBytes,
+                      static_cast<unsigned>(k * DC * 2 + half * kWRowBytes + 16 * w_swz(k, p)));
         }
     }
-#pragma unroll
-    for (int bb = 0; bb < kAbsorbBatch; ++bb) {
-        red[w][bb][2 * lane] = acc[bb][0];
-        red[w][bb][2 * lane + 1] = acc[bb][1];
-    }
-    __syncthreads();
-    // 8 batches x 128 columns = 1024 outputs, 4 per thread, summed in wave order.
-    for (int e = tid; e < kAbsorbBatch * 128; e += 256) {
-        const int bb = e / 128, c = e % 128;
-        if (bb >= nb) continue;
-        const float v = ((red[0][bb][c] + red[1][bb][c]) + red[2][bb][c]) + red[3][bb][c];
-        reinterpret_cast<__bf16 *>(qa)[(static_cast<int64_t>(b0 + bb) * H + h) * DQK + qtr * 128 + c] =
-            static_cast<__bf16>(v);
-    }
-    if (rope_lane) {  // RoPE query channels beside q~
-        if (rope_base > 0.0) {
-            const int b = rv / T;
-            const int pos = static_cast<int>(min<int64_t>(max(seqlens[b], 0), n_max)) - T + (rv - b * T);
-            if (pos > 0) {
-                const double theta = pow(rope_base, -2.0 * ri / DR);
-                double sn, cs;
-                sincos(static_cast<double>(pos) * theta, &sn, &cs);
-                const double x0 = bf16lo(two), x1 = bf16hi(two);
-                two = pack_bf16(static_cast<float>(x0 * cs - x1 * sn),
-                                static_cast<float>(x0 * sn + x1 * cs));
+
+    // RoPE query channels beside q~ (x = 0 only): one pair per thread, 8
+    // rows per pass.
+    if (half == 0) {
+        for (int e = tid; e < nrows * (DR / 2); e += 256) {
+            const int rv = row0 + e / (DR / 2), ri = e % (DR / 2);
+            const int64_t rrow = static_cast<int64_t>(rv) * H + h;
+            uint32_t two = *reinterpret_cast<const uint32_t *>(q_rope + rrow * DR + 2 * ri);
+            if (rope_base > 0.0) {
+                const int b = rv / T;
+                const int pos = static_cast<int>(min<int64_t>(max(seqlens[b], 0), n_max)) - T + (rv - b * T);
+                if (pos > 0) {
+                    const double theta = pow(rope_base, -2.0 * ri / DR);
+                    double sn, cs;
+                    sincos(static_cast<double>(pos) * theta, &sn, &cs);
+                    const double x0 = bf16lo(two), x1 = bf16hi(two);
+                    two = pack_bf16(static_cast<float>(x0 * cs - x1 * sn),
+                                    static_cast<float>(x0 * sn + x1 * cs));
+                }
             }
+            *reinterpret_cast<uint32_t *>(qa + rrow * DQK + DC + 2 * ri) = two;
         }
-        *reinterpret_cast<uint32_t *>(qa + rrow * DQK + DC + 2 * ri) = two;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    // A operand (W^T, rows = columns of q~, K = k): lane l takes column
+    // 64 w + 32 nb + l % 32 and k = 16 s + 8 (l / 32) .. + 7 as two
+    // transposing reads of 4 rows; in its group of 16 lanes, lane a
+    // addresses row 4 (a / 4) + (0 | 4) ... + 8 (l / 32) and the 4 columns
+    // 16 (l / 16 % 2) + 4 (a % 4) .. + 3 of the block.
+    const int a16 = lane & 15, G = lane >> 4;
+    const int krow = 8 * (G >> 1) + (a16 >> 2);               // + 16 s, + 4 for the second read
+    const int ccol = 64 * wu + 16 * (G & 1) + 4 * (a16 & 3);  // + 32 nb
+    auto a_op = [&](int s, int nb) -> u32x4 {
+        u32x2 v[2];
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+            const int k = 16 * s + krow + 4 * hlf, c = ccol + 32 * nb;
+            v[hlf] = lds_read_tr4(wt + k * kWRowBytes + 16 * w_swz(k, c >> 3) + 8 * ((c >> 2) & 1));
+        }
+        return u32x4{v[0][0], v[0][1], v[1][0], v[1][1]};
+    };
+    for (int mb = 0; mb * 32 < nrows; ++mb) {
+        // B operand: query row row0 + 32 mb + l % 32 (clamped), k = 16 s + 8 (l / 32) .. + 7
+        const int rv = row0 + 32 * mb + (lane & 31);
+        const uint16_t *qrow = q_nope + (static_cast<int64_t>(min(rv, B - 1)) * H + h) * DN + 8 * (lane >> 5);
+        u32x4 qb[DN / 16];
+#pragma unroll
+        for (int s = 0; s < DN / 16; ++s) qb[s] = *reinterpret_cast<const u32x4 *>(qrow + 16 * s);
+        f32x16 acc[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < DN / 16; ++s)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32(a_op(s, nb), qb[s], acc[nb]);
+        // acc[nb][r]: q~ row rv, column 256 half + 64 w + 32 nb + 8 (r / 4) + 4 (l / 32) + r % 4
+        if (rv < B) {
+            uint16_t *dst = qa + (static_cast<int64_t>(rv) * H + h) * DQK + half * kAbsorbCols + 64 * wu +
+                            4 * (lane >> 5);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<u32x2 *>(dst + 32 * nb + 8 * j) =
+                        u32x2{pack_bf16(acc[nb][4 * j], acc[nb][4 * j + 1]),
+                              pack_bf16(acc[nb][4 * j + 2], acc[nb][4 * j + 3])};
+        }
     }
 }
 
@@ -208,7 +393,8 @@ __device__ __forceinline__ void vm_wait()
 }
 
 __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
-    int T, int H, int S, int64_t n_max, const uint16_t *__restrict__ ckv, int64_t ckv_sb, int ckv_rowb,
+    int T, int H, const int4 *__restrict__ plan_items, int64_t n_max,
+    const uint16_t *__restrict__ ckv, int64_t ckv_sb, int ckv_rowb,
     const uint16_t *__restrict__ kpe, int64_t kpe_sb, int kpe_rowb,
     const int32_t *__restrict__ seqlens, const uint16_t *__restrict__ qa, float c2,
     float *__restrict__ part_o, float *__restrict__ part_ml)
@@ -216,9 +402,13 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) unsigned char tiles[kTileBufs * kTileBytes];
     __shared__ __attribute__((aligned(16))) unsigned char pbuf[2 * kPBytes];
 
-    // Query row v = b * T + t: query t of sequence b (T = 1 for decode)
-    // attends to the causal prefix of its sequence's cache.
-    const int sp = blockIdx.x, hg = blockIdx.y, v = blockIdx.z;
+    // Work item = a range of tiles of query row v = b * T + t: query t of
+    // sequence b (T = 1 for decode) attends to the causal prefix of its
+    // sequence's cache.
+    const int item = blockIdx.x, hg = blockIdx.y;
+    const int4 work = plan_items[item];
+    const int v = work.x;
+    if (v < 0) return;  // unused item: nothing reads its partials
     const int b = v / T, tq = v - b * T;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, known uniform
@@ -229,14 +419,12 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     const int hs = hs0 + l16;                              // query row of this lane (score A operand)
 
     const int L = query_len(seqlens[b], n_max, T, tq);
-    const int ntiles_seq = (L + kTile - 1) / kTile;
-    const int tps = (ntiles_seq + S - 1) / S;
-    const int start = sp * tps * kTile;
-    const int end = min(L, start + tps * kTile);
+    const int start = work.y * kTile;
+    const int end = min(L, work.z * kTile);
 
     if (start >= end) {  // empty split: weight zero in the merge, O never read
         if (g == 0) {
-            const int64_t prow = (static_cast<int64_t>(v) * S + sp) * H + hs;
+            const int64_t prow = static_cast<int64_t>(item) * H + hs;
             part_ml[prow * 2 + 0] = -INFINITY;
             part_ml[prow * 2 + 1] = 0.f;
         }
@@ -507,7 +695,7 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
     ov |= __shfl_xor(ov, 4);
     ov |= __shfl_xor(ov, 8);
     float *stage = reinterpret_cast<float *>(tiles);  // [128 heads][kStageRow]
-    float *obase = part_o + ((static_cast<int64_t>(v) * S + sp) * H + hg * 128) * DC;
+    float *obase = part_o + (static_cast<int64_t>(item) * H + hg * 128) * DC;
     __syncthreads();  // every wave is done with the last tile
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -533,7 +721,7 @@ __global__ __launch_bounds__(kThreadsDec, 1) void decode_splitkv_bf16_kernel(
         // kernel recomputes it with the split's true maximum.
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t row = (static_cast<int64_t>(v) * S + sp) * H + hs0 + 4 * g + r;
+            const int64_t row = static_cast<int64_t>(item) * H + hs0 + 4 * g + r;
             part_ml[row * 2 + 0] = ((ov >> r) & 1) ? __builtin_nanf("") : m_ref[r];
             part_ml[row * 2 + 1] = l_tot[r];
         }
@@ -563,6 +751,7 @@ struct CacheView {
     const int32_t *seqlens;
     const uint16_t *qa;      // [B * T][H][576] absorbed queries (bf16)
     float c2;                // softmax scale * log2(e)
+    const int4 *items;       // the work plan's item table
 };
 
 __device__ float block_reduce(float v, float *red, bool is_max)
@@ -579,21 +768,20 @@ __device__ float block_reduce(float v, float *red, bool is_max)
     return r;
 }
 
-// Recompute one (query row, split, head) partial: scores against the split's
-// rows, their maximum, then weights, mass and the weighted latent sum.
-__device__ void recompute_partial(const CacheView &cv, int H, int S, int v, int sp, int h,
-                                  float *part_o, float *part_ml)
+// Recompute one (work item, head) partial: scores against the item's rows,
+// their maximum, then weights, mass and the weighted latent sum.
+__device__ void recompute_partial(const CacheView &cv, int H, int item, int h, float *part_o,
+                                  float *part_ml)
 {
     __shared__ float q[DQK];
     __shared__ float pw[256];
     __shared__ float red[4];
     const int tid = threadIdx.x;
-    const int b = v / cv.T;
+    const int4 work = cv.items[item];
+    const int v = work.x, b = v / cv.T;
     const int L = query_len(cv.seqlens[b], cv.n_max, cv.T, v - b * cv.T);
-    const int ntiles_seq = (L + kSplitGranule - 1) / kSplitGranule;
-    const int tps = (ntiles_seq + S - 1) / S;
-    const int start = sp * tps * kSplitGranule;
-    const int end = min(L, start + tps * kSplitGranule);
+    const int start = work.y * kSplitGranule;
+    const int end = min(L, work.z * kSplitGranule);
     const uint16_t *qrow = cv.qa + (static_cast<int64_t>(v) * H + h) * DQK;
     for (int k = tid; k < DQK; k += 256) q[k] = bf16lo(qrow[k]);
     __syncthreads();
@@ -623,7 +811,7 @@ __device__ void recompute_partial(const CacheView &cv, int H, int S, int v, int 
         }
         __syncthreads();
     }
-    const int64_t prow = (static_cast<int64_t>(v) * S + sp) * H + h;
+    const int64_t prow = static_cast<int64_t>(item) * H + h;
     part_o[prow * DC + 2 * tid] = o0;
     part_o[prow * DC + 2 * tid + 1] = o1;
     if (tid == 0) {
@@ -637,7 +825,7 @@ __device__ void recompute_partial(const CacheView &cv, int H, int S, int v, int 
 // attention output before the up-projection, for a caller that folds W_UV
 // into its output projection) instead of W_UV[h] o_lat.
 template <bool kUpProj>
-__global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
+__global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, const int2 *__restrict__ row_tab,
                                                                 float *__restrict__ part_o,
                                                                 float *__restrict__ part_ml,
                                                                 const uint16_t *__restrict__ w_uv,
@@ -652,12 +840,30 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
     __shared__ __attribute__((aligned(16))) f32x4 half_sum[2][DC / 4];
     __shared__ __attribute__((aligned(16))) float ol[DC];
 
-    const int64_t base = static_cast<int64_t>(v) * S * H + h;  // row of split 0
+    // The row's splits are work items first .. first + S - 1, in ascending
+    // order of their context ranges.
+    const int2 rt = row_tab[v];
+    const int first = rt.x, S = rt.y;
+    if (S == 0) {  // no context: a zero row
+        if constexpr (kUpProj) {
+            const int64_t oi = (static_cast<int64_t>(v) * H + h) * DV + tid;
+            if (tid < DV) {
+                if (out_bf16) reinterpret_cast<uint16_t *>(out)[oi] = 0;
+                else reinterpret_cast<float *>(out)[oi] = 0.f;
+            }
+        } else {
+            const int64_t oi = (static_cast<int64_t>(v) * H + h) * DC + 2 * tid;
+            if (out_bf16) *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(out) + oi) = 0u;
+            else *reinterpret_cast<float2 *>(reinterpret_cast<float *>(out) + oi) = float2{0.f, 0.f};
+        }
+        return;
+    }
+    const int64_t base = static_cast<int64_t>(first) * H + h;  // row of split 0
     if constexpr (!kUpProj) {
         if (S == 1) {  // one split: o = O / l, no cross-split weighting
             float m0 = part_ml[base * 2], l0 = part_ml[base * 2 + 1];
             if (__builtin_isnan(m0)) {  // marked: recompute with the split's true maximum
-                recompute_partial(cv, H, 1, v, 0, h, part_o, part_ml);
+                recompute_partial(cv, H, first, h, part_o, part_ml);
                 m0 = part_ml[base * 2];
                 l0 = part_ml[base * 2 + 1];
             }
@@ -722,7 +928,7 @@ __global__ __launch_bounds__(256) void merge_upproj_bf16_kernel(int H, int S,
     if (any_nan) {
         for (int sp = 0; sp < S; ++sp)
             if (__builtin_isnan(part_ml[(base + static_cast<int64_t>(sp) * H) * 2]))
-                recompute_partial(cv, H, S, v, sp, h, part_o, part_ml);
+                recompute_partial(cv, H, first + sp, h, part_o, part_ml);
         if (tid < S) {
             ms = part_ml[(base + static_cast<int64_t>(tid) * H) * 2];
             ls = part_ml[(base + static_cast<int64_t>(tid) * H) * 2 + 1];
@@ -892,20 +1098,23 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
     uint16_t *qa = static_cast<uint16_t *>(ws.q);
     const int rows = s.B * s.T;  // query rows
     if (events && events[0]) (void)hipEventRecord(events[0], st);
+    int4 *plan_items = reinterpret_cast<int4 *>(ws.plan_items);
+    int2 *plan_rows = reinterpret_cast<int2 *>(ws.plan_rows);
     {
-        dim3 grid(4, s.H, (rows + kAbsorbBatch - 1) / kAbsorbBatch);
+        const PlanArgs plan{rows, s.T, s.S, s.items, plan_target(s.H), s.n_max, plan_items, plan_rows};
+        dim3 grid(3, s.H, (rows + kAbsorbRows - 1) / kAbsorbRows);
         absorb_bf16_kernel<<<grid, 256, 0, st>>>(rows, s.H, s.T, s.n_max, seqlens, s.q_rope_base,
                                                  static_cast<const uint16_t *>(q_nope),
                                                  static_cast<const uint16_t *>(q_rope),
-                                                 static_cast<const uint16_t *>(w_uk), qa);
+                                                 static_cast<const uint16_t *>(w_uk), qa, plan);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (events && events[1]) (void)hipEventRecord(events[1], st);
     {
-        dim3 grid(s.S, s.H / 128, rows);
+        dim3 grid(s.items, s.H / 128);
         decode_splitkv_bf16_kernel<<<grid, kThreadsDec, 0, st>>>(
-            s.T, s.H, s.S, s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb,
+            s.T, s.H, plan_items, s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb,
             static_cast<int>(s.ckv_sn * 2), static_cast<const uint16_t *>(kpe), s.kpe_sb,
             static_cast<int>(s.kpe_sn * 2), seqlens, qa, s.scale * kLog2e, ws.part_o, ws.part_ml);
         hipError_t e = hipGetLastError();
@@ -915,11 +1124,11 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
     dim3 grid(s.H, rows);
     CacheView cv{s.T, s.n_max, static_cast<const uint16_t *>(ckv), s.ckv_sb, s.ckv_sn,
                  static_cast<const uint16_t *>(kpe), s.kpe_sb, s.kpe_sn, seqlens, qa,
-                 s.scale * kLog2e};
+                 s.scale * kLog2e, plan_items};
     hipError_t e;
     if (w_uv && batched_upproj(s, true)) {
         // many query rows: merge into fp32 latents, then one product per head
-        merge_upproj_bf16_kernel<false><<<grid, 256, 0, st>>>(s.H, s.S, ws.part_o, ws.part_ml,
+        merge_upproj_bf16_kernel<false><<<grid, 256, 0, st>>>(s.H, plan_rows, ws.part_o, ws.part_ml,
                                                               nullptr, ws.o_lat, 0, cv);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -928,10 +1137,10 @@ hipError_t launch_decode_bf16(const DecodeShape &s, const void *q_nope, const vo
                                                   static_cast<const uint16_t *>(w_uv), out, s.out_bf16);
     } else if (w_uv) {
         merge_upproj_bf16_kernel<true><<<grid, 256, 0, st>>>(
-            s.H, s.S, ws.part_o, ws.part_ml, static_cast<const uint16_t *>(w_uv), out, s.out_bf16, cv);
+            s.H, plan_rows, ws.part_o, ws.part_ml, static_cast<const uint16_t *>(w_uv), out, s.out_bf16, cv);
     } else {
         merge_upproj_bf16_kernel<false><<<grid, 256, 0, st>>>(
-            s.H, s.S, ws.part_o, ws.part_ml, nullptr, out, s.out_bf16, cv);
+            s.H, plan_rows, ws.part_o, ws.part_ml, nullptr, out, s.out_bf16, cv);
     }
     e = hipGetLastError();
     if (events && events[3]) (void)hipEventRecord(events[3], st);

@@ -71,16 +71,15 @@ bool bf16_dims_ok(int64_t H, int64_t dc, int64_t dr, int64_t dn, int64_t dv)
     return dc == 512 && dr == 64 && dn == 128 && dv == 128 && H % 128 == 0;
 }
 
-// rows = query rows (batch for decode, batch * tokens for absorbed prefill).
-int auto_splits(int32_t dtype, int64_t rows, int64_t heads, int64_t n_max)
+// Split count of the fp32 path; rows = query rows (batch for decode, batch *
+// tokens for absorbed prefill).
+int auto_splits(int64_t rows, int64_t heads, int64_t n_max)
 {
-    // Enough (query row, split) blocks to cover the 256 compute units about
-    // once, but at least four 32-token tiles of context per split so the
-    // split partials stay small next to the cache rows they summarise.
+    // Enough (query row, head, split) blocks to cover the 256 compute units
+    // about once, but at least four 32-token tiles of context per split so
+    // the split partials stay small next to the cache rows they summarise.
     const int64_t tiles = (n_max + mla::kSplitGranule - 1) / mla::kSplitGranule;
-    const int64_t groups =
-        dtype == MLA_BF16 ? rows * (heads / mla::decode_bf16_heads_per_block((int)heads))
-                          : rows * heads;
+    const int64_t groups = rows * heads;
     const int64_t target = 256;
     int64_t s = (target + groups - 1) / groups;
     int64_t cap = tiles / 4;
@@ -88,6 +87,45 @@ int auto_splits(int32_t dtype, int64_t rows, int64_t heads, int64_t n_max)
     if (s < 1) s = 1;
     if (s > mla::kMaxSplits) s = mla::kMaxSplits;
     return (int)s;
+}
+
+// Items the bf16 balanced plan gives one query row holding all n_max rows of
+// its sequence (host-side report; the device builds the plan from the actual
+// lengths).  B sequences of T queries: query t sees n_max - (T - 1 - t) rows.
+int plan_splits_full(int64_t B, int64_t T, int64_t H, int64_t n_max)
+{
+    const int G = mla::plan_target((int)H);
+    auto nt_of = [&](int64_t t) {
+        const int64_t L = n_max - (T - 1 - t);
+        return L > 0 ? (L + mla::kSplitGranule - 1) / mla::kSplitGranule : (int64_t)0;
+    };
+    int64_t tiles = 0, active = 0, max_nt = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t nt = nt_of(t);
+        tiles += B * nt;
+        active += nt > 0 ? B : 0;
+        max_nt = nt > max_nt ? nt : max_nt;
+    }
+    if (active == 0) return 0;
+    if (active >= G) return 1;
+    int lo, hi;
+    mla::plan_bounds(tiles, (int)active, (int)max_nt, G, &lo, &hi);
+    while (lo < hi) {
+        const int mid = lo + (hi - lo) / 2;
+        int64_t n = 0;
+        for (int64_t t = 0; t < T; ++t) n += B * ((nt_of(t) + mid - 1) / mid);
+        if (n <= G) hi = mid; else lo = mid + 1;
+    }
+    return (int)((max_nt + lo - 1) / lo);
+}
+
+// The bf16 path's plan for B * T query rows: a fixed split count S (> 0) or
+// the balanced plan (S = 0).  The parameter checks bound B * T by 65535 and
+// S by kMaxSplits, so the item count stays below 2^24.
+void set_plan(mla::DecodeShape *s, int64_t B, int64_t T, int S)
+{
+    s->S = S;
+    s->items = (int)mla::plan_capacity(B * T, s->H, S);
 }
 
 mla_status check_rope_base(double base, int64_t dr)
@@ -160,7 +198,12 @@ mla::DecodeShape make_shape(const mla_decode_params *p)
     s.kpe_sn = p->kpe_stride_n;
     s.scale = p->softmax_scale > 0.f ? p->softmax_scale
                                      : (float)(1.0 / sqrt((double)(p->d_n + p->d_r)));
-    s.S = p->num_splits > 0 ? p->num_splits : auto_splits(p->dtype, p->batch, p->heads, p->n_max);
+    if (p->dtype == MLA_BF16) {
+        set_plan(&s, p->batch, 1, p->num_splits);
+    } else {
+        s.S = p->num_splits > 0 ? p->num_splits : auto_splits(p->batch, p->heads, p->n_max);
+        s.items = s.B * s.S;
+    }
     s.out_bf16 = p->out_dtype == MLA_BF16;
     s.q_rope_base = p->q_rope_base;
     return s;
@@ -187,10 +230,15 @@ namespace mla {
 
 size_t decode_workspace_layout(const DecodeShape &s, bool bf16, DecodeWorkspace *ws, void *base)
 {
-    const size_t rows = (size_t)s.B * (size_t)s.T * (size_t)s.H;  // (query row, head) pairs
+    const size_t qrows = (size_t)s.B * (size_t)s.T;  // query rows
+    const size_t rows = qrows * (size_t)s.H;           // (query row, head) pairs
     const size_t qbytes = bf16 ? rows * (size_t)(s.dc + s.dr) * 2 : rows * (size_t)s.dc * 4;
-    const size_t obytes = rows * (size_t)s.S * (size_t)s.dc * 4;
-    const size_t mlbytes = rows * (size_t)s.S * 2 * 4;
+    // partial (O, m, l) per (query row, split, head), or per (item, head)
+    const size_t units = bf16 ? (size_t)s.items * (size_t)s.H : rows * (size_t)s.S;
+    const size_t obytes = units * (size_t)s.dc * 4;
+    const size_t mlbytes = units * 2 * 4;
+    const size_t ibytes = bf16 ? (size_t)s.items * 4 * sizeof(int) : 0;
+    const size_t vbytes = bf16 ? qrows * 2 * sizeof(int) : 0;
     // the fp32 path rotates q_rope into its own buffer; the bf16 absorb kernel
     // rotates while it copies q_rope beside q~
     const size_t rbytes = (s.q_rope_base > 0.0 && !bf16) ? rows * (size_t)s.dr * 4 : 0;
@@ -199,7 +247,9 @@ size_t decode_workspace_layout(const DecodeShape &s, bool bf16, DecodeWorkspace 
     const size_t off_ml = off_o + round_up(obytes, kAlign);
     const size_t off_r = off_ml + round_up(mlbytes, kAlign);
     const size_t off_l = off_r + round_up(rbytes, kAlign);
-    const size_t total = off_l + round_up(lbytes, kAlign);
+    const size_t off_i = off_l + round_up(lbytes, kAlign);
+    const size_t off_v = off_i + round_up(ibytes, kAlign);
+    const size_t total = off_v + round_up(vbytes, kAlign);
     if (ws) {
         char *b = static_cast<char *>(base);
         ws->q = b;
@@ -207,6 +257,8 @@ size_t decode_workspace_layout(const DecodeShape &s, bool bf16, DecodeWorkspace 
         ws->part_ml = reinterpret_cast<float *>(b + off_ml);
         ws->q_rope = rbytes ? b + off_r : nullptr;
         ws->o_lat = lbytes ? reinterpret_cast<float *>(b + off_l) : nullptr;
+        ws->plan_items = ibytes ? reinterpret_cast<int *>(b + off_i) : nullptr;
+        ws->plan_rows = vbytes ? reinterpret_cast<int *>(b + off_v) : nullptr;
     }
     return total;
 }
@@ -218,6 +270,8 @@ extern "C" {
 int mla_decode_num_splits(const mla_decode_params *p)
 {
     if (check_decode_params(p) != MLA_OK) return 0;
+    if (p->dtype == MLA_BF16 && p->num_splits == 0)
+        return plan_splits_full(p->batch, 1, p->heads, p->n_max);
     return make_shape(p).S;
 }
 
@@ -537,8 +591,13 @@ mla::DecodeShape make_absorbed_shape(const mla_prefill_params *p)
     s.kpe_sn = p->kpe_stride_n;
     s.scale = p->softmax_scale > 0.f ? p->softmax_scale
                                      : (float)(1.0 / sqrt((double)(p->d_n + p->d_r)));
-    s.S = p->num_splits > 0 ? p->num_splits
-                            : auto_splits(p->dtype, p->batch * p->tokens, p->heads, p->n_max);
+    if (p->dtype == MLA_BF16) {
+        set_plan(&s, p->batch, p->tokens, p->num_splits);
+    } else {
+        s.S = p->num_splits > 0 ? p->num_splits
+                                : auto_splits(p->batch * p->tokens, p->heads, p->n_max);
+        s.items = s.B * s.T * s.S;
+    }
     s.out_bf16 = p->out_dtype == MLA_BF16;
     s.q_rope_base = p->q_rope_base;
     return s;
@@ -650,6 +709,8 @@ mla_status mla_prefill_naive(const mla_prefill_params *p, const void *q_nope, co
 int mla_prefill_absorbed_num_splits(const mla_prefill_params *p)
 {
     if (check_prefill_absorbed_params(p) != MLA_OK) return 0;
+    if (p->dtype == MLA_BF16 && p->num_splits == 0)
+        return plan_splits_full(p->batch, p->tokens, p->heads, p->n_max);
     return make_absorbed_shape(p).S;
 }
 

@@ -23,19 +23,69 @@ struct DecodeShape {
     int64_t n_max;
     int64_t ckv_sb, ckv_sn, kpe_sb, kpe_sn;
     float scale;         // softmax scale (natural-log units)
-    int S;               // context splits per query row
+    // fp32 path: context splits per query row.  bf16 path: the caller's fixed
+    // split count, or 0 for the balanced work plan (see items).
+    int S;
+    // bf16 path: work items the split-KV launch covers (its grid), each a
+    // range of one query row's tiles; the partials are stored per item.
+    int items;
     int out_bf16;        // output stored as bf16 (else fp32)
     double q_rope_base;  // > 0: rotate q_rope at each query's position first
 };
+
+// The bf16 split-KV work plan.  With a fixed split count S every query row is
+// cut into S equal tile ranges (items v * S .. v * S + S - 1).  Without one,
+// each row is cut into ranges of at most C tiles, C the smallest width (at
+// least kPlanMinTiles) for which the whole call needs no more than
+// kPlanTargetItems / head groups items (one workgroup per compute unit); a
+// row's items are consecutive, in ascending tile order.
+// Rows that cannot be held to that budget (as many active rows as items, or
+// more) get one item each.  A row never gets more than kMaxSplits items.
+constexpr int kPlanTargetItems = 256;
+constexpr int kPlanMinTiles = 4;
+__host__ __device__ inline int plan_target(int H)
+{
+    const int groups = H / 128 > 0 ? H / 128 : 1;
+    return kPlanTargetItems / groups > 0 ? kPlanTargetItems / groups : 1;
+}
+// Items the split-KV grid covers: fixed split count, or the plan's bound.
+inline int64_t plan_capacity(int64_t rows, int H, int fixed_S)
+{
+    if (fixed_S > 0) return rows * fixed_S;
+    return rows > plan_target(H) ? rows : plan_target(H);
+}
+// Search interval of the plan's width C (tiles per item) when 0 < active <
+// target (tiles = sum of the rows' tile counts nt_v, max_nt their maximum).
+// Every C in it keeps a row at kMaxSplits items or fewer, and C = hi meets
+// the budget: sum_v ceil(nt_v / C) <= tiles / C + active <= target for
+// C >= tiles / (target - active), and the sum is active for C >= max_nt.
+// The item count only falls as C grows, so the plan takes the smallest C in
+// [lo, hi] that meets the budget by bisection.
+__host__ __device__ inline void plan_bounds(int64_t tiles, int active, int max_nt, int target,
+                                            int *lo, int *hi)
+{
+    int64_t l = (tiles + target - 1) / target;
+    const int64_t per_row = (static_cast<int64_t>(max_nt) + kMaxSplits - 1) / kMaxSplits;
+    if (l < kPlanMinTiles) l = kPlanMinTiles;
+    if (l < per_row) l = per_row;
+    const int64_t room = target - active;
+    int64_t h = (tiles + room - 1) / room;
+    if (h > max_nt) h = max_nt;  // C >= max_nt: one item per active row, also within budget
+    if (h < l) h = l;
+    *lo = static_cast<int>(l);
+    *hi = static_cast<int>(h);
+}
 
 // Workspace carving, identical for the fp32 and bf16 paths except for the
 // query buffer's element type and width.  Rows are the B * T query rows.
 struct DecodeWorkspace {
     void *q;          // bf16 path: [rows][H][dc+dr] bf16 pre-absorbed query; fp32: [rows][H][dc] fp32
-    float *part_o;    // [rows][S][H][dc]   un-normalised latent accumulators per split
-    float *part_ml;   // [rows][S][H][2]    running max (log2 units) and softmax mass per split
+    float *part_o;    // fp32: [rows][S][H][dc]; bf16: [items][H][dc]  un-normalised latent sums
+    float *part_ml;   // fp32: [rows][S][H][2];  bf16: [items][H][2]   reference max (log2) and mass
     void *q_rope;     // fp32 path with q rotation: [rows][H][dr] q_rope rotated at its position
     float *o_lat;     // bf16 path with many query rows: [rows][H][dc] merged latents
+    int *plan_items;  // bf16 path: [items][4] query row (-1: unused), first tile, end tile, 0
+    int *plan_rows;   // bf16 path: [rows][2] first item, item count
 };
 
 // With many (query row, head) pairs (a decode batch of 8 or more at 128

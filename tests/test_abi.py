@@ -77,17 +77,33 @@ def test_decode_workspace_size():
     o = 8 * 32 * 128 * 512 * 4
     ml = 8 * 32 * 128 * 2 * 4
     lat = 8 * 128 * 512 * 4        # merged latents for the batched up-projection (B*H >= 1024)
+    plan = lambda items, rows: rnd(items * 16) + rnd(rows * 8)   # item and row tables
     rnd = lambda x: (x + 255) // 256 * 256
-    assert ws == rnd(q) + rnd(o) + rnd(ml) + rnd(lat)
+    assert ws == rnd(q) + rnd(o) + rnd(ml) + rnd(lat) + plan(8 * 32, 8)
     # batch 4 (B*H = 512) keeps the fused merge + up-projection: no latent buffer
     assert mla.decode_workspace_bytes(_v3_params(batch=4, num_splits=32)) == \
-        rnd(q // 2) + rnd(o // 2) + rnd(ml // 2)
+        rnd(q // 2) + rnd(o // 2) + rnd(ml // 2) + plan(4 * 32, 4)
+    # the balanced plan (num_splits = 0) sizes its partials for 256 items
+    # (one per compute unit) whatever the batch below 256
+    for batch in (1, 8, 100):
+        got = mla.decode_workspace_bytes(_v3_params(batch=batch))
+        qb = batch * 128 * 576 * 2
+        latb = batch * 128 * 512 * 4 if batch * 128 >= 1024 else 0
+        assert got == rnd(qb) + rnd(256 * 128 * 512 * 4) + rnd(256 * 128 * 8) + rnd(latb) + \
+            plan(256, batch)
+    # 300 sequences: one item each at most
+    assert mla.decode_workspace_bytes(_v3_params(batch=300)) == \
+        rnd(300 * 128 * 576 * 2) + rnd(300 * 128 * 512 * 4) + rnd(300 * 128 * 8) + \
+        rnd(300 * 128 * 512 * 4) + plan(300, 300)
     # the bf16 path rotates q_rope while placing it beside q~ (no extra room);
     # the fp32 path keeps a rotated copy
     assert mla.decode_workspace_bytes(_v3_params(num_splits=32, q_rope_base=10000.0)) == ws
     f32 = dict(dtype=mla.MLA_F32, out_dtype=mla.MLA_F32, num_splits=32)
     assert mla.decode_workspace_bytes(_v3_params(q_rope_base=10000.0, **f32)) == \
         mla.decode_workspace_bytes(_v3_params(**f32)) + rnd(8 * 128 * 64 * 4)
+    # the fp32 path has no plan tables
+    assert mla.decode_workspace_bytes(_v3_params(**f32)) == \
+        rnd(8 * 128 * 512 * 4) + rnd(8 * 32 * 128 * 512 * 4) + rnd(8 * 32 * 128 * 8)
     assert mla.decode_workspace_bytes(_v3_params()) > 0            # auto split count
     assert mla.decode_workspace_bytes(_v3_params(d_c=256)) == 0    # unsupported -> 0
     assert mla.decode_workspace_bytes(_v3_params(batch=0)) == 0
@@ -224,6 +240,31 @@ def test_prefill_workspace_and_validation():
     assert call(p, ptrs=[vp(0)] + args[1:]) == mla.MLA_ERR_INVALID_ARG
 
 
+def test_decode_num_splits_balanced_plan():
+    # bf16, num_splits = 0: the smallest width C >= 4 tiles with at most 256
+    # items in all, reported for sequences holding all n_max = 131072 rows
+    # (4096 tiles of 32): B sequences get 256 / B items each while that
+    # leaves C >= 4 and at most 256 per sequence.
+    for batch, want in ((1, 256), (2, 128), (4, 64), (8, 32), (32, 8), (128, 2)):
+        assert mla.decode_num_splits(_v3_params(batch=batch)) == want, batch
+    # 200 sequences: 2 items each would be 400 > 256, so one each; likewise 300
+    assert mla.decode_num_splits(_v3_params(batch=200)) == 1
+    assert mla.decode_num_splits(_v3_params(batch=300)) == 1
+    # 4096 rows (128 tiles) at batch 8: C = 4 -> 32 items per sequence
+    short = dict(n_max=4096, ckv_stride_b=4096 * 576, kpe_stride_b=4096 * 576)
+    assert mla.decode_num_splits(_v3_params(**short)) == 32
+    # 64 rows (2 tiles): the 4-tile minimum keeps each sequence whole
+    tiny = dict(n_max=64, ckv_stride_b=64 * 576, kpe_stride_b=64 * 576)
+    assert mla.decode_num_splits(_v3_params(**tiny)) == 1
+    # 3 sequences: 256 // 3 = 85 items at most -> C = ceil(4096 / 85) = 49 ->
+    # 84 items per sequence (252 in all)
+    assert mla.decode_num_splits(_v3_params(batch=3)) == 84
+    # a fixed count is reported as set
+    assert mla.decode_num_splits(_v3_params(num_splits=5)) == 5
+    # the fp32 path picks one count from the sizes: 256 / (8 * 128) -> 1
+    assert mla.decode_num_splits(_v3_params(dtype=mla.MLA_F32, out_dtype=mla.MLA_F32)) == 1
+
+
 def test_prefill_absorbed_workspace_and_splits():
     T = 16
     p = _prefill_params(tokens=T, n_max=131072, ckv_stride_b=131072 * 576,
@@ -233,8 +274,11 @@ def test_prefill_absorbed_workspace_and_splits():
     assert mla.prefill_absorbed_num_splits(p) == 4
     # q~ | q_rope, partials and (m, l) of 4 splits, and the merged latents of
     # the batched up-projection (query rows x heads = 2048 >= 1024)
+    # and the plan's item table (16 query rows x 4 items of 16 bytes) and row
+    # table (16 x 8 bytes)
     assert mla.prefill_absorbed_workspace_bytes(p) == \
-        rnd(rows * 576 * 2) + rnd(rows * 4 * 512 * 4) + rnd(rows * 4 * 2 * 4) + rnd(rows * 512 * 4)
+        rnd(rows * 576 * 2) + rnd(rows * 4 * 512 * 4) + rnd(rows * 4 * 2 * 4) + \
+        rnd(rows * 512 * 4) + rnd(T * 4 * 16) + rnd(T * 8)
     # auto split count: enough (query row, split) blocks for the chip
     auto = _prefill_params(tokens=T, n_max=131072, ckv_stride_b=131072 * 576,
                            kpe_stride_b=131072 * 576)
