@@ -28,14 +28,89 @@ def say(*args):
     sys.stdout.flush()
 
 
+# Guard bands: outputs and workspaces of the parity runs are placed inside
+# larger allocations whose GUARD bytes before and after hold GUARD_BYTE; a
+# kernel that writes past either end of its buffer fails the run.
+GUARD = 4096
+GUARD_BYTE = 0xA5
+
+
+class Guarded:
+    def __init__(self):
+        self._raws = []
+
+    def tensor(self, shape, dtype):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        raw = torch.full((n + 2 * GUARD,), GUARD_BYTE, dtype=torch.uint8, device="cuda")
+        self._raws.append((raw, n))
+        return raw[GUARD:GUARD + n].view(dtype).view(tuple(shape))
+
+    def bytes(self, n):
+        return self.tensor((int(n),), torch.uint8)
+
+    def check(self, what):
+        torch.cuda.synchronize()
+        for raw, n in self._raws:
+            head_ok = bool((raw[:GUARD] == GUARD_BYTE).all())
+            tail_ok = bool((raw[GUARD + n:] == GUARD_BYTE).all())
+            assert head_ok and tail_ok, f"{what}: a write landed in the guard band " \
+                f"({'before' if not head_ok else 'after'} a {n}-byte buffer)"
+
+
+def _out_dtype(params):
+    return torch.float32 if params.out_dtype == mla.MLA_F32 else torch.bfloat16
+
+
 def run_decode(case, *, num_splits=0, out_dtype=None, tensors=None):
     t = tensors if tensors is not None else decode_tensors(case)
     odt = {None: None, "f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
-    out = mla.decode(t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv_cache"],
-                     t["kpe_cache"], t["seqlens"], softmax_scale=case.scale,
-                     num_splits=num_splits, out_dtype=odt)
-    torch.cuda.synchronize()
+    args = (t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv_cache"], t["kpe_cache"])
+    params = mla.decode_params(*args, softmax_scale=case.scale, num_splits=num_splits,
+                               out_dtype=odt)
+    g = Guarded()
+    out = g.tensor((params.batch, params.heads, params.d_v), _out_dtype(params))
+    ws = g.bytes(mla.decode_workspace_bytes(params))
+    mla.decode(*args, t["seqlens"], out=out, workspace=ws, params=params)
+    g.check("decode")
     return out
+
+
+def run_prefill_naive(t, scale, out_dtype=None):
+    """mla_prefill_naive with guarded output and workspace."""
+    args = (t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv"], t["kpe"])
+    params = mla.prefill_params(*args, softmax_scale=scale, out_dtype=out_dtype)
+    g = Guarded()
+    B, T, H, _ = t["q_nope"].shape
+    out = g.tensor((B, T, H, params.d_v), _out_dtype(params))
+    ws = g.bytes(mla.prefill_workspace_bytes(params))
+    mla.prefill_naive(*args, t["seqlens"], out=out, workspace=ws, params=params)
+    g.check("prefill_naive")
+    return out
+
+
+def run_prefill_absorbed(t, scale, out_dtype=None, num_splits=0):
+    """mla_prefill_absorbed with guarded output and workspace."""
+    args = (t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv"], t["kpe"])
+    params = mla.prefill_params(*args, softmax_scale=scale, out_dtype=out_dtype,
+                                num_splits=num_splits)
+    g = Guarded()
+    B, T, H, _ = t["q_nope"].shape
+    out = g.tensor((B, T, H, params.d_v), _out_dtype(params))
+    ws = g.bytes(mla.prefill_absorbed_workspace_bytes(params))
+    mla.prefill_absorbed(*args, t["seqlens"], out=out, workspace=ws, params=params)
+    g.check("prefill_absorbed")
+    return out
+
+
+def run_output_proj(x, w, out_dtype=None, num_splits=0):
+    """mla_output_proj with guarded output and workspace."""
+    params = mla.proj_params(x, w, out_dtype=out_dtype, num_splits=num_splits)
+    g = Guarded()
+    y = g.tensor((x.shape[0], w.shape[0]), _out_dtype(params))
+    ws = g.bytes(mla.output_proj_workspace_bytes(params))
+    mla.output_proj(x, w, out=y, workspace=ws, params=params)
+    g.check("output_proj")
+    return y
 
 
 def oracle_decode(case, pairs=None, naive=False):
@@ -90,6 +165,7 @@ def gather_pairs(out: torch.Tensor, pairs) -> np.ndarray:
     return np.stack([o[b, h] for b, h in pairs])
 
 
-__all__ = ["say", "run_decode", "oracle_decode", "metrics", "assert_close", "gather_pairs",
+__all__ = ["say", "run_decode", "run_prefill_naive", "run_prefill_absorbed", "run_output_proj",
+           "Guarded", "oracle_decode", "metrics", "assert_close", "gather_pairs",
            "oracle_latents",
            "to_device", "to_host_f64", "decode_tensors", "F32_TOL"]

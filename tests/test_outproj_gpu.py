@@ -9,7 +9,7 @@ import torch
 
 import mla_latent_kv_12_amd as mla
 import oracle
-from gpu_util import assert_close, metrics, say, to_device, to_host_f64
+from gpu_util import Guarded, assert_close, metrics, run_output_proj, say, to_device, to_host_f64
 from mla_latent_kv_12_amd import datagen
 from mla_latent_kv_12_amd.tensors import decode_tensors
 
@@ -25,10 +25,9 @@ def normals(rng, shape, std, dtype):
 
 
 def run_proj(x, w, dtype, out_dtype="f32", num_splits=0):
-    y = mla.output_proj(to_device(x, dtype), to_device(w, dtype),
+    y = run_output_proj(to_device(x, dtype), to_device(w, dtype),
                         out_dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16,
                         num_splits=num_splits)
-    torch.cuda.synchronize()
     return to_host_f64(y)
 
 
@@ -100,10 +99,18 @@ def test_decode_latent_matches_oracle(dtype, dims, H, L, splits):
     case = datagen.make_decode_case(B=2, H=H, n_max=max(L), dtype=dtype, seed=4300 + L[1],
                                     seqlens=L, **dims)
     t = decode_tensors(case)
-    o = mla.decode_latent(t["q_nope"], t["q_rope"], t["w_uk"], t["ckv_cache"], t["kpe_cache"],
-                          t["seqlens"], softmax_scale=case.scale, out_dtype=torch.float32,
-                          num_splits=splits)
-    torch.cuda.synchronize()
+    # output and workspace inside guard bands
+    params = mla.decode_params(t["q_nope"], t["q_rope"], t["w_uk"],
+                               torch.empty((H, 128 if dtype == "bf16" else 1, case.dc),
+                                           dtype=t["w_uk"].dtype, device="meta"),
+                               t["ckv_cache"], t["kpe_cache"], softmax_scale=case.scale,
+                               out_dtype=torch.float32, num_splits=splits)
+    g = Guarded()
+    o = g.tensor((2, H, case.dc), torch.float32)
+    ws = g.bytes(mla.decode_workspace_bytes(params))
+    mla.decode_latent(t["q_nope"], t["q_rope"], t["w_uk"], t["ckv_cache"], t["kpe_cache"],
+                      t["seqlens"], out=o, workspace=ws, params=params)
+    g.check("decode_latent")
     ref = oracle.decode_latent(case.q_nope, case.q_rope, case.w_uk, case.ckv, case.kpe,
                                case.seqlens, case.scale)
     assert_close(to_host_f64(o), ref, dtype, "merged latent")

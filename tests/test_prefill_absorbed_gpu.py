@@ -6,7 +6,8 @@ import torch
 
 import mla_latent_kv_12_amd as mla
 import oracle
-from gpu_util import assert_close, metrics, run_decode, say, to_device, to_host_f64
+from gpu_util import (assert_close, metrics, run_decode, run_prefill_absorbed, say, to_device,
+                      to_host_f64)
 from mla_latent_kv_12_amd import datagen
 
 pytestmark = pytest.mark.gpu
@@ -33,10 +34,7 @@ def tensors(case):
 def run_absorbed(case, t=None, out_dtype="f32", num_splits=0):
     t = t or tensors(case)
     odt = {None: None, "f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
-    out = mla.prefill_absorbed(t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv"],
-                               t["kpe"], t["seqlens"], softmax_scale=case.scale, out_dtype=odt,
-                               num_splits=num_splits)
-    torch.cuda.synchronize()
+    out = run_prefill_absorbed(t, case.scale, out_dtype=odt, num_splits=num_splits)
     return to_host_f64(out)
 
 

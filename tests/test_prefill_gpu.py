@@ -5,7 +5,8 @@ import torch
 
 import mla_latent_kv_12_amd as mla
 import oracle
-from gpu_util import assert_close, oracle_latents, run_decode, say, to_device, to_host_f64
+from gpu_util import (assert_close, oracle_latents, run_decode, run_prefill_naive, say, to_device,
+                      to_host_f64)
 from mla_latent_kv_12_amd import datagen
 
 pytestmark = pytest.mark.gpu
@@ -23,9 +24,7 @@ def prefill_tensors(case):
 def run_prefill(case, t=None, out_dtype=None):
     t = t or prefill_tensors(case)
     odt = {None: None, "f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
-    out = mla.prefill_naive(t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"], t["ckv"], t["kpe"],
-                            t["seqlens"], softmax_scale=case.scale, out_dtype=odt)
-    torch.cuda.synchronize()
+    out = run_prefill_naive(t, case.scale, out_dtype=odt)
     return to_host_f64(out)
 
 
